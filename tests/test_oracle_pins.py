@@ -1,0 +1,16 @@
+"""The oracle against its pins (CPU only)."""
+
+import pytest
+
+import oracle
+from tests import pins
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.default()
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(o, pin):
+    pin(o)
