@@ -1,0 +1,145 @@
+/*
+ * tb.h -- C ABI of libtb.so, the ternary-weight int8 FFN decode path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation, after "perf(bonsai): decode and small packed batches read
+ * the FFN from a ternary copy through a dp4a GEMV" (sparkinfer PR #1154),
+ * Summary and commit message:
+ *   - decode reads each FFN's stored ternary weight blocks;
+ *   - a Hadamard rotation emits one int8 copy of the activation, which gate
+ *     and up share;
+ *   - an integer dot-product GEMV folds the per-block scales into each
+ *     block's integer sum;
+ *   - a packed step of up to 8 rows gives every row exactly the bytes it gets
+ *     alone.
+ * Formats: the bonsai-edge-serve README (model list, "kernels/") names
+ * ternary weights in groups of 128, and a 1-bit variant.
+ *
+ * Conventions for every entry point
+ *   Memory   All array pointers are DEVICE pointers, owned by the caller,
+ *            16-byte aligned, row-major and contiguous. tb_matrix structs and
+ *            the tb_matrix pointers are HOST memory; they are read during the
+ *            call only. The library allocates no device memory and keeps no
+ *            pointer after it returns.
+ *   Rows     m is the number of activation rows, 1 <= m <= 8. Rows are
+ *            independent. Row r's outputs are bit-identical for every m and
+ *            for every position r in the batch.
+ *   Shapes   k is a multiple of 128 (k >= 128); n >= 1. nb = k / 128.
+ *   Stream   stream is a hipStream_t passed as void*; 0 is the null stream.
+ *            Work is enqueued on it asynchronously. Inputs must stay valid,
+ *            and outputs unread, until the stream has run it.
+ *   Errors   Arguments are checked before anything is launched. A bad value
+ *            returns TB_EINVAL, a misaligned pointer TB_EALIGN, an input that
+ *            overlaps an output TB_EINVAL, and a shape this build cannot run
+ *            TB_EUNSUPPORTED. In all of these cases nothing is enqueued. A HIP
+ *            error at launch returns TB_EHIP. A fault while the kernel runs
+ *            surfaces at the caller's next synchronisation. Nothing is
+ *            printed, nothing aborts, and no C++ exception crosses the ABI.
+ *   Numbers  Inputs must be finite. Results are deterministic: the same
+ *            inputs give the same bytes on every run.
+ */
+#ifndef TB_H
+#define TB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TB_ABI_VERSION 1
+#define TB_BLOCK 128
+#define TB_MAX_ROWS 8
+
+enum tb_status {
+    TB_OK = 0,
+    TB_EINVAL = -1,       /* bad shape, null pointer, unknown format, aliasing */
+    TB_EALIGN = -2,       /* a pointer is not 16-byte aligned */
+    TB_EUNSUPPORTED = -3, /* valid arguments this build cannot run (e.g. LDS too small) */
+    TB_EHIP = -4          /* the HIP runtime reported an error */
+};
+
+enum tb_format {
+    /* 2-bit ternary codes. Weight i of a row is the 2-bit field at byte i>>2,
+     * bits 2*(i&3) and 2*(i&3)+1, least significant first. Code 0 -> 0,
+     * 1 -> +1, 2 -> -1, 3 -> 0. codes: uint8[n][nb][32]. */
+    TB_FMT_TERNARY2 = 0,
+    /* 1-bit signs. Weight i is bit i&7 of byte i>>3; 1 -> +1, 0 -> -1.
+     * codes: uint8[n][nb][16]. */
+    TB_FMT_SIGN1 = 1
+};
+
+/* One weight matrix with n output rows and k inputs.
+ * scales: uint16[n][nb], IEEE binary16 bit patterns, one per 128-weight
+ * block. The dequantised weight is W[j][i] = scale[j][i/128] * t(j, i). */
+typedef struct tb_matrix {
+    const void *codes;
+    const uint16_t *scales;
+    int32_t n;
+    int32_t k;
+    int32_t fmt; /* enum tb_format */
+} tb_matrix;
+
+/* Rotate and quantise activation rows: the "Hadamard rotation emits the int8
+ * copy" step (PR #1154, commit message).
+ * For every row r and 128-block b, with v = x[r][128b .. 128b+127]:
+ *   u = H v       unnormalised Walsh-Hadamard transform, H[i][j] =
+ *                 (-1)^popcount(i&j). Butterfly stages of span 1, 2, ..., 64
+ *                 in that order, each (a, b) -> (a+b, a-b) in fp32.
+ *   amax = max |u_i|. If amax == 0, q = 0 and dq = 0.
+ *   Otherwise q_i = rint(u_i * (127/amax)) (fp32, ties to even) and
+ *   dq = amax * fp32(1/(127*sqrt(128))).
+ * So q*dq approximates (H/sqrt(128)) v, an orthonormal rotation of v.
+ *   x  float [m][k]     input
+ *   q  int8  [m][k]     output
+ *   dq float [m][k/128] output */
+int tb_rotate_quant_i8(const float *x, int m, int k, int8_t *q, float *dq, void *stream);
+
+/* Ternary (or sign) GEMV: the "dp4a GEMV" with "per-block fold" and
+ * "shuffle tree" (PR #1154, commit message).
+ *   isum[r][j][b] = sum_i t(j, 128b+i) * q[r][128b+i]          (int32, exact)
+ *   y[r][j]       = sum_b scale[j][b] * dq[r][b] * isum[r][j][b]  (fp32 fold)
+ *   w  matrix with w->k inputs, w->n outputs, fmt TERNARY2 or SIGN1
+ *   q  int8 [m][w->k], dq float [m][w->k/128]   (from tb_rotate_quant_i8)
+ *   y  float [m][w->n] output
+ * The fp32 fold is within 1e-4 * sum_b |term_b| of the exact value. */
+int tb_gemv_ternary(const tb_matrix *w, const int8_t *q, const float *dq, int m, float *y,
+                    void *stream);
+
+/* Gate and up GEMVs from one shared int8 copy, then the SiLU gate ("the
+ * Hadamard rotation emits that int8 copy for gate and up to share", PR #1154,
+ * commit message):
+ *   g = gemv(wg, q, dq), u = gemv(wu, q, dq), h[r][j] = silu(g) * u with
+ *   silu(z) = z / (1 + exp(-z)).
+ *   wg, wu  same n, k and fmt
+ *   h       float [m][wg->n] output */
+int tb_ffn_gateup_silu(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q,
+                       const float *dq, int m, float *h, void *stream);
+
+/* Down projection of the FFN: rotate and quantise h exactly like
+ * tb_rotate_quant_i8, into caller-owned workspace, then the GEMV. The pages'
+ * int8 scratch is allocated with the weight copy, never as hidden static
+ * memory (PR #1154, Summary), so here the caller passes it in.
+ *   h       float [m][wd->k]    input (the output of tb_ffn_gateup_silu)
+ *   qh_ws   int8  [m][wd->k]    workspace; holds rotquant(h) on return
+ *   dqh_ws  float [m][wd->k/128] workspace; holds its scales on return
+ *   y       float [m][wd->n]    output */
+int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,
+                float *y, void *stream);
+
+/* Test export: the per-block integer sums of tb_gemv_ternary, from the same
+ * decode and dot-product code, before the scale fold.
+ *   isum int32 [m][w->n][w->k/128] output */
+int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream);
+
+/* Static description of a status code; never NULL. */
+const char *tb_status_str(int status);
+
+/* TB_ABI_VERSION of the built library. */
+int tb_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TB_H */

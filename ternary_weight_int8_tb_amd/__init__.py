@@ -1,0 +1,153 @@
+"""Python binding of libtb.so: ternary-weight int8 FFN decode on MI355X (gfx950).
+
+Argument marshalling only. Every step of the path runs in the HIP kernels of
+``csrc/tb.hip`` behind the C ABI in ``include/tb.h``. The functions take the
+ABI's names; torch tensors supply device memory and the stream. There is no
+CPU fallback: if libtb.so is missing or cannot be loaded, every call raises.
+
+Importing this package loads nothing. ``synth`` (the input generator) works
+without a GPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtb.so")
+
+TB_OK, TB_EINVAL, TB_EALIGN, TB_EUNSUPPORTED, TB_EHIP = 0, -1, -2, -3, -4
+TB_FMT_TERNARY2, TB_FMT_SIGN1 = 0, 1
+BLOCK = 128
+MAX_ROWS = 8
+
+# every symbol include/tb.h declares
+ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_ffn_gateup_silu", "tb_ffn_down",
+               "tb_gemv_block_sums", "tb_status_str", "tb_abi_version")
+
+
+class TbError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({tb_status_str(status)})")
+
+
+class CMatrix(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("n", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("fmt", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_MP = ctypes.POINTER(CMatrix)
+_SIGS = {
+    "tb_rotate_quant_i8": ([_P, _I, _I, _P, _P, _P], _I),
+    "tb_gemv_ternary": ([_MP, _P, _P, _I, _P, _P], _I),
+    "tb_ffn_gateup_silu": ([_MP, _MP, _P, _P, _I, _P, _P], _I),
+    "tb_ffn_down": ([_MP, _P, _I, _P, _P, _P, _P], _I),
+    "tb_gemv_block_sums": ([_MP, _P, _I, _P, _P], _I),
+    "tb_status_str": ([_I], ctypes.c_char_p),
+    "tb_abi_version": ([], _I),
+}
+
+_lib: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtb.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def tb_status_str(status: int) -> str:
+    return lib().tb_status_str(int(status)).decode()
+
+
+def tb_abi_version() -> int:
+    return lib().tb_abi_version()
+
+
+class Matrix:
+    """A weight matrix on the device: codes and scales tensors plus its shape and format."""
+
+    def __init__(self, codes, scales, n: int, k: int, fmt: int):
+        self.codes, self.scales = codes, scales
+        self.n, self.k, self.fmt = int(n), int(k), int(fmt)
+        self._c = CMatrix(codes.data_ptr(), scales.data_ptr(), self.n, self.k, self.fmt)
+
+    @property
+    def c(self) -> CMatrix:
+        return self._c
+
+    @property
+    def nbytes(self) -> int:
+        return self.codes.numel() * self.codes.element_size() + \
+            self.scales.numel() * self.scales.element_size()
+
+    @classmethod
+    def upload(cls, packed, device="cuda") -> "Matrix":
+        """Copy a host matrix (synth.PackedMatrix) to the device."""
+        import torch
+        codes = torch.from_numpy(packed.codes).to(device)
+        scales = torch.from_numpy(packed.scales.view("int16")).to(device)
+        return cls(codes, scales, packed.n, packed.k, packed.fmt)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _rows(t) -> int:
+    return int(t.shape[0]) if t.dim() > 1 else 1
+
+
+def _call(name: str, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != TB_OK:
+        raise TbError(name, rc)
+
+
+def tb_rotate_quant_i8(x, q, dq, stream=None) -> None:
+    """x float32 [m][k] -> q int8 [m][k], dq float32 [m][k/128] (device tensors)."""
+    m, k = _rows(x), int(x.shape[-1])
+    _call("tb_rotate_quant_i8", x.data_ptr(), m, k, q.data_ptr(), dq.data_ptr(), _stream(stream))
+
+
+def tb_gemv_ternary(w: Matrix, q, dq, y, stream=None) -> None:
+    """y float32 [m][w.n] = GEMV of w against the int8 rows q with scales dq."""
+    _call("tb_gemv_ternary", ctypes.byref(w.c), q.data_ptr(), dq.data_ptr(), _rows(q),
+          y.data_ptr(), _stream(stream))
+
+
+def tb_ffn_gateup_silu(wg: Matrix, wu: Matrix, q, dq, h, stream=None) -> None:
+    """h float32 [m][wg.n] = silu(wg q) * (wu q), from one shared int8 copy."""
+    _call("tb_ffn_gateup_silu", ctypes.byref(wg.c), ctypes.byref(wu.c), q.data_ptr(),
+          dq.data_ptr(), _rows(q), h.data_ptr(), _stream(stream))
+
+
+def tb_ffn_down(wd: Matrix, h, qh_ws, dqh_ws, y, stream=None) -> None:
+    """y float32 [m][wd.n] = down GEMV of rotquant(h); qh_ws/dqh_ws are the workspace."""
+    _call("tb_ffn_down", ctypes.byref(wd.c), h.data_ptr(), _rows(h), qh_ws.data_ptr(),
+          dqh_ws.data_ptr(), y.data_ptr(), _stream(stream))
+
+
+def tb_gemv_block_sums(w: Matrix, q, isum, stream=None) -> None:
+    """isum int32 [m][w.n][w.k/128]: the integer block sums before the scale fold."""
+    _call("tb_gemv_block_sums", ctypes.byref(w.c), q.data_ptr(), _rows(q), isum.data_ptr(),
+          _stream(stream))

@@ -1,0 +1,33 @@
+"""Build libtb.so, the HIP library of this package, for gfx950 (in-tree)."""
+
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "tb.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libtb.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
+    # one IEEE rounding per fp32 operation: no fused multiply-add, correctly rounded division
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # no packed fp32 instructions (v_pk_*_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def build(out: str = LIB, extra: list[str] | None = None) -> str:
+    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", INCLUDE, SRC, "-o", out + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())
