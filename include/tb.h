@@ -71,7 +71,10 @@ enum tb_format {
 
 /* One weight matrix with n output rows and k inputs.
  * scales: uint16[n][nb], IEEE binary16 bit patterns, one per 128-weight
- * block. The dequantised weight is W[j][i] = scale[j][i/128] * t(j, i). */
+ * block. The dequantised weight is W[j][i] = scale[j][i/128] * t(j, i).
+ * The kernels read scales as aligned 4-byte words; when n * nb is odd the
+ * 2 bytes after the array (in the same aligned word) are read and ignored.
+ * Each of codes and scales must be smaller than 2 GiB (else TB_EUNSUPPORTED). */
 typedef struct tb_matrix {
     const void *codes;
     const uint16_t *scales;

@@ -8,6 +8,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "tb.hip")
+PROBE_SRC = os.path.join(PKG, "csrc", "probe.hip")
+PROBE_LIB = os.path.join(PKG, "libtb_probe.so")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtb.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -22,11 +24,17 @@ FLAGS = [
 ]
 
 
-def build(out: str = LIB, extra: list[str] | None = None) -> str:
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", INCLUDE, SRC, "-o", out + ".tmp"]
+def _compile(src: str, out: str, extra: list[str] | None = None) -> str:
+    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", INCLUDE, src, "-o", out + ".tmp"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out
+
+
+def build(out: str = LIB, extra: list[str] | None = None) -> str:
+    """Build libtb.so (the path) and libtb_probe.so (benchmark probes)."""
+    _compile(PROBE_SRC, PROBE_LIB)
+    return _compile(SRC, out, extra)
 
 
 if __name__ == "__main__":

@@ -6,31 +6,22 @@
 //      (rotquant_kernel);
 //   2. an integer dot-product GEMV streams the stored ternary blocks, stages the int8
 //      activation once per workgroup, folds each block's scale into its integer sum, and
-//      reduces with a lane shuffle tree (gemv_kernel);
+//      reduces with a lane shuffle tree (gemv_ring_kernel, gemv_sliced_kernel);
 //   3. packed steps of up to 8 rows give every row the bytes it gets alone: each row's lane
 //      walk, block fold and reduction tree do not depend on the row count M.
 //
 // gfx950 mapping (the pages' sm_120 design is prior art; this is the CDNA4 one):
 //   * wave64. A wave covers 4 weight rows x 16 "chunk lanes". A chunk is 16 bytes of codes:
-//     64 ternary weights (half a block) or 128 sign weights (one block). In each iteration
-//     the 16 lanes of a row read 256 contiguous bytes: fully coalesced 16-byte non-temporal
-//     loads.
-//   * 2-bit decode without a lookup in memory. For one 32-bit code word (16 weights):
-//     and-masks 0x03030303 / 0x0C0C0C0C on w and on w >> 4 give byte selectors. v_perm_b32
-//     maps each selector byte to the int8 weight {0, +1, -1, 0}; the 0x0C case uses perm's
-//     selector values 4, 8 and 12 directly. That is 9 VALU ops per 16 weights, shared by
-//     all M rows. Each resulting word holds weights {j, j+4, j+8, j+12}, so the activation
-//     is staged in LDS as a 4x4 byte transpose of every 16-byte group, and
-//     v_dot4c_i32_i8 consumes both words as they are.
-//   * The activation LDS layout is [m][code word j][chunk c] of 16-byte groups, so the 16
-//     lanes of a row read 256 consecutive bytes per ds_read_b128: no bank conflicts,
-//     without padding. The 4 row groups of a wave read the same addresses (broadcast).
-//   * The two half-block sums of a block are combined with one DPP quad_perm add (exact
-//     integers). The fp32 fold is tau = (scale * dq) * float(isum), accumulated per lane in
-//     block order, then a fixed __shfl_down tree over the lanes of the row.
-//   * The sign format uses isum = 2 * dot(bits, q) - sum(q). Bits come from shift-and
-//     (w >> j) & 0x01010101, with the activation staged as an 8x4 transpose, and sum(q) is
-//     computed once per block while staging.
+//     64 ternary weights (half a block) or 128 sign weights (one block). In each step the
+//     16 lanes of a row read 256 contiguous bytes: coalesced 16-byte non-temporal loads.
+//   * Persistent streaming (gemv_ring_kernel): one workgroup of 8 waves per CU stages the
+//     int8 activation once, then every wave walks a flat list of (row tile, chunk step)
+//     items. Loads run 8 items ahead through a register ring, so each CU keeps about
+//     64 KB of weights in flight, across row-tile boundaries too.
+//   * 2-bit decode with v_perm_b32 (9 VALU ops per 16 weights, shared by all M rows),
+//     v_dot4c_i32_i8 against the LDS-staged transposed activation, one DPP add to join the
+//     two half-block sums, an fp32 fold per block and a fixed shuffle tree per row
+//     (tb_device.h).
 //   * No MFMA: with M <= 8 rows this is not a dense contraction. No floating-point atomics.
 #include <hip/hip_runtime.h>
 
@@ -41,83 +32,31 @@
 #include <mutex>
 
 #include "tb.h"
+#include "tb_device.h"
 
 namespace {
 
-constexpr int kBlock = 128;
-constexpr int kThreads = 256;         // 4 waves
-constexpr int kRowsPerWG = 16;        // 4 waves x 4 row groups
-constexpr int kChunkLanes = 16;
+using namespace tbk;
+
+constexpr int kRotThreads = 256;
+constexpr int kSlicedThreads = 256;
+constexpr int kRingWaves = 8;
+constexpr int kRingThreads = 64 * kRingWaves;
+constexpr int kRingDepth = 8;
 
 enum Mode { kModeY = 0, kModeGateUp = 1, kModeIsum = 2 };
 
-// ------------------------------------------------------------------------------------
-// Rotate + quantise: 16 lanes per 128-block, lane L holds elements 8L .. 8L+7.
-// Stages of span 1, 2, 4 are inside a lane. Spans 8, 16, 32, 64 pair lane L with
-// L ^ 1, 2, 4, 8. Ascending order; each butterfly is (a, b) -> (a + b, a - b) in fp32.
-// ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void rotquant_kernel(const float *__restrict__ x,
-                                                            long nblocks,
-                                                            int8_t *__restrict__ q,
-                                                            float *__restrict__ dq, float unit)
+__global__ __launch_bounds__(kRotThreads) void rotquant_kernel(const float *__restrict__ x,
+                                                               long nblocks,
+                                                               int8_t *__restrict__ q,
+                                                               float *__restrict__ dq, float unit)
 {
-    const int lane16 = threadIdx.x & 15;
-    const long blk = (long)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
+    const long blk = (long)blockIdx.x * (kRotThreads / 16) + (threadIdx.x >> 4);
     if (blk >= nblocks)
-        return;  // the whole 16-lane group leaves together; shuffles stay inside a group
-
-    const float *src = x + blk * kBlock + lane16 * 8;
-    const float4 lo = *reinterpret_cast<const float4 *>(src);
-    const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
-    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (!(e & h)) {
-                const float a = v[e], b = v[e + h];
-                v[e] = a + b;
-                v[e + h] = a - b;
-            }
-        }
-    }
-#pragma unroll
-    for (int s = 1; s < 16; s <<= 1) {
-        const bool upper = (lane16 & s) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float other = __shfl_xor(v[e], s, 16);
-            v[e] = upper ? (other - v[e]) : (v[e] + other);
-        }
-    }
-
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        amax = fmaxf(amax, fabsf(v[e]));
-#pragma unroll
-    for (int s = 1; s < 16; s <<= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, s, 16));
-
-    uint32_t packed[2] = {0u, 0u};
-    if (amax != 0.0f) {
-        const float inv = 127.0f / amax;  // IEEE division (correctly rounded build)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float r = rintf(v[e] * inv);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            packed[e >> 2] |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * (e & 3));
-        }
-    }
-    *reinterpret_cast<uint2 *>(q + blk * kBlock + lane16 * 8) = make_uint2(packed[0], packed[1]);
-    if (lane16 == 0)
-        dq[blk] = amax != 0.0f ? amax * unit : 0.0f;
+        return;  // the whole 16-lane group leaves together; its shuffles stay inside it
+    rotquant16<false>(x + blk * kBlock, q + blk * kBlock, dq + blk, threadIdx.x & 15, unit);
 }
 
-// ------------------------------------------------------------------------------------
-// GEMV
-// ------------------------------------------------------------------------------------
 struct GemvArgs {
     const uint8_t *codes0;   // the matrix, or gate
     const uint16_t *scales0;
@@ -128,106 +67,168 @@ struct GemvArgs {
     const float *dq;         // [M][k/128]
     float *out;              // y or h: [M][n]
     int32_t *isum;           // block-sum export: [M][n][k/128]
-    int slice_chunks;        // chunks of K staged per LDS pass (multiple of 16)
+    int slice_chunks;        // LDS slots per pass (sliced kernel)
+    uint32_t codes_bytes;    // per matrix, < 2^31 (buffer addressing)
+    uint32_t scales_bytes;
 };
 
-__device__ __forceinline__ uint32_t byte_at(uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; }
-
-// 4x4 byte transpose: out[j] = (byte j of r0, byte j of r1, byte j of r2, byte j of r3).
-__device__ __forceinline__ uint4 transpose4x4(uint4 r)
+// Writes the results of one finished row (lane 0 of the row's 16 lanes).
+template <int M, int MODE>
+__device__ __forceinline__ void store_row(const GemvArgs &a, int row, const float (&acc0)[M],
+                                          const float (&acc1)[M])
 {
-    uint4 o;
-    o.x = byte_at(r.x, 0) | byte_at(r.y, 0) << 8 | byte_at(r.z, 0) << 16 | byte_at(r.w, 0) << 24;
-    o.y = byte_at(r.x, 1) | byte_at(r.y, 1) << 8 | byte_at(r.z, 1) << 16 | byte_at(r.w, 1) << 24;
-    o.z = byte_at(r.x, 2) | byte_at(r.y, 2) << 8 | byte_at(r.z, 2) << 16 | byte_at(r.w, 2) << 24;
-    o.w = byte_at(r.x, 3) | byte_at(r.y, 3) << 8 | byte_at(r.z, 3) << 16 | byte_at(r.w, 3) << 24;
-    return o;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        a.out[(size_t)m * a.n + row] = MODE == kModeGateUp ? silu_gate(acc0[m], acc1[m]) : acc0[m];
 }
 
-// Ternary decode of one code word into the four int8x4 words {j, j+4, j+8, j+12}.
-// Selector bytes 0..3 index the table 0x00FF0100 -> {0, +1, -1, 0}. For the masked field
-// at bits 2..3 the selector is 4c: 0 -> byte 0 of S1 (0), 4 -> byte 0 of S0 (+1),
-// 8 -> sign of bit 15 of S1 (0xFF = -1), 12 -> 0.
-__device__ __forceinline__ void decode_ternary(uint32_t w, uint32_t &d0, uint32_t &d1,
-                                               uint32_t &d2, uint32_t &d3)
-{
-    const uint32_t w4 = w >> 4;
-    d0 = __builtin_amdgcn_perm(0u, 0x00FF0100u, w & 0x03030303u);
-    d1 = __builtin_amdgcn_perm(1u, 0x00008000u, w & 0x0C0C0C0Cu);
-    d2 = __builtin_amdgcn_perm(0u, 0x00FF0100u, w4 & 0x03030303u);
-    d3 = __builtin_amdgcn_perm(1u, 0x00008000u, w4 & 0x0C0C0C0Cu);
-}
-
-__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c)
-{
-    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
-}
-
-// Swap-adjacent-lanes add: lane 2i and 2i+1 both get their sum (exact integers).
-__device__ __forceinline__ int pair_add(int v)
-{
-    return v + __builtin_amdgcn_update_dpp(0, v, 0xB1 /* quad_perm [1,0,3,2] */, 0xF, 0xF, false);
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Weights are read exactly once per call: stream them past the caches.
-__device__ __forceinline__ uint4 load_nt(const uint8_t *p)
-{
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ float half_bits_to_float(uint16_t h)
-{
-    return static_cast<float>(__builtin_bit_cast(_Float16, h));
-}
-
-__device__ __forceinline__ float silu_gate(float g, float u)
-{
-    return g / (1.0f + expf(-g)) * u;
-}
-
-// LDS layout (bytes): act [M][slice] | dq float [M][nb] | qsum int [M][nb] (sign only)
+// ------------------------------------------------------------------------------------
+// Persistent ring GEMV: the whole activation is staged once per workgroup (step-major
+// layout); waves walk their (tile, step) items with loads kRingDepth items ahead.
+// A wave owns row tiles t0, t0 + GW, t0 + 2 GW, ... (4 rows each); in step i of a tile,
+// lane cl reads chunk 16 i + cl of its row. The per-row arithmetic is the same as in every
+// other kernel here: lane cl folds its chunks in order of i, then the fixed row tree.
+//
+// The loop is written for the VALU budget: at M = 1 one 1 KB wave item needs 52 VALU ops
+// of decode and dot products, so the rest is kept to a handful. All addresses advance
+// incrementally (no multiplies); rows past n, items past the wave's work and ragged
+// chunks use out-of-range buffer offsets, which read zeros; the fold runs unconditionally
+// (an invalid lane has zero codes and a zero scale, so it adds zero).
+// ------------------------------------------------------------------------------------
 template <int M, int FMT, int MODE>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
+__global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
-    constexpr bool kTern = FMT == TB_FMT_TERNARY2;
+    using L = StepLayout<M, FMT>;
     constexpr bool kTwo = MODE == kModeGateUp;
-    constexpr int kWeightsPerChunk = kTern ? 64 : 128;
+    constexpr int kWpc = Fmt<FMT>::kWeightsPerChunk;
+    constexpr int kCpb = Fmt<FMT>::kChunksPerBlock;
+    constexpr int kBlocksPerStep = kChunkLanes / kCpb;   // 8 ternary, 16 sign
 
     const int k = a.k, n = a.n, nb = k / kBlock;
-    const int C = k / kWeightsPerChunk;          // chunks per row
-    const int S = a.slice_chunks;                // chunks per LDS pass
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, cl = lane & 15;
-    const int row = blockIdx.x * kRowsPerWG + (tid >> 6) * 4 + (lane >> 4);
-    const bool row_ok = row < n;
-    const size_t row_bytes = (size_t)C * 16;
+    const int C = k / kWpc;                 // chunks per row
+    const int I = (C + kChunkLanes - 1) / kChunkLanes;
+    const int tid = threadIdx.x, lane = tid & 63, cl = lane & 15, rl = lane >> 4;
+    // Row tiles are dealt round-robin over workgroups first, then over the waves of a
+    // workgroup: tile t goes to workgroup t % G, wave (t / G) % W. Every CU gets the same
+    // number of tiles (to within one).
+    const int gw = blockIdx.x + gridDim.x * (tid >> 6);   // this wave's first tile
+    const int GW = gridDim.x * kRingWaves;                 // tile stride between its tiles
+    const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
+    const int NT = gw < T ? (T - gw + GW - 1) / GW : 0;
+    const int J = NT * I;
+    const uint32_t row_bytes = (uint32_t)C * 16u;
 
     uint8_t *act = lds;
-    float *dq_s = reinterpret_cast<float *>(lds + (size_t)M * S * kWeightsPerChunk);
-    int *qsum_s = reinterpret_cast<int *>(dq_s + M * nb);
+    // block terms, zero padded by one step of blocks so invalid lanes read zeros
+    float *dq_s = reinterpret_cast<float *>(lds + (size_t)I * L::kStepBytes);
+    int *qsum_s = reinterpret_cast<int *>(dq_s + (size_t)(nb + kBlocksPerStep) * M);
 
-    // scales and dq (and for sign, per-block sum(q)) for the whole row are staged once
-    if (MODE != kModeIsum)
-        for (int i = tid; i < M * nb; i += kThreads)
-            dq_s[i] = a.dq[i];
-    if (!kTern) {
-        for (int i = tid; i < M * nb; i += kThreads) {
-            const int8_t *src = a.q + (size_t)i * kBlock;  // [m][b] blocks are contiguous
+    const __amdgpu_buffer_rsrc_t rout =
+        MODE == kModeIsum ? buffer_rsrc(a.isum, (uint32_t)((size_t)M * n * nb * 4))
+                          : buffer_rsrc(a.out, (uint32_t)((size_t)M * n * 4));
+    const __amdgpu_buffer_rsrc_t rc0 = buffer_rsrc(a.codes0, a.codes_bytes);
+    const __amdgpu_buffer_rsrc_t rsc0 = buffer_rsrc(a.scales0, a.scales_bytes);
+    const __amdgpu_buffer_rsrc_t rc1 = buffer_rsrc(kTwo ? a.codes1 : a.codes0, a.codes_bytes);
+    const __amdgpu_buffer_rsrc_t rsc1 = buffer_rsrc(kTwo ? a.scales1 : a.scales0, a.scales_bytes);
+
+    // ---- load-side cursor: per-lane byte offsets of the next item ---------------------
+    // Lanes whose chunk is past C in the last step of a row (ragged k) read zeros.
+    const uint32_t ragged = (C % kChunkLanes != 0 && cl >= C % kChunkLanes) ? kOutOfRange : 0u;
+    int ltile = 0, lstep = 0;
+    uint32_t lrow = (uint32_t)(gw * kRowsPerWave + rl);
+    uint32_t loff = lrow * row_bytes + (uint32_t)cl * 16u;               // codes
+    uint32_t lsoff = (lrow * (uint32_t)nb + (uint32_t)(cl / kCpb)) * 2u;  // scales
+    if (NT == 0) {
+        loff = kOutOfRange;
+        lsoff = kOutOfRange;
+    }
+
+    uint4 rb0[kRingDepth], rb1[kRingDepth];
+    // scales travel as 32-bit values: 16-bit ring entries would be packed in pairs, and
+    // packing waits for the loads
+    uint32_t rs0[kRingDepth], rs1[kRingDepth];
+    auto issue = [&](uint4 &w0, uint4 &w1, uint32_t &s0, uint32_t &s1) {
+        const uint32_t extra = lstep == I - 1 ? ragged : 0u;
+        w0 = buffer_load16_nt(rc0, loff + extra);
+        s0 = buffer_load_u32(rsc0, (lsoff & ~3u) + extra);
+        if (kTwo) {
+            w1 = buffer_load16_nt(rc1, loff + extra);
+            s1 = buffer_load_u32(rsc1, (lsoff & ~3u) + extra);
+        } else {
+            w1 = make_uint4(0, 0, 0, 0);
+            s1 = 0;
+        }
+        if (++lstep == I) {
+            lstep = 0;
+            ++ltile;
+            lrow += (uint32_t)(GW * kRowsPerWave);
+            if (ltile < NT) {
+                loff = lrow * row_bytes + (uint32_t)cl * 16u;
+                lsoff = (lrow * (uint32_t)nb + (uint32_t)(cl / kCpb)) * 2u;
+            } else {
+                loff = kOutOfRange;
+                lsoff = kOutOfRange;
+            }
+        } else {
+            loff += 16u * kChunkLanes;
+            lsoff += 2u * kBlocksPerStep;
+        }
+    };
+
+    // ---- first staging round, ring prologue, rest of the staging -------------------
+    constexpr int kStageRound = 4;
+    const int units = M * C * 4;
+    StageUnit<FMT> su[kStageRound];
+#pragma unroll
+    for (int r = 0; r < kStageRound; ++r)
+        if (tid + r * kRingThreads < units)
+            stage_unit_load_step<M, FMT, false>(su[r], a.q, k, tid + r * kRingThreads);
+#pragma unroll
+    for (int d = 0; d < kRingDepth; ++d)
+        issue(rb0[d], rb1[d], rs0[d], rs1[d]);
+#pragma unroll
+    for (int r = 0; r < kStageRound; ++r)
+        if (tid + r * kRingThreads < units)
+            stage_unit_store_step<M, FMT>(su[r], act, k, tid + r * kRingThreads);
+    for (int u = tid + kStageRound * kRingThreads; u < units; u += kRingThreads) {
+        StageUnit<FMT> one;
+        stage_unit_load_step<M, FMT, false>(one, a.q, k, u);
+        stage_unit_store_step<M, FMT>(one, act, k, u);
+    }
+    // block terms [b][m] (transposed from the [m][b] input) plus zero padding
+    for (int i = tid; i < (nb + kBlocksPerStep) * M; i += kRingThreads) {
+        const int b = i / M, m = i % M;
+        dq_s[i] = (MODE != kModeIsum && b < nb) ? a.dq[m * nb + b] : 0.0f;
+        if (FMT == TB_FMT_SIGN1) {
             int s = 0;
-            for (int j = 0; j < kBlock; j += 16) {
-                const uint4 g = *reinterpret_cast<const uint4 *>(src + j);
-                s = dot4(g.x, 0x01010101u, s);
-                s = dot4(g.y, 0x01010101u, s);
-                s = dot4(g.z, 0x01010101u, s);
-                s = dot4(g.w, 0x01010101u, s);
+            if (b < nb) {
+                const int8_t *src = a.q + (size_t)m * k + (size_t)b * kBlock;
+                for (int j = 0; j < kBlock; j += 16) {
+                    const uint4 g = *reinterpret_cast<const uint4 *>(src + j);
+                    s = dot4(g.x, 0x01010101u, s);
+                    s = dot4(g.y, 0x01010101u, s);
+                    s = dot4(g.z, 0x01010101u, s);
+                    s = dot4(g.w, 0x01010101u, s);
+                }
             }
             qsum_s[i] = s;
         }
     }
+    __syncthreads();
+
+    // ---- compute-side cursor ----------------------------------------------------------
+    const uint8_t *lds_lane = act + cl * 16;
+    const int blk_lane = cl / kCpb;                 // block of this lane within a step
+    int cstep = 0, ctile = 0;
+    int crow = gw * kRowsPerWave + rl;
+    const uint8_t *cact = lds_lane;
+    const float *cdq = dq_s + blk_lane * M;
+    const int *cqs = qsum_s + blk_lane * M;
+    uint32_t cisum = ((uint32_t)crow * (uint32_t)nb + (uint32_t)blk_lane) * 4u;   // isum export
+    // which half of a scale word belongs to this lane: the parity of its block index,
+    // fixed within a row tile because a step advances the block by an even count
+    uint32_t cshift = (((uint32_t)crow * (uint32_t)nb + (uint32_t)blk_lane) & 1u) * 16u;
 
     float acc0[M], acc1[M];
 #pragma unroll
@@ -235,183 +236,147 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
         acc0[m] = 0.0f;
         acc1[m] = 0.0f;
     }
+    const int Jpad = (J + kRingDepth - 1) / kRingDepth * kRingDepth;
+    for (int j0 = 0; j0 < Jpad; j0 += kRingDepth) {
+#pragma unroll
+        for (int d = 0; d < kRingDepth; ++d) {
+            // Consume the slot first, then refill it: the refill reuses the slot's
+            // registers (no copy at the loop latch, which would wait for every load), and
+            // the scheduling barrier keeps consume/refill interleaved slot by slot.
+            int is0[M], is1[M];
+            chunk_sums_step<M, FMT, kTwo>(rb0[d], rb1[d], cact, is0, is1);
+            // the scale is the half of the loaded word at bit cshift (0 or 16)
+            const float s0 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(rs0[d], cshift, 16));
+            const float s1 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(rs1[d], cshift, 16));
+            if (MODE == kModeIsum) {
+                // the export writes every valid block once (even lane of a ternary pair)
+                const bool wr = ctile < NT && crow < n &&
+                                cstep * kChunkLanes + cl < C && (kCpb == 1 || !(cl & 1));
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const int v = FMT == TB_FMT_SIGN1 ? 2 * is0[m] - cqs[m] : is0[m];
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        (uint32_t)v, rout, wr ? cisum : kOutOfRange, m * n * nb * 4, 0);
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    int v0 = is0[m], v1 = is1[m];
+                    if (FMT == TB_FMT_SIGN1) {
+                        v0 = 2 * v0 - cqs[m];
+                        v1 = 2 * v1 - cqs[m];
+                    }
+                    const float dqv = cdq[m];
+                    acc0[m] += (s0 * dqv) * (float)v0;
+                    if (kTwo)
+                        acc1[m] += (s1 * dqv) * (float)v1;
+                }
+            }
+            issue(rb0[d], rb1[d], rs0[d], rs1[d]);
+            if (++cstep == I) {
+                // end of a row tile: tree, store, reset (wave-uniform branch)
+                if (MODE != kModeIsum) {
+                    row_tree<M, FMT, kTwo>(acc0, acc1);
+                    const bool wr = ctile < NT && cl == 0 && crow < n;
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        buffer_store_f32(rout, wr ? (uint32_t)crow * 4u : kOutOfRange,
+                                         kTwo ? silu_gate(acc0[m], acc1[m]) : acc0[m], m * n * 4);
+                        acc0[m] = 0.0f;
+                        acc1[m] = 0.0f;
+                    }
+                }
+                cstep = 0;
+                ++ctile;
+                crow += GW * kRowsPerWave;
+                cact = lds_lane;
+                cdq = dq_s + blk_lane * M;
+                cqs = qsum_s + blk_lane * M;
+                cisum = ((uint32_t)crow * (uint32_t)nb + (uint32_t)blk_lane) * 4u;
+                cshift = (((uint32_t)crow * (uint32_t)nb + (uint32_t)blk_lane) & 1u) * 16u;
+            } else {
+                cact += L::kStepBytes;
+                cdq += kBlocksPerStep * M;
+                cqs += kBlocksPerStep * M;
+                cisum += kBlocksPerStep * 4u;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
 
+// ------------------------------------------------------------------------------------
+// Sliced GEMV: for a K * M too large to stage at once. The activation is staged in
+// slices of S chunks; each workgroup covers 16 rows. The per-row arithmetic is the same
+// as in the ring kernel: lane cl folds chunks 16 i + cl in order of i.
+// ------------------------------------------------------------------------------------
+template <int M, int FMT, int MODE>
+__global__ __launch_bounds__(kSlicedThreads) void gemv_sliced_kernel(GemvArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    constexpr bool kTwo = MODE == kModeGateUp;
+    constexpr int kWpc = Fmt<FMT>::kWeightsPerChunk;
+    constexpr int kCpb = Fmt<FMT>::kChunksPerBlock;
+
+    const int k = a.k, n = a.n, nb = k / kBlock;
+    const int C = k / kWpc;
+    const int S = a.slice_chunks;
+    const int tid = threadIdx.x, lane = tid & 63, cl = lane & 15;
+    const int row = blockIdx.x * (kSlicedThreads / 64) * kRowsPerWave + (tid >> 6) * 4 + (lane >> 4);
+    const bool row_ok = row < n;
+    const size_t row_bytes = (size_t)C * 16;
+
+    uint8_t *act = lds;
+    float *dq_s = reinterpret_cast<float *>(lds + (size_t)M * S * kWpc);
+    int *qsum_s = reinterpret_cast<int *>(dq_s + M * nb);
+    stage_block_terms<M, FMT, false>(dq_s, qsum_s, a.dq, a.q, nb, MODE != kModeIsum, tid,
+                                     kSlicedThreads);
+
+    float acc0[M], acc1[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        acc0[m] = 0.0f;
+        acc1[m] = 0.0f;
+    }
     const uint8_t *rp0 = a.codes0 + (size_t)(row_ok ? row : 0) * row_bytes;
     const uint8_t *rp1 = kTwo ? a.codes1 + (size_t)(row_ok ? row : 0) * row_bytes : nullptr;
     const uint16_t *sp0 = a.scales0 + (size_t)(row_ok ? row : 0) * nb;
     const uint16_t *sp1 = kTwo ? a.scales1 + (size_t)(row_ok ? row : 0) * nb : nullptr;
 
     for (int c0 = 0; c0 < C; c0 += S) {
-        const int sc = min(S, C - c0);  // chunks in this slice
-        __syncthreads();                // previous slice fully consumed
-        // ---- stage q[:, c0 .. c0+sc) into LDS, transposed -----------------------------
-        if (kTern) {
-            // one unit = 16 activations = one code word's worth
-            const int units = M * sc * 4;
-            for (int u = tid; u < units; u += kThreads) {
-                const int m = u / (sc * 4), g = u % (sc * 4);
-                const int c = g >> 2, j = g & 3;
-                const uint4 r = *reinterpret_cast<const uint4 *>(
-                    a.q + (size_t)m * k + (size_t)(c0 + c) * 64 + j * 16);
-                *reinterpret_cast<uint4 *>(act + (size_t)m * S * 64 + ((size_t)j * S + c) * 16) =
-                    transpose4x4(r);
-            }
-        } else {
-            // one unit = 32 activations = one dword of sign bits; 8 words out (2 x uint4)
-            const int units = M * sc * 4;
-            for (int u = tid; u < units; u += kThreads) {
-                const int m = u / (sc * 4), g = u % (sc * 4);
-                const int c = g >> 2, d = g & 3;
-                const uint8_t *src = reinterpret_cast<const uint8_t *>(a.q) + (size_t)m * k +
-                                     (size_t)(c0 + c) * 128 + d * 32;
-                const uint4 lo = *reinterpret_cast<const uint4 *>(src);
-                const uint4 hi = *reinterpret_cast<const uint4 *>(src + 16);
-                const uint32_t r[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                // word j = (q[j], q[8+j], q[16+j], q[24+j]); q[8p+j] is byte j&3 of r[2p + j/4]
-                uint32_t o[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    o[j] = byte_at(r[0 + (j >> 2)], j & 3) | byte_at(r[2 + (j >> 2)], j & 3) << 8 |
-                           byte_at(r[4 + (j >> 2)], j & 3) << 16 |
-                           byte_at(r[6 + (j >> 2)], j & 3) << 24;
-                uint8_t *dst = act + (size_t)m * S * 128;
-                *reinterpret_cast<uint4 *>(dst + ((size_t)(d * 2 + 0) * S + c) * 16) =
-                    make_uint4(o[0], o[1], o[2], o[3]);
-                *reinterpret_cast<uint4 *>(dst + ((size_t)(d * 2 + 1) * S + c) * 16) =
-                    make_uint4(o[4], o[5], o[6], o[7]);
-            }
-        }
+        const int sc = min(S, C - c0);
+        __syncthreads();   // previous slice consumed
+        stage_act<M, FMT, false>(act, S, a.q, k, c0, sc, tid, kSlicedThreads);
         __syncthreads();
-
-        // ---- stream this slice's codes -------------------------------------------------
         for (int cc = cl; cc < ((sc + 15) & ~15); cc += kChunkLanes) {
             const int c = c0 + cc;
             const bool ok = row_ok && cc < sc;
+            const int b = c / kCpb;
             const uint4 w0 = ok ? load_nt(rp0 + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
             const uint4 w1 = (kTwo && ok) ? load_nt(rp1 + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
-            const int b = kTern ? (c >> 1) : c;
             const float s0 = ok ? half_bits_to_float(sp0[b]) : 0.0f;
             const float s1 = (kTwo && ok) ? half_bits_to_float(sp1[b]) : 0.0f;
-
             int is0[M], is1[M];
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                is0[m] = 0;
-                is1[m] = 0;
-            }
-            if (kTern) {
-                const uint32_t cw0[4] = {w0.x, w0.y, w0.z, w0.w};
-                const uint32_t cw1[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t d0, d1, d2, d3, e0 = 0, e1 = 0, e2 = 0, e3 = 0;
-                    decode_ternary(cw0[j], d0, d1, d2, d3);
-                    if (kTwo)
-                        decode_ternary(cw1[j], e0, e1, e2, e3);
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        const uint4 av = *reinterpret_cast<const uint4 *>(
-                            act + (size_t)m * S * 64 + ((size_t)j * S + (ok ? cc : 0)) * 16);
-                        is0[m] = dot4(d0, av.x, is0[m]);
-                        is0[m] = dot4(d1, av.y, is0[m]);
-                        is0[m] = dot4(d2, av.z, is0[m]);
-                        is0[m] = dot4(d3, av.w, is0[m]);
-                        if (kTwo) {
-                            is1[m] = dot4(e0, av.x, is1[m]);
-                            is1[m] = dot4(e1, av.y, is1[m]);
-                            is1[m] = dot4(e2, av.z, is1[m]);
-                            is1[m] = dot4(e3, av.w, is1[m]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    is0[m] = pair_add(is0[m]);
-                    if (kTwo)
-                        is1[m] = pair_add(is1[m]);
-                }
-            } else {
-                const uint32_t cw0[4] = {w0.x, w0.y, w0.z, w0.w};
-                const uint32_t cw1[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        uint32_t bits0[4], bits1[4] = {0, 0, 0, 0};
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            bits0[j] = (cw0[d] >> (4 * h + j)) & 0x01010101u;
-                            if (kTwo)
-                                bits1[j] = (cw1[d] >> (4 * h + j)) & 0x01010101u;
-                        }
-#pragma unroll
-                        for (int m = 0; m < M; ++m) {
-                            const uint4 av = *reinterpret_cast<const uint4 *>(
-                                act + (size_t)m * S * 128 +
-                                ((size_t)(d * 2 + h) * S + (ok ? cc : 0)) * 16);
-                            is0[m] = dot4(bits0[0], av.x, is0[m]);
-                            is0[m] = dot4(bits0[1], av.y, is0[m]);
-                            is0[m] = dot4(bits0[2], av.z, is0[m]);
-                            is0[m] = dot4(bits0[3], av.w, is0[m]);
-                            if (kTwo) {
-                                is1[m] = dot4(bits1[0], av.x, is1[m]);
-                                is1[m] = dot4(bits1[1], av.y, is1[m]);
-                                is1[m] = dot4(bits1[2], av.z, is1[m]);
-                                is1[m] = dot4(bits1[3], av.w, is1[m]);
-                            }
-                        }
-                    }
-                }
-                if (ok) {
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        const int qs = qsum_s[m * nb + b];
-                        is0[m] = 2 * is0[m] - qs;
-                        if (kTwo)
-                            is1[m] = 2 * is1[m] - qs;
-                    }
-                }
-            }
-
+            chunk_sums<M, FMT, kTwo>(w0, w1, act, S, ok ? cc : 0, is0, is1);
             if (!ok)
                 continue;
             if (MODE == kModeIsum) {
-                if (!kTern || !(cl & 1)) {
+                if (kCpb == 1 || !(cl & 1)) {
 #pragma unroll
                     for (int m = 0; m < M; ++m)
-                        a.isum[((size_t)m * n + row) * nb + b] = is0[m];
+                        a.isum[((size_t)m * n + row) * nb + b] =
+                            FMT == TB_FMT_SIGN1 ? 2 * is0[m] - qsum_s[m * nb + b] : is0[m];
                 }
                 continue;
             }
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const float d = dq_s[m * nb + b];
-                acc0[m] += (s0 * d) * (float)is0[m];
-                if (kTwo)
-                    acc1[m] += (s1 * d) * (float)is1[m];
-            }
+            fold_chunk<M, FMT, kTwo>(is0, is1, s0, s1, dq_s, qsum_s, nb, b, acc0, acc1);
         }
     }
-
     if (MODE == kModeIsum)
         return;
-
-    // ---- shuffle tree over the lanes of each row (odd lanes of the ternary format hold
-    //      duplicates of their even neighbour, so they are skipped) -------------------------
-#pragma unroll
-    for (int off = kTern ? 2 : 1; off < kChunkLanes; off <<= 1) {
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            acc0[m] += __shfl_down(acc0[m], off, kChunkLanes);
-            if (kTwo)
-                acc1[m] += __shfl_down(acc1[m], off, kChunkLanes);
-        }
-    }
-    if (cl == 0 && row_ok) {
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            a.out[(size_t)m * n + row] = kTwo ? silu_gate(acc0[m], acc1[m]) : acc0[m];
-    }
+    row_tree<M, FMT, kTwo>(acc0, acc1);
+    if (cl == 0 && row_ok)
+        store_row<M, MODE>(a, row, acc0, acc1);
 }
 
 // ------------------------------------------------------------------------------------
@@ -419,52 +384,62 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a)
 // ------------------------------------------------------------------------------------
 using GemvFn = void (*)(GemvArgs);
 
-template <int FMT, int MODE>
-GemvFn pick_gemv(int m)
-{
-    switch (m) {
-    case 1: return gemv_kernel<1, FMT, MODE>;
-    case 2: return gemv_kernel<2, FMT, MODE>;
-    case 3: return gemv_kernel<3, FMT, MODE>;
-    case 4: return gemv_kernel<4, FMT, MODE>;
-    case 5: return gemv_kernel<5, FMT, MODE>;
-    case 6: return gemv_kernel<6, FMT, MODE>;
-    case 7: return gemv_kernel<7, FMT, MODE>;
-    case 8: return gemv_kernel<8, FMT, MODE>;
-    default: return nullptr;
+#define TB_KERNEL_TABLE(NAME)                                                                  \
+    template <int FMT, int MODE>                                                               \
+    GemvFn NAME##_pick_m(int m)                                                                \
+    {                                                                                          \
+        switch (m) {                                                                           \
+        case 1: return NAME<1, FMT, MODE>;                                                     \
+        case 2: return NAME<2, FMT, MODE>;                                                     \
+        case 3: return NAME<3, FMT, MODE>;                                                     \
+        case 4: return NAME<4, FMT, MODE>;                                                     \
+        case 5: return NAME<5, FMT, MODE>;                                                     \
+        case 6: return NAME<6, FMT, MODE>;                                                     \
+        case 7: return NAME<7, FMT, MODE>;                                                     \
+        case 8: return NAME<8, FMT, MODE>;                                                     \
+        default: return nullptr;                                                               \
+        }                                                                                      \
+    }                                                                                          \
+    GemvFn NAME##_pick(int fmt, int mode, int m)                                               \
+    {                                                                                          \
+        if (fmt == TB_FMT_TERNARY2) {                                                          \
+            if (mode == kModeY) return NAME##_pick_m<TB_FMT_TERNARY2, kModeY>(m);               \
+            if (mode == kModeGateUp) return NAME##_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m);     \
+            return NAME##_pick_m<TB_FMT_TERNARY2, kModeIsum>(m);                               \
+        }                                                                                      \
+        if (mode == kModeY) return NAME##_pick_m<TB_FMT_SIGN1, kModeY>(m);                      \
+        if (mode == kModeGateUp) return NAME##_pick_m<TB_FMT_SIGN1, kModeGateUp>(m);            \
+        return NAME##_pick_m<TB_FMT_SIGN1, kModeIsum>(m);                                      \
     }
-}
 
-GemvFn pick(int fmt, int mode, int m)
-{
-    if (fmt == TB_FMT_TERNARY2) {
-        if (mode == kModeY) return pick_gemv<TB_FMT_TERNARY2, kModeY>(m);
-        if (mode == kModeGateUp) return pick_gemv<TB_FMT_TERNARY2, kModeGateUp>(m);
-        return pick_gemv<TB_FMT_TERNARY2, kModeIsum>(m);
-    }
-    if (mode == kModeY) return pick_gemv<TB_FMT_SIGN1, kModeY>(m);
-    if (mode == kModeGateUp) return pick_gemv<TB_FMT_SIGN1, kModeGateUp>(m);
-    return pick_gemv<TB_FMT_SIGN1, kModeIsum>(m);
-}
+TB_KERNEL_TABLE(gemv_ring_kernel)
+TB_KERNEL_TABLE(gemv_sliced_kernel)
 
 constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+    int lds_limit = 0;   // 0 = not queried yet
+    int cus = 0;
+};
 std::mutex g_mu;
-int g_lds_limit[kMaxDevices];  // 0 = not queried yet
+DeviceInfo g_dev[kMaxDevices];
 
-int device_lds_limit(int *limit)
+int device_info(DeviceInfo *out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return TB_EHIP;
     std::lock_guard<std::mutex> lock(g_mu);
-    if (g_lds_limit[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-            v <= 0)
+    DeviceInfo &d = g_dev[dev];
+    if (d.lds_limit == 0) {
+        int lds = 0, cus = 0;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            lds <= 0 || cus <= 0)
             return TB_EHIP;
-        g_lds_limit[dev] = v;
+        d.lds_limit = lds;
+        d.cus = cus;
     }
-    *limit = g_lds_limit[dev];
+    *out = d;
     return TB_OK;
 }
 
@@ -486,6 +461,11 @@ int check_matrix(const tb_matrix *w)
         return TB_EINVAL;
     if (!aligned16(w->codes) || !aligned16(w->scales))
         return TB_EALIGN;
+    // buffer addressing: each array must stay below 2 GiB
+    const size_t nb = (size_t)(w->k / kBlock);
+    const size_t cb = (size_t)w->n * (size_t)w->k / (w->fmt == TB_FMT_TERNARY2 ? 4 : 8);
+    if (cb >= ((size_t)1 << 31) || (size_t)w->n * nb * 2 >= ((size_t)1 << 31))
+        return TB_EUNSUPPORTED;
     return TB_OK;
 }
 
@@ -497,41 +477,37 @@ size_t scales_bytes(const tb_matrix *w) { return (size_t)w->n * (size_t)(w->k / 
 
 int check_rows(int m) { return (m >= 1 && m <= TB_MAX_ROWS) ? TB_OK : TB_EINVAL; }
 
+float dq_unit() { return static_cast<float>(1.0 / (127.0 * std::sqrt(128.0))); }
+
 int launch_rotquant(const float *x, int m, int k, int8_t *q, float *dq, hipStream_t stream)
 {
     const long nblocks = (long)m * (k / kBlock);
-    const int grid = (int)((nblocks + kThreads / 16 - 1) / (kThreads / 16));
-    const float unit = static_cast<float>(1.0 / (127.0 * std::sqrt(128.0)));
-    hipLaunchKernelGGL(rotquant_kernel, dim3(grid), dim3(kThreads), 0, stream, x, nblocks, q, dq,
-                       unit);
+    const int grid = (int)((nblocks + kRotThreads / 16 - 1) / (kRotThreads / 16));
+    hipLaunchKernelGGL(rotquant_kernel, dim3(grid), dim3(kRotThreads), 0, stream, x, nblocks, q,
+                       dq, dq_unit());
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
-// LDS bytes for a given slice; the slice shrinks until the workgroup fits the device limit.
-int plan_lds(int fmt, int m, int k, int limit, int *slice_chunks, size_t *lds_bytes)
+size_t block_terms_bytes(int fmt, int m, int nb)
 {
-    const int wpc = fmt == TB_FMT_TERNARY2 ? 64 : 128;
-    const int C = k / wpc, nb = k / kBlock;
-    const size_t fixed = (size_t)m * nb * 4 * (fmt == TB_FMT_TERNARY2 ? 1 : 2);
-    int S = (C + 15) & ~15;
-    for (;;) {
-        const size_t bytes = (size_t)m * S * wpc + fixed;
-        if (bytes <= (size_t)limit) {
-            *slice_chunks = S;
-            *lds_bytes = bytes;
-            return TB_OK;
-        }
-        if (S <= 16)
-            return TB_EUNSUPPORTED;
-        S = ((S / 2) + 15) & ~15;
-    }
+    return (size_t)m * nb * 4 * (fmt == TB_FMT_TERNARY2 ? 1 : 2);
+}
+
+int set_lds(GemvFn fn, size_t lds)
+{
+    if (lds <= 65536)
+        return TB_OK;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess
+               ? TB_OK
+               : TB_EHIP;
 }
 
 int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t *q,
                 const float *dq, int m, float *out, int32_t *isum, hipStream_t stream)
 {
-    int limit = 0;
-    int rc = device_lds_limit(&limit);
+    DeviceInfo info;
+    int rc = device_info(&info);
     if (rc)
         return rc;
     GemvArgs a;
@@ -545,32 +521,52 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     a.dq = dq;
     a.out = out;
     a.isum = isum;
-    size_t lds = 0;
-    rc = plan_lds(w0->fmt, m, w0->k, limit, &a.slice_chunks, &lds);
-    if (rc)
-        return rc;
-    GemvFn fn = pick(w0->fmt, mode, m);
+    a.codes_bytes = (uint32_t)codes_bytes(w0);
+    // scales are read as aligned 4-byte words: when n * nb is odd the last word's upper
+    // half lies past the array, inside the same aligned word (which cannot cross a page),
+    // and is ignored
+    a.scales_bytes = (uint32_t)((scales_bytes(w0) + 3) & ~(size_t)3);
+    const int wpc = w0->fmt == TB_FMT_TERNARY2 ? 64 : 128;
+    const int C = w0->k / wpc, nb = w0->k / kBlock;
+    const size_t terms = block_terms_bytes(w0->fmt, m, nb);
+
+    // whole activation in LDS: the persistent ring kernel, one workgroup per CU
+    const int steps = (C + kChunkLanes - 1) / kChunkLanes;
+    const size_t step_bytes = (size_t)(w0->fmt == TB_FMT_TERNARY2 ? 1024 : 2048) * m;
+    const size_t pad_blocks = (size_t)(kChunkLanes / (w0->fmt == TB_FMT_TERNARY2 ? 2 : 1));
+    const size_t ring_terms = (size_t)m * (nb + pad_blocks) * 4 * (w0->fmt == TB_FMT_TERNARY2 ? 1 : 2);
+    const size_t ring_lds = (size_t)steps * step_bytes + ring_terms;
+    if (ring_lds <= (size_t)info.lds_limit) {
+        GemvFn fn = gemv_ring_kernel_pick(w0->fmt, mode, m);
+        if (!fn)
+            return TB_EINVAL;
+        if ((rc = set_lds(fn, ring_lds)))
+            return rc;
+        // one workgroup per CU (fewer only if there are fewer row tiles than CUs)
+        const long tiles = (w0->n + kRowsPerWave - 1) / kRowsPerWave;
+        const int grid = (int)(tiles < info.cus ? tiles : info.cus);
+        a.slice_chunks = C;
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(kRingThreads), ring_lds, stream, a);
+        return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+    }
+    // otherwise stage the activation in slices of S chunks (S a multiple of 16)
+    int S = (C + 15) & ~15;
+    while ((size_t)m * S * wpc + terms > (size_t)info.lds_limit) {
+        if (S <= 16)
+            return TB_EUNSUPPORTED;
+        S = ((S / 2) + 15) & ~15;
+    }
+    const size_t lds = (size_t)m * S * wpc + terms;
+    GemvFn fn = gemv_sliced_kernel_pick(w0->fmt, mode, m);
     if (!fn)
         return TB_EINVAL;
-    if (lds > 65536 &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return TB_EHIP;
-    const int grid = (w0->n + kRowsPerWG - 1) / kRowsPerWG;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, stream, a);
+    if ((rc = set_lds(fn, lds)))
+        return rc;
+    a.slice_chunks = S;
+    const int rows_per_wg = (kSlicedThreads / 64) * kRowsPerWave;
+    const int grid = (w0->n + rows_per_wg - 1) / rows_per_wg;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kSlicedThreads), lds, stream, a);
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
-}
-
-// Validates a GEMV-shaped call: activations q/dq of m rows against matrix w.
-int check_activation(const tb_matrix *w, const int8_t *q, const float *dq, int m)
-{
-    if (!q || !dq)
-        return TB_EINVAL;
-    if (!aligned16(q) || !aligned16(dq))
-        return TB_EALIGN;
-    (void)w;
-    (void)m;
-    return TB_OK;
 }
 
 }  // namespace
@@ -613,11 +609,9 @@ int tb_gemv_ternary(const tb_matrix *w, const int8_t *q, const float *dq, int m,
     int rc = check_matrix(w);
     if (rc)
         return rc;
-    if (check_rows(m) || !y)
+    if (check_rows(m) || !y || !q || !dq)
         return TB_EINVAL;
-    if ((rc = check_activation(w, q, dq, m)))
-        return rc;
-    if (!aligned16(y))
+    if (!aligned16(q) || !aligned16(dq) || !aligned16(y))
         return TB_EALIGN;
     const Range ry = range_of(y, (size_t)m * w->n * 4);
     if (overlaps(ry, range_of(w->codes, codes_bytes(w))) ||
@@ -638,11 +632,9 @@ int tb_ffn_gateup_silu(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q
         return rc;
     if (wg->n != wu->n || wg->k != wu->k || wg->fmt != wu->fmt)
         return TB_EINVAL;
-    if (check_rows(m) || !h)
+    if (check_rows(m) || !h || !q || !dq)
         return TB_EINVAL;
-    if ((rc = check_activation(wg, q, dq, m)))
-        return rc;
-    if (!aligned16(h))
+    if (!aligned16(q) || !aligned16(dq) || !aligned16(h))
         return TB_EALIGN;
     const Range rh = range_of(h, (size_t)m * wg->n * 4);
     if (overlaps(rh, range_of(wg->codes, codes_bytes(wg))) ||
@@ -697,7 +689,8 @@ int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum
         return TB_EALIGN;
     const Range ri = range_of(isum, (size_t)m * w->n * (w->k / kBlock) * 4);
     if (overlaps(ri, range_of(w->codes, codes_bytes(w))) ||
-        overlaps(ri, range_of(w->scales, scales_bytes(w))) || overlaps(ri, range_of(q, (size_t)m * w->k)))
+        overlaps(ri, range_of(w->scales, scales_bytes(w))) ||
+        overlaps(ri, range_of(q, (size_t)m * w->k)))
         return TB_EINVAL;
     return launch_gemv(kModeIsum, w, nullptr, q, nullptr, m, nullptr, isum,
                        static_cast<hipStream_t>(stream));

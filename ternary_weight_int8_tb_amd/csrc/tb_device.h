@@ -1,0 +1,572 @@
+// tb_device.h -- device building blocks of the ternary-weight int8 FFN kernels (gfx950).
+//
+// Included by tb.hip only. Every block here is shared by all entry points, so that
+// one weight row is computed the same way whichever kernel runs it: the same lane walk
+// over its chunks, the same block fold order and the same reduction tree, for every row
+// count M. The pages state this property for the batched kernel ("perf(bonsai): decode and
+// small packed batches read the FFN from a ternary copy through a dp4a GEMV",
+// sparkinfer PR #1154, commit message): each row's lane walk, per-block fold and shuffle
+// tree are unchanged, so a batched row is bit-identical to its single-row run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tb.h"
+
+namespace tbk {
+
+constexpr int kBlock = 128;
+constexpr int kChunkLanes = 16;   // lanes that share one weight row
+constexpr int kRowsPerWave = 4;   // 64 lanes / 16
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<TB_FMT_TERNARY2> {
+    static constexpr int kWeightsPerChunk = 64;   // 16 bytes of 2-bit codes, half a block
+    static constexpr int kChunksPerBlock = 2;
+};
+template <>
+struct Fmt<TB_FMT_SIGN1> {
+    static constexpr int kWeightsPerChunk = 128;  // 16 bytes of sign bits, one block
+    static constexpr int kChunksPerBlock = 1;
+};
+
+__device__ __forceinline__ uint32_t byte_at(uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; }
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c)
+{
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// Weights are read exactly once per call: stream them past the caches.
+__device__ __forceinline__ uint4 load_nt(const uint8_t *p)
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Raw buffer descriptors (gfx9 layout: stride 0, num_records in bytes, 32-bit data format).
+// A load whose offset is past num_records returns zeros and touches no memory: the
+// streaming loops use that instead of branches, so every slot issues the same loads and
+// the compiler can keep many of them in flight.
+constexpr uint32_t kBufWord3 = 0x00020000u;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // callers keep num_records below this
+constexpr int kAuxNonTemporal = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             (int)kBufWord3);
+}
+
+__device__ __forceinline__ uint4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNonTemporal);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint16_t buffer_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// The 4-byte word holding the 2-byte value at byte offset off (off & ~3). A 32-bit ring
+// entry needs no zero-extension, which the compiler would otherwise place at the loop
+// latch, where it waits for every outstanding load.
+__device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// soffset: a wave-uniform byte offset added to off (not part of the range check).
+__device__ __forceinline__ void buffer_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v,
+                                                 int soffset = 0)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, soffset, 0);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+__device__ __forceinline__ float silu_gate(float g, float u)
+{
+    return g / (1.0f + expf(-g)) * u;
+}
+
+// Swap-adjacent-lanes add: lanes 2i and 2i+1 both get their sum (exact integers).
+__device__ __forceinline__ int pair_add(int v)
+{
+    return v + __builtin_amdgcn_update_dpp(0, v, 0xB1 /* quad_perm [1,0,3,2] */, 0xF, 0xF, false);
+}
+
+// Ternary decode of one 32-bit code word (16 weights) into four int8x4 words; word j
+// holds weights {j, j+4, j+8, j+12}. Selector bytes 0..3 index the table 0x00FF0100 ->
+// {0, +1, -1, 0}. For the field masked in place at bits 2..3 the selector is 4c:
+// 0 -> byte 0 of S1 (0), 4 -> byte 0 of S0 (+1), 8 -> sign of bit 15 of S1 (0xFF = -1),
+// 12 -> 0. Nine VALU operations, shared by all rows of the batch.
+__device__ __forceinline__ void decode_ternary(uint32_t w, uint32_t &d0, uint32_t &d1,
+                                               uint32_t &d2, uint32_t &d3)
+{
+    const uint32_t w4 = w >> 4;
+    d0 = __builtin_amdgcn_perm(0u, 0x00FF0100u, w & 0x03030303u);
+    d1 = __builtin_amdgcn_perm(1u, 0x00008000u, w & 0x0C0C0C0Cu);
+    d2 = __builtin_amdgcn_perm(0u, 0x00FF0100u, w4 & 0x03030303u);
+    d3 = __builtin_amdgcn_perm(1u, 0x00008000u, w4 & 0x0C0C0C0Cu);
+}
+
+// ------------------------------------------------------------------------------------
+// Rotate + quantise one 128-block with a 16-lane group. Lane L holds elements
+// 8L .. 8L+7. Butterfly spans 1, 2, 4 are inside the lane; spans 8, 16, 32, 64 pair lane L
+// with L ^ 1, 2, 4, 8. Ascending order, each (a, b) -> (a + b, a - b) in fp32. Then
+// amax = max |u|; if amax != 0, q = rint(u * (127 / amax)) (IEEE division, ties to
+// even) and dq = amax * unit; else q = 0 and dq = 0. Writes 8 q bytes per lane, and dq
+// from lane 0 of the group.
+// ------------------------------------------------------------------------------------
+template <bool kCoherentIO>
+__device__ __forceinline__ void rotquant16(const float *src, int8_t *qdst, float *dqdst,
+                                           int lane16, float unit)
+{
+    float v[8];
+    if (kCoherentIO) {
+        // data written by other workgroups of the same launch: read it device-coherently
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[e] = __hip_atomic_load(src + lane16 * 8 + e, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        const float4 lo = *reinterpret_cast<const float4 *>(src + lane16 * 8);
+        const float4 hi = *reinterpret_cast<const float4 *>(src + lane16 * 8 + 4);
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    }
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (!(e & h)) {
+                const float a = v[e], b = v[e + h];
+                v[e] = a + b;
+                v[e + h] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1) {
+        const bool upper = (lane16 & s) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float other = __shfl_xor(v[e], s, 16);
+            v[e] = upper ? (other - v[e]) : (v[e] + other);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, s, 16));
+
+    uint32_t packed[2] = {0u, 0u};
+    if (amax != 0.0f) {
+        const float inv = 127.0f / amax;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float r = rintf(v[e] * inv);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            packed[e >> 2] |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * (e & 3));
+        }
+    }
+    const float dq = amax != 0.0f ? amax * unit : 0.0f;
+    uint32_t *qw = reinterpret_cast<uint32_t *>(qdst + lane16 * 8);
+    if (kCoherentIO) {
+        __hip_atomic_store(qw, packed[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(qw + 1, packed[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane16 == 0)
+            __hip_atomic_store(dqdst, dq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        *reinterpret_cast<uint2 *>(qw) = make_uint2(packed[0], packed[1]);
+        if (lane16 == 0)
+            *dqdst = dq;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Activation staging. q[M][k] (global) -> LDS, chunks [c0, c0 + sc) into slots [0, sc).
+// Ternary: per row m, S slots of 64 activations laid out [code word j][slot] as 16-byte
+//   groups, each group the 4x4 byte transpose of 16 consecutive activations, to match
+//   decode_ternary's word order.
+// Sign: per row m, S slots of 128 activations laid out [dword d][half h][slot]; word j of
+//   (d, h) holds activations {32d + 4h + j + 8p : p = 0..3}, to match (w >> j) & 0x01010101.
+// Lanes of a row read consecutive slots, so ds_read_b128 sees no bank conflicts.
+// COHERENT: q was written by other workgroups of the same launch.
+// ------------------------------------------------------------------------------------
+template <bool COHERENT>
+__device__ __forceinline__ uint4 load16(const int8_t *p)
+{
+    if (COHERENT) {
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(p);
+        uint4 r;
+        r.x = __hip_atomic_load(w + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        r.y = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        r.z = __hip_atomic_load(w + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        r.w = __hip_atomic_load(w + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return r;
+    }
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+// One staging unit: 16 activations (ternary: one code word's worth) or 32 (sign: one
+// dword of sign bits). stage_unit_load reads it, stage_unit_store writes it transposed.
+template <int FMT>
+struct StageUnit {
+    uint4 lo, hi;
+};
+
+template <int FMT, bool COHERENT>
+__device__ __forceinline__ void stage_unit_load(StageUnit<FMT> &u, const int8_t *q, int k, int c0,
+                                                int sc, int unit)
+{
+    const int m = unit / (sc * 4), g = unit % (sc * 4);
+    const int c = g >> 2, j = g & 3;
+    if (FMT == TB_FMT_TERNARY2) {
+        u.lo = load16<COHERENT>(q + (size_t)m * k + (size_t)(c0 + c) * 64 + j * 16);
+    } else {
+        const int8_t *src = q + (size_t)m * k + (size_t)(c0 + c) * 128 + j * 32;
+        u.lo = load16<COHERENT>(src);
+        u.hi = load16<COHERENT>(src + 16);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void stage_unit_store(const StageUnit<FMT> &u, uint8_t *act, int S,
+                                                 int sc, int unit)
+{
+    const int m = unit / (sc * 4), g = unit % (sc * 4);
+    const int c = g >> 2, j = g & 3;
+    if (FMT == TB_FMT_TERNARY2) {
+        const uint4 r = u.lo;
+        uint4 o;
+        o.x = byte_at(r.x, 0) | byte_at(r.y, 0) << 8 | byte_at(r.z, 0) << 16 | byte_at(r.w, 0) << 24;
+        o.y = byte_at(r.x, 1) | byte_at(r.y, 1) << 8 | byte_at(r.z, 1) << 16 | byte_at(r.w, 1) << 24;
+        o.z = byte_at(r.x, 2) | byte_at(r.y, 2) << 8 | byte_at(r.z, 2) << 16 | byte_at(r.w, 2) << 24;
+        o.w = byte_at(r.x, 3) | byte_at(r.y, 3) << 8 | byte_at(r.z, 3) << 16 | byte_at(r.w, 3) << 24;
+        *reinterpret_cast<uint4 *>(act + (size_t)m * S * 64 + ((size_t)j * S + c) * 16) = o;
+    } else {
+        const uint32_t r[8] = {u.lo.x, u.lo.y, u.lo.z, u.lo.w, u.hi.x, u.hi.y, u.hi.z, u.hi.w};
+        // word i holds (q[i], q[8+i], q[16+i], q[24+i]); q[8p+i] is byte i&3 of r[2p+i/4]
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            o[i] = byte_at(r[0 + (i >> 2)], i & 3) | byte_at(r[2 + (i >> 2)], i & 3) << 8 |
+                   byte_at(r[4 + (i >> 2)], i & 3) << 16 | byte_at(r[6 + (i >> 2)], i & 3) << 24;
+        uint8_t *dst = act + (size_t)m * S * 128;
+        *reinterpret_cast<uint4 *>(dst + ((size_t)(j * 2 + 0) * S + c) * 16) =
+            make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(dst + ((size_t)(j * 2 + 1) * S + c) * 16) =
+            make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+template <int M, int FMT, bool COHERENT>
+__device__ __forceinline__ void stage_act(uint8_t *act, int S, const int8_t *q, int k, int c0,
+                                          int sc, int tid, int nthreads)
+{
+    const int units = M * sc * 4;
+    for (int u = tid; u < units; u += nthreads) {
+        StageUnit<FMT> su;
+        stage_unit_load<FMT, COHERENT>(su, q, k, c0, sc, u);
+        stage_unit_store<FMT>(su, act, S, sc, u);
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Step-major activation layout, used by the streaming kernels. Chunk c of row m sits in
+// step c / 16, lane slot c % 16. All 16 chunks of a step, for all M rows, are one
+// contiguous block of kStepBytes:
+//   ternary: [code word j][row m][slot] x 16 bytes   (kStepBytes = 1024 * M)
+//   sign:    [dword d][half h][row m][slot] x 16 bytes (kStepBytes = 2048 * M)
+// A lane's reads within one step are therefore at compile-time offsets from a single
+// base address (lane slot * 16 + step * kStepBytes), and the 16 lanes of a row read 256
+// consecutive bytes: no bank conflicts.
+// ------------------------------------------------------------------------------------
+template <int M, int FMT>
+struct StepLayout {
+    static constexpr int kPlanes = FMT == TB_FMT_TERNARY2 ? 4 : 8;   // 16-byte groups per chunk
+    static constexpr int kStepBytes = kPlanes * M * 256;
+    __device__ static constexpr int offset(int plane, int m) { return (plane * M + m) * 256; }
+};
+
+template <int M, int FMT, bool COHERENT>
+__device__ __forceinline__ void stage_unit_load_step(StageUnit<FMT> &u, const int8_t *q, int k,
+                                                     int unit)
+{
+    // unit = (m, chunk c, part j): 4 parts per chunk (16 activations ternary, 32 sign)
+    const int per_row = (FMT == TB_FMT_TERNARY2 ? k / 64 : k / 128) * 4;
+    const int m = unit / per_row, g = unit % per_row;
+    const int c = g >> 2, j = g & 3;
+    if (FMT == TB_FMT_TERNARY2) {
+        u.lo = load16<COHERENT>(q + (size_t)m * k + (size_t)c * 64 + j * 16);
+    } else {
+        const int8_t *src = q + (size_t)m * k + (size_t)c * 128 + j * 32;
+        u.lo = load16<COHERENT>(src);
+        u.hi = load16<COHERENT>(src + 16);
+    }
+}
+
+template <int M, int FMT>
+__device__ __forceinline__ void stage_unit_store_step(const StageUnit<FMT> &u, uint8_t *act, int k,
+                                                      int unit)
+{
+    using L = StepLayout<M, FMT>;
+    const int per_row = (FMT == TB_FMT_TERNARY2 ? k / 64 : k / 128) * 4;
+    const int m = unit / per_row, g = unit % per_row;
+    const int c = g >> 2, j = g & 3;
+    uint8_t *base = act + (size_t)(c >> 4) * L::kStepBytes + (c & 15) * 16;
+    if (FMT == TB_FMT_TERNARY2) {
+        const uint4 r = u.lo;
+        uint4 o;
+        o.x = byte_at(r.x, 0) | byte_at(r.y, 0) << 8 | byte_at(r.z, 0) << 16 | byte_at(r.w, 0) << 24;
+        o.y = byte_at(r.x, 1) | byte_at(r.y, 1) << 8 | byte_at(r.z, 1) << 16 | byte_at(r.w, 1) << 24;
+        o.z = byte_at(r.x, 2) | byte_at(r.y, 2) << 8 | byte_at(r.z, 2) << 16 | byte_at(r.w, 2) << 24;
+        o.w = byte_at(r.x, 3) | byte_at(r.y, 3) << 8 | byte_at(r.z, 3) << 16 | byte_at(r.w, 3) << 24;
+        *reinterpret_cast<uint4 *>(base + L::offset(j, m)) = o;
+    } else {
+        const uint32_t r[8] = {u.lo.x, u.lo.y, u.lo.z, u.lo.w, u.hi.x, u.hi.y, u.hi.z, u.hi.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            o[i] = byte_at(r[0 + (i >> 2)], i & 3) | byte_at(r[2 + (i >> 2)], i & 3) << 8 |
+                   byte_at(r[4 + (i >> 2)], i & 3) << 16 | byte_at(r[6 + (i >> 2)], i & 3) << 24;
+        *reinterpret_cast<uint4 *>(base + L::offset(j * 2 + 0, m)) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(base + L::offset(j * 2 + 1, m)) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+// Integer sums of one chunk against all M rows, step-major layout; `lds` is this lane's
+// slot address in the current step. Same arithmetic as chunk_sums.
+template <int M, int FMT, bool TWO>
+__device__ __forceinline__ void chunk_sums_step(const uint4 &w0, const uint4 &w1, const uint8_t *lds,
+                                                int (&is0)[M], int (&is1)[M])
+{
+    using L = StepLayout<M, FMT>;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        is0[m] = 0;
+        is1[m] = 0;
+    }
+    const uint32_t cw0[4] = {w0.x, w0.y, w0.z, w0.w};
+    const uint32_t cw1[4] = {w1.x, w1.y, w1.z, w1.w};
+    if (FMT == TB_FMT_TERNARY2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t d0, d1, d2, d3, e0 = 0, e1 = 0, e2 = 0, e3 = 0;
+            decode_ternary(cw0[j], d0, d1, d2, d3);
+            if (TWO)
+                decode_ternary(cw1[j], e0, e1, e2, e3);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint4 av = *reinterpret_cast<const uint4 *>(lds + L::offset(j, m));
+                is0[m] = dot4(d0, av.x, is0[m]);
+                is0[m] = dot4(d1, av.y, is0[m]);
+                is0[m] = dot4(d2, av.z, is0[m]);
+                is0[m] = dot4(d3, av.w, is0[m]);
+                if (TWO) {
+                    is1[m] = dot4(e0, av.x, is1[m]);
+                    is1[m] = dot4(e1, av.y, is1[m]);
+                    is1[m] = dot4(e2, av.z, is1[m]);
+                    is1[m] = dot4(e3, av.w, is1[m]);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            is0[m] = pair_add(is0[m]);
+            if (TWO)
+                is1[m] = pair_add(is1[m]);
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t b0[4], b1[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    b0[j] = (cw0[d] >> (4 * h + j)) & 0x01010101u;
+                    if (TWO)
+                        b1[j] = (cw1[d] >> (4 * h + j)) & 0x01010101u;
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const uint4 av = *reinterpret_cast<const uint4 *>(lds + L::offset(d * 2 + h, m));
+                    is0[m] = dot4(b0[0], av.x, is0[m]);
+                    is0[m] = dot4(b0[1], av.y, is0[m]);
+                    is0[m] = dot4(b0[2], av.z, is0[m]);
+                    is0[m] = dot4(b0[3], av.w, is0[m]);
+                    if (TWO) {
+                        is1[m] = dot4(b1[0], av.x, is1[m]);
+                        is1[m] = dot4(b1[1], av.y, is1[m]);
+                        is1[m] = dot4(b1[2], av.z, is1[m]);
+                        is1[m] = dot4(b1[3], av.w, is1[m]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// dq[M][nb] -> LDS; for the sign format also sum(q) per block -> LDS (int).
+template <int M, int FMT, bool COHERENT>
+__device__ __forceinline__ void stage_block_terms(float *dq_s, int *qsum_s, const float *dq,
+                                                  const int8_t *q, int nb, bool need_dq, int tid,
+                                                  int nthreads)
+{
+    if (need_dq)
+        for (int i = tid; i < M * nb; i += nthreads)
+            dq_s[i] = COHERENT ? __hip_atomic_load(dq + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : dq[i];
+    if (FMT == TB_FMT_SIGN1) {
+        for (int i = tid; i < M * nb; i += nthreads) {
+            const int8_t *src = q + (size_t)i * kBlock;   // [m][b] blocks are contiguous
+            int s = 0;
+            for (int j = 0; j < kBlock; j += 16) {
+                const uint4 g = load16<COHERENT>(src + j);
+                s = dot4(g.x, 0x01010101u, s);
+                s = dot4(g.y, 0x01010101u, s);
+                s = dot4(g.z, 0x01010101u, s);
+                s = dot4(g.w, 0x01010101u, s);
+            }
+            qsum_s[i] = s;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Integer sums of one 16-byte chunk against all M staged rows. TWO: a second matrix
+// (up) shares the activation reads. Ternary: each lane holds half a block, and the
+// partner's half is added with one DPP op, so both lanes hold the block sum. Sign: the
+// dot of the 0/1 bits; the caller applies isum = 2 * dot - sum(q).
+// slot: the chunk's LDS slot (any valid slot when the lane has no chunk; its codes are 0).
+// ------------------------------------------------------------------------------------
+template <int M, int FMT, bool TWO>
+__device__ __forceinline__ void chunk_sums(const uint4 &w0, const uint4 &w1, const uint8_t *act,
+                                           int S, int slot, int (&is0)[M], int (&is1)[M])
+{
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        is0[m] = 0;
+        is1[m] = 0;
+    }
+    const uint32_t cw0[4] = {w0.x, w0.y, w0.z, w0.w};
+    const uint32_t cw1[4] = {w1.x, w1.y, w1.z, w1.w};
+    if (FMT == TB_FMT_TERNARY2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t d0, d1, d2, d3, e0 = 0, e1 = 0, e2 = 0, e3 = 0;
+            decode_ternary(cw0[j], d0, d1, d2, d3);
+            if (TWO)
+                decode_ternary(cw1[j], e0, e1, e2, e3);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint4 av =
+                    *reinterpret_cast<const uint4 *>(act + (size_t)m * S * 64 + ((size_t)j * S + slot) * 16);
+                is0[m] = dot4(d0, av.x, is0[m]);
+                is0[m] = dot4(d1, av.y, is0[m]);
+                is0[m] = dot4(d2, av.z, is0[m]);
+                is0[m] = dot4(d3, av.w, is0[m]);
+                if (TWO) {
+                    is1[m] = dot4(e0, av.x, is1[m]);
+                    is1[m] = dot4(e1, av.y, is1[m]);
+                    is1[m] = dot4(e2, av.z, is1[m]);
+                    is1[m] = dot4(e3, av.w, is1[m]);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            is0[m] = pair_add(is0[m]);
+            if (TWO)
+                is1[m] = pair_add(is1[m]);
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t b0[4], b1[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    b0[j] = (cw0[d] >> (4 * h + j)) & 0x01010101u;
+                    if (TWO)
+                        b1[j] = (cw1[d] >> (4 * h + j)) & 0x01010101u;
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const uint4 av = *reinterpret_cast<const uint4 *>(
+                        act + (size_t)m * S * 128 + ((size_t)(d * 2 + h) * S + slot) * 16);
+                    is0[m] = dot4(b0[0], av.x, is0[m]);
+                    is0[m] = dot4(b0[1], av.y, is0[m]);
+                    is0[m] = dot4(b0[2], av.z, is0[m]);
+                    is0[m] = dot4(b0[3], av.w, is0[m]);
+                    if (TWO) {
+                        is1[m] = dot4(b1[0], av.x, is1[m]);
+                        is1[m] = dot4(b1[1], av.y, is1[m]);
+                        is1[m] = dot4(b1[2], av.z, is1[m]);
+                        is1[m] = dot4(b1[3], av.w, is1[m]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Block fold of one chunk: acc += (scale * dq) * float(isum), once per block.
+// Ternary: both lanes of a block hold the same sums and fold the same term; the tree
+// reads only the even lane. Sign: isum = 2 * dot - sum(q) first.
+template <int M, int FMT, bool TWO>
+__device__ __forceinline__ void fold_chunk(int (&is0)[M], int (&is1)[M], float s0, float s1,
+                                           const float *dq_s, const int *qsum_s, int nb, int b,
+                                           float (&acc0)[M], float (&acc1)[M])
+{
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (FMT == TB_FMT_SIGN1) {
+            const int qs = qsum_s[m * nb + b];
+            is0[m] = 2 * is0[m] - qs;
+            if (TWO)
+                is1[m] = 2 * is1[m] - qs;
+        }
+        const float d = dq_s[m * nb + b];
+        acc0[m] += (s0 * d) * (float)is0[m];
+        if (TWO)
+            acc1[m] += (s1 * d) * (float)is1[m];
+    }
+}
+
+// Fixed shuffle tree over the 16 lanes of a row; lane 0 of the row ends with the total:
+// ((a0 + a2) + (a4 + a6)) + ((a8 + a10) + (a12 + a14)) for ternary (odd lanes hold
+// copies), or the same over all 16 lanes for sign.
+template <int M, int FMT, bool TWO>
+__device__ __forceinline__ void row_tree(float (&acc0)[M], float (&acc1)[M])
+{
+#pragma unroll
+    for (int off = FMT == TB_FMT_TERNARY2 ? 2 : 1; off < kChunkLanes; off <<= 1) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            acc0[m] += __shfl_down(acc0[m], off, kChunkLanes);
+            if (TWO)
+                acc1[m] += __shfl_down(acc1[m], off, kChunkLanes);
+        }
+    }
+}
+
+}  // namespace tbk

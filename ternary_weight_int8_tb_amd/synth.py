@@ -25,7 +25,8 @@ block plus the same scales.
   per byte and places the base-3 digits of ``d`` in the four fields. This is
   exact, and about 4x faster than drawing codes one by one.
 * Sign bits are i.i.d. Bernoulli(1/2), so every code byte is uniform over
-  all 256 values. Bit ``i`` sits in byte ``i >> 3``, bit ``i & 7``.
+  all 256 values. Bit ``i`` sits in byte ``i >> 3``, bit ``i & 7``. The bytes
+  are drawn as full-range uint32 words and read as little-endian bytes.
 * Scales are ``lognormal(mu=-4, sigma=0.5)`` rounded to IEEE binary16 (round
   to nearest even) and stored as raw uint16 bit patterns.
 
@@ -160,7 +161,9 @@ def sign_matrix(n: int, k: int, seed: int, layer: int, tensor: int) -> PackedMat
         raise ValueError("k must be a multiple of 128")
     nb = k // BLOCK
     rng = rng_for(seed, layer, tensor)
-    codes = np.frombuffer(rng.bytes(n * k // 8), np.uint8).reshape(n, nb, 16).copy()
+    # uniform bytes from full-range 32-bit draws, read as little-endian bytes
+    words = rng.integers(0, 2 ** 32, n * k // 32, dtype=np.uint32)
+    codes = words.astype("<u4").view(np.uint8).reshape(n, nb, 16)
     scales = _scales(rng, n, nb)
     return PackedMatrix(codes, scales, n, k, FMT_SIGN1)
 

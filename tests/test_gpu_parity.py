@@ -125,7 +125,7 @@ def test_code3_and_zero_cases(o):
 
 # ----------------------------------------------------------------- a5: gate/up + SiLU
 @pytest.mark.parametrize("fmt", [TERN, SIGN])
-@pytest.mark.parametrize("n,k,m", [(384, 256, 1), (2176, 640, 3), (1040, 5120, 8)])
+@pytest.mark.parametrize("n,k,m", [(384, 256, 1), (2176, 640, 3), (1152, 5120, 8)])
 def test_gateup_silu(o, fmt, n, k, m):
     say(f"gateup fmt={fmt} n={n} k={k} m={m}")
     layer = synth.ffn_layer(11, 0, fmt, hidden=k, inter=n)
