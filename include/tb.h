@@ -41,6 +41,7 @@
 #ifndef TB_H
 #define TB_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -134,6 +135,44 @@ int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float
  * decode and dot-product code, before the scale fold.
  *   isum int32 [m][w->n][w->k/128] output */
 int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream);
+
+/* ---- Fused FFN layers ----------------------------------------------------
+ * One launch runs num_layers whole FFN layers of the same shape: for each
+ * layer, exactly tb_rotate_quant_i8(x) -> tb_ffn_gateup_silu ->
+ * tb_ffn_down (the stages of PR #1154's decode step, Summary and commit
+ * message). Outputs are bit-identical to those three calls. One workgroup per
+ * compute unit stays resident for all layers and streams the weights without
+ * pausing at kernel boundaries; layers run strictly one after another (layer
+ * l+1 starts after every output of layer l is written).
+ *   layers   host array of num_layers weight sets: gate, up [inter x hidden],
+ *            down [hidden x inter], one fmt; inter a multiple of 128.
+ *   x        float [num_layers][m][hidden] (one input per layer), or with
+ *            TB_FFN_CHAIN float [m][hidden]: layer l+1 then takes layer l's y.
+ *   y        float [num_layers][m][hidden] outputs.
+ *   ws       device workspace of at least tb_ffn_workspace_bytes(m, hidden,
+ *            inter) bytes, 16-byte aligned, initialised once with
+ *            tb_ffn_workspace_init before its first use. It holds h, rotquant(h)
+ *            and the synchronisation words; every call leaves it ready for the
+ *            next. Calls that share a workspace must not overlap in time.
+ * Synchronisation between workgroups waits a bounded time (the spin limit of
+ * tb_ffn_workspace_init; 0 selects 100 ms). If a wait runs out, for instance
+ * because other work occupies compute units so that not all workgroups can
+ * be resident, the call abandons its work (outputs undefined) and sets a
+ * sticky error in the workspace, read with tb_ffn_workspace_error; later
+ * calls on that workspace do nothing until it is initialised again. */
+typedef struct tb_ffn_weights {
+    tb_matrix gate, up, down;
+} tb_ffn_weights;
+
+#define TB_FFN_CHAIN 1u
+
+size_t tb_ffn_workspace_bytes(int m, int hidden, int inter);  /* 0 for bad arguments */
+int tb_ffn_workspace_init(void *ws, size_t ws_bytes, uint32_t spin_ticks, void *stream);
+int tb_ffn_layers(const tb_ffn_weights *layers, int num_layers, const float *x, int m,
+                  unsigned flags, void *ws, size_t ws_bytes, float *y, void *stream);
+/* Blocking: synchronises with the device and returns the sticky error word
+ * (0 = none) in *error. */
+int tb_ffn_workspace_error(const void *ws, int *error);
 
 /* Static description of a status code; never NULL. */
 const char *tb_status_str(int status);

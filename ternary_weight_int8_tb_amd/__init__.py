@@ -24,7 +24,9 @@ MAX_ROWS = 8
 
 # every symbol include/tb.h declares
 ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_ffn_gateup_silu", "tb_ffn_down",
-               "tb_gemv_block_sums", "tb_status_str", "tb_abi_version")
+               "tb_gemv_block_sums", "tb_ffn_workspace_bytes", "tb_ffn_workspace_init",
+               "tb_ffn_layers", "tb_ffn_workspace_error", "tb_status_str", "tb_abi_version")
+TB_FFN_CHAIN = 1
 
 
 class TbError(RuntimeError):
@@ -38,6 +40,10 @@ class CMatrix(ctypes.Structure):
                 ("k", ctypes.c_int32), ("fmt", ctypes.c_int32)]
 
 
+class CFfnWeights(ctypes.Structure):
+    _fields_ = [("gate", CMatrix), ("up", CMatrix), ("down", CMatrix)]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _MP = ctypes.POINTER(CMatrix)
@@ -47,6 +53,11 @@ _SIGS = {
     "tb_ffn_gateup_silu": ([_MP, _MP, _P, _P, _I, _P, _P], _I),
     "tb_ffn_down": ([_MP, _P, _I, _P, _P, _P, _P], _I),
     "tb_gemv_block_sums": ([_MP, _P, _I, _P, _P], _I),
+    "tb_ffn_workspace_bytes": ([_I, _I, _I], ctypes.c_size_t),
+    "tb_ffn_workspace_init": ([_P, ctypes.c_size_t, ctypes.c_uint32, _P], _I),
+    "tb_ffn_layers": ([ctypes.POINTER(CFfnWeights), _I, _P, _I, ctypes.c_uint, _P, ctypes.c_size_t,
+                       _P, _P], _I),
+    "tb_ffn_workspace_error": ([_P, ctypes.POINTER(_I)], _I),
     "tb_status_str": ([_I], ctypes.c_char_p),
     "tb_abi_version": ([], _I),
 }
@@ -151,3 +162,47 @@ def tb_gemv_block_sums(w: Matrix, q, isum, stream=None) -> None:
     """isum int32 [m][w.n][w.k/128]: the integer block sums before the scale fold."""
     _call("tb_gemv_block_sums", ctypes.byref(w.c), q.data_ptr(), _rows(q), isum.data_ptr(),
           _stream(stream))
+
+
+def tb_ffn_workspace_bytes(m: int, hidden: int, inter: int) -> int:
+    """Bytes of device workspace tb_ffn_layers needs for m rows (0 for bad arguments)."""
+    return int(lib().tb_ffn_workspace_bytes(int(m), int(hidden), int(inter)))
+
+
+def tb_ffn_workspace_init(ws, spin_ticks: int = 0, stream=None) -> None:
+    """Initialise a workspace (uint8 device tensor); spin_ticks 0 = the default limit."""
+    _call("tb_ffn_workspace_init", ws.data_ptr(), ws.numel() * ws.element_size(),
+          int(spin_ticks), _stream(stream))
+
+
+def tb_ffn_workspace_error(ws) -> int:
+    """The sticky error word of a workspace (synchronises with the device)."""
+    err = _I(0)
+    _call("tb_ffn_workspace_error", ws.data_ptr(), ctypes.byref(err))
+    return int(err.value)
+
+
+class FfnLayers:
+    """A host array of tb_ffn_weights for tb_ffn_layers, built once from (gate, up, down)."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        self.arr = (CFfnWeights * len(self.layers))()
+        for i, (g, u, d) in enumerate(self.layers):
+            self.arr[i].gate, self.arr[i].up, self.arr[i].down = g.c, u.c, d.c
+
+    def __len__(self) -> int:
+        return len(self.layers)
+
+
+def tb_ffn_layers(layers: FfnLayers, x, ws, y, chain: bool = False, stream=None) -> None:
+    """Run len(layers) whole FFN layers (one launch per 32 layers).
+
+    x float32 [L][m][hidden] (or [m][hidden] with chain=True: layer l+1 takes layer l's y),
+    y float32 [L][m][hidden], ws an initialised uint8 workspace tensor."""
+    if y.dim() != 3:
+        raise ValueError("y must be [layers][m][hidden]")
+    m = int(y.shape[1])
+    _call("tb_ffn_layers", layers.arr, len(layers), x.data_ptr(), m,
+          TB_FFN_CHAIN if chain else 0, ws.data_ptr(), ws.numel() * ws.element_size(),
+          y.data_ptr(), _stream(stream))

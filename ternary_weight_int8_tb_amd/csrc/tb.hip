@@ -28,11 +28,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 
 #include "tb.h"
 #include "tb_device.h"
+#include "tb_fused.h"
 
 namespace {
 
@@ -42,7 +44,7 @@ constexpr int kRotThreads = 256;
 constexpr int kSlicedThreads = 256;
 constexpr int kRingWaves = 8;
 constexpr int kRingThreads = 64 * kRingWaves;
-constexpr int kRingDepth = 8;
+constexpr int kRingDepth = 4;
 
 enum Mode { kModeY = 0, kModeGateUp = 1, kModeIsum = 2 };
 
@@ -569,6 +571,81 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
+
+// ------------------------------------------------------------------------------------
+// Fused FFN layers
+// ------------------------------------------------------------------------------------
+using FusedFn = void (*)(FusedArgs);
+
+template <int FMT>
+FusedFn fused_pick_m(int m)
+{
+    switch (m) {
+    case 1: return ffn_layers_kernel<1, FMT>;
+    case 2: return ffn_layers_kernel<2, FMT>;
+    case 3: return ffn_layers_kernel<3, FMT>;
+    case 4: return ffn_layers_kernel<4, FMT>;
+    case 5: return ffn_layers_kernel<5, FMT>;
+    case 6: return ffn_layers_kernel<6, FMT>;
+    case 7: return ffn_layers_kernel<7, FMT>;
+    case 8: return ffn_layers_kernel<8, FMT>;
+    default: return nullptr;
+    }
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct WsLayout {
+    size_t sync, h, qh, dqh, qsumh, total;
+};
+
+WsLayout ws_layout(int m, int inter)
+{
+    WsLayout w;
+    const size_t nbi = (size_t)inter / kBlock;
+    w.sync = 0;
+    w.h = align256((size_t)kSyncWords * 4);
+    w.qh = align256(w.h + (size_t)m * inter * 4);
+    w.dqh = align256(w.qh + (size_t)m * inter);
+    w.qsumh = align256(w.dqh + (size_t)m * nbi * 4);
+    w.total = align256(w.qsumh + (size_t)m * nbi * 4);
+    return w;
+}
+
+// LDS bytes of the fused kernel (must match ffn_layers_kernel's carve-up).
+size_t fused_lds_bytes(int fmt, int m, int hidden, int inter)
+{
+    const int wpc = fmt == TB_FMT_TERNARY2 ? 64 : 128;
+    const int step = (fmt == TB_FMT_TERNARY2 ? 1024 : 2048) * m;
+    const int I0 = (hidden / wpc + kChunkLanes - 1) / kChunkLanes;
+    const int I1 = (inter / wpc + kChunkLanes - 1) / kChunkLanes;
+    const size_t act = std::max((size_t)I1 * step, (size_t)I0 * step + (size_t)m * hidden);
+    const int bps = kChunkLanes / (fmt == TB_FMT_TERNARY2 ? 2 : 1);
+    const size_t nbmax = (size_t)std::max(hidden, inter) / kBlock + bps;
+    return act + 2 * nbmax * m * 4 + 16;
+}
+
+int check_ffn_shapes(const tb_ffn_weights *L, int n, int *hidden, int *inter, int *fmt)
+{
+    for (int i = 0; i < n; ++i) {
+        int rc;
+        if ((rc = check_matrix(&L[i].gate)) || (rc = check_matrix(&L[i].up)) ||
+            (rc = check_matrix(&L[i].down)))
+            return rc;
+        const int H = L[i].gate.k, N = L[i].gate.n, F = L[i].gate.fmt;
+        if (L[i].up.k != H || L[i].up.n != N || L[i].down.k != N || L[i].down.n != H ||
+            L[i].up.fmt != F || L[i].down.fmt != F || N % kBlock)
+            return TB_EINVAL;
+        if (i == 0) {
+            *hidden = H;
+            *inter = N;
+            *fmt = F;
+        } else if (H != *hidden || N != *inter || F != *fmt) {
+            return TB_EINVAL;
+        }
+    }
+    return TB_OK;
+}
 }  // namespace
 
 // ====================================================================================
@@ -694,6 +771,118 @@ int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum
         return TB_EINVAL;
     return launch_gemv(kModeIsum, w, nullptr, q, nullptr, m, nullptr, isum,
                        static_cast<hipStream_t>(stream));
+}
+
+
+size_t tb_ffn_workspace_bytes(int m, int hidden, int inter)
+{
+    (void)hidden;
+    if (check_rows(m) || inter < kBlock || inter % kBlock)
+        return 0;
+    return ws_layout(m, inter).total;
+}
+
+int tb_ffn_workspace_init(void *ws, size_t ws_bytes, uint32_t spin_ticks, void *stream)
+{
+    if (!ws || ws_bytes < (size_t)kSyncWords * 4)
+        return TB_EINVAL;
+    if (!aligned16(ws))
+        return TB_EALIGN;
+    hipLaunchKernelGGL(ffn_workspace_init_kernel, dim3(1), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<uint32_t *>(ws), spin_ticks);
+    return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+}
+
+int tb_ffn_workspace_error(const void *ws, int *error)
+{
+    if (!ws || !error)
+        return TB_EINVAL;
+    uint32_t v = 0;
+    if (hipMemcpy(&v, static_cast<const uint32_t *>(ws) + kSyncError, 4, hipMemcpyDeviceToHost) !=
+        hipSuccess)
+        return TB_EHIP;
+    *error = (int)v;
+    return TB_OK;
+}
+
+int tb_ffn_layers(const tb_ffn_weights *layers, int num_layers, const float *x, int m,
+                  unsigned flags, void *ws, size_t ws_bytes, float *y, void *stream)
+{
+    if (!layers || num_layers < 1 || !x || !y || !ws || check_rows(m) || (flags & ~TB_FFN_CHAIN))
+        return TB_EINVAL;
+    int H = 0, N = 0, F = 0;
+    int rc = check_ffn_shapes(layers, num_layers, &H, &N, &F);
+    if (rc)
+        return rc;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(ws))
+        return TB_EALIGN;
+    const WsLayout wl = ws_layout(m, N);
+    if (ws_bytes < wl.total)
+        return TB_EINVAL;
+    const bool chain = (flags & TB_FFN_CHAIN) != 0;
+    const Range rx = range_of(x, (size_t)(chain ? 1 : num_layers) * m * H * 4),
+                ry = range_of(y, (size_t)num_layers * m * H * 4), rw = range_of(ws, wl.total);
+    if (overlaps(rx, ry) || overlaps(rx, rw) || overlaps(ry, rw))
+        return TB_EINVAL;
+    for (int i = 0; i < num_layers; ++i) {
+        const tb_matrix *mats[3] = {&layers[i].gate, &layers[i].up, &layers[i].down};
+        for (const tb_matrix *w : mats)
+            if (overlaps(ry, range_of(w->codes, codes_bytes(w))) ||
+                overlaps(ry, range_of(w->scales, scales_bytes(w))) ||
+                overlaps(rw, range_of(w->codes, codes_bytes(w))) ||
+                overlaps(rw, range_of(w->scales, scales_bytes(w))))
+                return TB_EINVAL;
+    }
+    DeviceInfo info;
+    if ((rc = device_info(&info)))
+        return rc;
+    const size_t lds = fused_lds_bytes(F, m, H, N);
+    if (lds > (size_t)info.lds_limit)
+        return TB_EUNSUPPORTED;
+    FusedFn fn = F == TB_FMT_TERNARY2 ? fused_pick_m<TB_FMT_TERNARY2>(m) : fused_pick_m<TB_FMT_SIGN1>(m);
+    if (!fn)
+        return TB_EINVAL;
+    if (lds > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return TB_EHIP;
+
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    FusedArgs a;
+    a.hidden = H;
+    a.inter = N;
+    a.sync = reinterpret_cast<uint32_t *>(wsb + wl.sync);
+    a.h = reinterpret_cast<float *>(wsb + wl.h);
+    a.qh = reinterpret_cast<int8_t *>(wsb + wl.qh);
+    a.dqh = reinterpret_cast<float *>(wsb + wl.dqh);
+    a.qsumh = reinterpret_cast<int *>(wsb + wl.qsumh);
+    a.gu_codes_bytes = (uint32_t)codes_bytes(&layers[0].gate);
+    a.gu_scales_bytes = (uint32_t)((scales_bytes(&layers[0].gate) + 3) & ~(size_t)3);
+    a.d_codes_bytes = (uint32_t)codes_bytes(&layers[0].down);
+    a.d_scales_bytes = (uint32_t)((scales_bytes(&layers[0].down) + 3) & ~(size_t)3);
+    a.unit = dq_unit();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // at most kMaxFusedLayers per launch; a chained sequence continues from the last y
+    for (int start = 0; start < num_layers; start += kMaxFusedLayers) {
+        const int cnt = std::min(kMaxFusedLayers, num_layers - start);
+        a.L = cnt;
+        for (int i = 0; i < kMaxFusedLayers; ++i) {
+            const tb_ffn_weights &w = layers[start + (i < cnt ? i : 0)];
+            a.layer[i].codes[0] = static_cast<const uint8_t *>(w.gate.codes);
+            a.layer[i].codes[1] = static_cast<const uint8_t *>(w.up.codes);
+            a.layer[i].codes[2] = static_cast<const uint8_t *>(w.down.codes);
+            a.layer[i].scales[0] = w.gate.scales;
+            a.layer[i].scales[1] = w.up.scales;
+            a.layer[i].scales[2] = w.down.scales;
+        }
+        a.chain = chain ? 1 : 0;
+        a.x = chain ? (start == 0 ? x : y + (size_t)(start - 1) * m * H) : x + (size_t)start * m * H;
+        a.y = y + (size_t)start * m * H;
+        hipLaunchKernelGGL(fn, dim3(info.cus), dim3(kFusedThreads), lds, s, a);
+        if (hipGetLastError() != hipSuccess)
+            return TB_EHIP;
+    }
+    return TB_OK;
 }
 
 }  // extern "C"

@@ -130,23 +130,13 @@ __device__ __forceinline__ void decode_ternary(uint32_t w, uint32_t &d0, uint32_
 // even) and dq = amax * unit; else q = 0 and dq = 0. Writes 8 q bytes per lane, and dq
 // from lane 0 of the group.
 // ------------------------------------------------------------------------------------
-template <bool kCoherentIO>
-__device__ __forceinline__ void rotquant16(const float *src, int8_t *qdst, float *dqdst,
-                                           int lane16, float unit)
+// Register core of the rotate-quantise step, for a 16-lane group holding one block:
+// v[8] = elements 8L .. 8L+7 of the block in lane L. Returns the lane's 8 codes packed
+// little-endian in packed[2], the block's dq, and the block's sum of codes (group total,
+// for the sign format's isum = 2 * dot - sum(q)).
+__device__ __forceinline__ void rotquant_regs(float (&v)[8], int lane16, float unit,
+                                              uint32_t (&packed)[2], float &dq, int &qsum)
 {
-    float v[8];
-    if (kCoherentIO) {
-        // data written by other workgroups of the same launch: read it device-coherently
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[e] = __hip_atomic_load(src + lane16 * 8 + e, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-        const float4 lo = *reinterpret_cast<const float4 *>(src + lane16 * 8);
-        const float4 hi = *reinterpret_cast<const float4 *>(src + lane16 * 8 + 4);
-        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-    }
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -175,17 +165,50 @@ __device__ __forceinline__ void rotquant16(const float *src, int8_t *qdst, float
     for (int s = 1; s < 16; s <<= 1)
         amax = fmaxf(amax, __shfl_xor(amax, s, 16));
 
-    uint32_t packed[2] = {0u, 0u};
+    packed[0] = 0u;
+    packed[1] = 0u;
+    int sum = 0;
     if (amax != 0.0f) {
         const float inv = 127.0f / amax;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float r = rintf(v[e] * inv);
             r = fminf(fmaxf(r, -127.0f), 127.0f);
-            packed[e >> 2] |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * (e & 3));
+            const int qi = (int)r;
+            sum += qi;
+            packed[e >> 2] |= (uint32_t)(uint8_t)(int8_t)qi << (8 * (e & 3));
         }
     }
-    const float dq = amax != 0.0f ? amax * unit : 0.0f;
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1)
+        sum += __shfl_xor(sum, s, 16);
+    dq = amax != 0.0f ? amax * unit : 0.0f;
+    qsum = sum;
+}
+
+// Rotate + quantise one 128-block with a 16-lane group (see rotquant_regs), from global
+// memory to global memory.
+template <bool kCoherentIO>
+__device__ __forceinline__ void rotquant16(const float *src, int8_t *qdst, float *dqdst,
+                                           int lane16, float unit)
+{
+    float v[8];
+    if (kCoherentIO) {
+        // data written by other workgroups of the same launch: read it device-coherently
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[e] = __hip_atomic_load(src + lane16 * 8 + e, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        const float4 lo = *reinterpret_cast<const float4 *>(src + lane16 * 8);
+        const float4 hi = *reinterpret_cast<const float4 *>(src + lane16 * 8 + 4);
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    }
+    uint32_t packed[2];
+    float dq;
+    int qsum;
+    rotquant_regs(v, lane16, unit, packed, dq, qsum);
     uint32_t *qw = reinterpret_cast<uint32_t *>(qdst + lane16 * 8);
     if (kCoherentIO) {
         __hip_atomic_store(qw, packed[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -119,3 +119,58 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(tb, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="missing"):
         tb.lib()
+
+
+def test_ffn_workspace_bytes(L):
+    # sync words, then h [m][inter] f32, q_h [m][inter] i8, dq_h and sum q_h [m][inter/128]
+    for m, inter in ((1, 384), (8, 17408), (3, 2176)):
+        nb = tb.tb_ffn_workspace_bytes(m, 5120, inter)
+        assert nb >= 4096 + m * inter * 5 + 2 * m * (inter // 128) * 4
+        assert nb % 256 == 0
+    assert tb.tb_ffn_workspace_bytes(0, 5120, 17408) == 0
+    assert tb.tb_ffn_workspace_bytes(9, 5120, 17408) == 0
+    assert tb.tb_ffn_workspace_bytes(1, 5120, 100) == 0
+
+
+def test_ffn_workspace_init_validation(L):
+    assert L.tb_ffn_workspace_init(None, 1 << 20, 0, None) == tb.TB_EINVAL
+    assert L.tb_ffn_workspace_init(ALIGNED, 64, 0, None) == tb.TB_EINVAL       # below the sync words
+    assert L.tb_ffn_workspace_init(ALIGNED + 4, 1 << 20, 0, None) == tb.TB_EALIGN
+    err = ctypes.c_int(7)
+    assert L.tb_ffn_workspace_error(None, ctypes.byref(err)) == tb.TB_EINVAL
+    assert L.tb_ffn_workspace_error(ALIGNED, None) == tb.TB_EINVAL
+
+
+def test_ffn_layers_validation(L):
+    H, N = 512, 384
+    base = 0x10000000
+
+    def weights(i, n_gate=N, fmt=0, k_down=N):
+        o = base + i * 0x100000
+        return tb.CFfnWeights(mat(o, o + 0x20000, N if n_gate is None else n_gate, H, fmt),
+                              mat(o + 0x40000, o + 0x60000, N, H, fmt),
+                              mat(o + 0x80000, o + 0xA0000, H, k_down, fmt))
+    arr = (tb.CFfnWeights * 2)(weights(0), weights(1))
+    ws_bytes = tb.tb_ffn_workspace_bytes(1, H, N)
+    X, Y, WS = 0x40000000, 0x48000000, 0x50000000
+
+    def call(a=arr, n=2, x=X, m=1, flags=0, ws=WS, wsb=ws_bytes, y=Y):
+        return L.tb_ffn_layers(a, n, x, m, flags, ws, wsb, y, None)
+    assert call(n=0) == tb.TB_EINVAL
+    assert call(a=None) == tb.TB_EINVAL
+    assert call(m=9) == tb.TB_EINVAL
+    assert call(flags=2) == tb.TB_EINVAL
+    assert call(x=0) == tb.TB_EINVAL
+    assert call(ws=0) == tb.TB_EINVAL
+    assert call(wsb=ws_bytes - 256) == tb.TB_EINVAL                  # workspace too small
+    assert call(x=X + 8) == tb.TB_EALIGN
+    assert call(ws=WS + 4) == tb.TB_EALIGN
+    assert call(y=X + 16) == tb.TB_EINVAL                             # y overlaps x
+    assert call(ws=Y + 256) == tb.TB_EINVAL                           # workspace overlaps y
+    assert call(y=base + 0x40) == tb.TB_EINVAL                        # y overlaps weights
+    bad = (tb.CFfnWeights * 2)(weights(0), weights(1, n_gate=256))  # gate/up rows differ
+    assert call(a=bad) == tb.TB_EINVAL
+    bad = (tb.CFfnWeights * 2)(weights(0), weights(1, fmt=1))       # formats differ
+    assert call(a=bad) == tb.TB_EINVAL
+    bad = (tb.CFfnWeights * 2)(weights(0), weights(1, k_down=256))  # down does not match
+    assert call(a=bad) == tb.TB_EINVAL
