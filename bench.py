@@ -4,16 +4,21 @@
 Workload: a 64-layer FFN weight stream with the 27B model's FFN shapes
 (hidden 5120, intermediate 17408). The layers are independently seeded
 synthetic ternary blocks: 2-bit codes with one fp16 scale per 128 weights,
-4,545,576,960 bytes in all, about 17x the 256 MiB last-level cache. A step is
-one pass over the 64 layers, in order, on one stream. Each layer runs
-tb_rotate_quant_i8(x), tb_ffn_gateup_silu and tb_ffn_down. The layers are
-not overlapped and no work is hoisted out of a step.
+4,545,576,960 bytes in all, about 17x the 256 MiB last-level cache. Each layer
+takes its own N(0,1) activation rows. A step is one pass over the 64 layers,
+in order: per layer rotate + quantise x, gate/up + SiLU gate, rotate +
+quantise h, down. Nothing is hoisted out of a step.
 
-Printed (stdout, one JSON line): weight GB/s at M=1 (the value), us/layer,
-% of the 8 TB/s HBM peak; the same at M=8; the 1-bit sign stream; the
-roofline of the dominant kernel (gate/up GEMV), timed with HIP events on
-its own stream; and the scalar CPU oracle timed on a bounded sample on
-this host.
+Two complete paths are timed at M=1, both with strict layer order (layer l+1
+starts after every output of layer l is written; no layer is overlapped with
+another and no work is hoisted out of a step): the fused entry point
+tb_ffn_layers (one persistent launch per 32 layers), and the three separate
+calls per layer (tb_rotate_quant_i8, tb_ffn_gateup_silu, tb_ffn_down) replayed
+from a HIP graph (and eagerly). The value is the faster of the two; the JSON
+names it. Also printed: the same at M=8; the 1-bit sign stream; the roofline
+of the headline path's dominant kernel, timed with HIP events on the stream it
+runs on; a 4 GiB streaming-read probe; and the scalar CPU oracle timed on a
+bounded sample on this host.
 """
 
 from __future__ import annotations
@@ -23,6 +28,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -79,7 +86,34 @@ class Stream64:
             tb.tb_ffn_down(wd, self.h, self.qh, self.dqh, self.y[l])
 
 
-def time_stream(torch, s: Stream64, steps: int, warmup: int, use_graph: bool):
+class Fused64:
+    """The same stream through tb_ffn_layers: one call per step (one launch per 32 layers)."""
+
+    def __init__(self, tb, layers_dev, xs, m, torch):
+        self.tb, self.m = tb, m
+        dev = "cuda"
+        k = layers_dev[0][0].k
+        n = layers_dev[0][0].n
+        self.arr = tb.FfnLayers(layers_dev)
+        self.x = torch.from_numpy(np.stack([x[:m] for x in xs])).to(dev)
+        self.y = torch.empty(len(layers_dev), m, k, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(tb.tb_ffn_workspace_bytes(m, k, n), dtype=torch.uint8, device=dev)
+        tb.tb_ffn_workspace_init(self.ws)
+
+    def step(self):
+        self.tb.tb_ffn_layers(self.arr, self.x, self.ws, self.y)
+
+    def check(self):
+        err = self.tb.tb_ffn_workspace_error(self.ws)
+        if err:
+            raise RuntimeError(f"tb_ffn_layers reported error {err}: not all workgroups resident")
+
+
+def time_stream(torch, s, steps: int, warmup: int, use_graph: bool):
+    """Time `steps` passes after `warmup` untimed ones.
+
+    Returns (mean seconds per step over the whole timed region, bracketed by device
+    synchronisation; per-step seconds from HIP events recorded between the steps)."""
     graph = None
     if use_graph:
         s.step()
@@ -91,23 +125,52 @@ def time_stream(torch, s: Stream64, steps: int, warmup: int, use_graph: bool):
     run = graph.replay if graph else s.step
     for _ in range(warmup):
         run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         run()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps, graph
+    total = (time.perf_counter() - t0) / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(steps)]
+    return total, per
+
+
+def read_probe(torch, nbytes: int, reps: int = 5):
+    """Achievable HBM read bandwidth: a 16-byte non-temporal streaming read of nbytes."""
+    import ctypes
+    from ternary_weight_int8_tb_amd import build as tb_build
+    path = os.path.join(ROOT, "ternary_weight_int8_tb_amd", "libtb_probe.so")
+    if not os.path.exists(path):
+        tb_build.build()
+    P = ctypes.CDLL(path)
+    P.tbp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for grid in (256, 512, 1024):
+        P.tbp_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, st)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            P.tbp_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, st)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return best
 
 
 def gateup_event_timing(torch, s: Stream64, reps: int):
-    """Mean gate/up kernel duration (s): HIP events around back-to-back gate/up launches.
-
-    One pass launches tb_ffn_gateup_silu once per layer, over every layer's weights
-    in turn (so each launch streams its 47 MB from HBM), on the current stream, with
-    one event before and one after the whole pass. Kernels on one stream run back to
-    back, so the mean is the kernel's own duration, comparable with the per-dispatch
-    durations of a kernel trace.
-    """
+    """Mean gate/up kernel duration (s): HIP events around back-to-back gate/up launches
+    over every layer's weights (each launch streams its 47 MB from HBM), on the current
+    stream, which is the stream the library launches on."""
     tb = s.tb
     tb.tb_rotate_quant_i8(s.x[0], s.q, s.dq)
     torch.cuda.synchronize()
@@ -122,6 +185,49 @@ def gateup_event_timing(torch, s: Stream64, reps: int):
         torch.cuda.synchronize()
         total += e0.elapsed_time(e1) * 1e-3
     return total / (reps * n)
+
+
+def fused_event_timing(torch, f: Fused64, reps: int):
+    """Mean duration (s) of one fused launch (32 layers), from HIP events on its stream.
+
+    tb_ffn_layers launches on the current stream (the default argument), which is the
+    stream torch.cuda.Event records on. Each repetition is one step (two back-to-back
+    launches of 32 layers) between two events; kernels on one stream run back to
+    back, so the mean per launch compares with the per-dispatch durations of a kernel
+    trace.
+    """
+    f.step()
+    torch.cuda.synchronize()
+    launches = (len(f.arr) + 31) // 32
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total = 0.0
+    for _ in range(reps):
+        e0.record()
+        f.step()
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1) * 1e-3
+    return total / (reps * launches)
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch of `kernel_key` from the committed counter summary, or None.
+
+    profiles/ffn64_stream_traffic.json holds calibrated FETCH_SIZE + WRITE_SIZE bytes per
+    launch with a sha256 of the kernel sources they were taken on; once the sources
+    change, the figure no longer describes the kernel and None is returned."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "ffn64_stream_traffic.json")
+    if not os.path.exists(path):
+        return None
+    doc = json.load(open(path))
+    h = hashlib.sha256()
+    for f in doc["source_files"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != doc["source_sha256"] or kernel_key not in doc["kernels"]:
+        return None
+    return int(doc["kernels"][kernel_key]["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(layers_host, xs, seconds: float):
@@ -161,7 +267,6 @@ def main():
         log("bench.py: only --gpus 1 is supported (the path is single-GPU; see the design notes)")
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import ternary_weight_int8_tb_amd as tb
@@ -185,54 +290,108 @@ def main():
     dev_layers = upload(layers)
     torch.cuda.synchronize()
 
+    f1 = Fused64(tb, dev_layers, xs, 1, torch)
     s1 = Stream64(tb, dev_layers, xs, 1, torch)
     if args.profile_only:
+        f1.step()
         s1.step()
         torch.cuda.synchronize()
-        log("profile pass done")
+        f1.check()
+        log("profile pass done (one fused step, one pass of separate calls)")
         return
 
-    use_graph = not args.no_graph
-    t1, _ = time_stream(torch, s1, args.steps, args.warmup, use_graph)
-    gb1 = step_bytes / t1 / 1e9
-    log(f"M=1: {t1 * 1e3:.3f} ms/step, {t1 / args.layers * 1e6:.2f} us/layer, {gb1:.1f} GB/s")
+    def summary(total, per):
+        per = sorted(per)
+        return {"value": round(step_bytes / total / 1e9, 2), "unit": "GB/s",
+                "ms_per_step": round(total * 1e3, 4),
+                "us_per_layer": round(total / args.layers * 1e6, 3),
+                "pct_hbm_peak": round(100 * step_bytes / total / 1e9 / HBM_PEAK_GBS, 2),
+                "event_median_ms": round(per[len(per) // 2] * 1e3, 4),
+                "event_min_ms": round(per[0] * 1e3, 4)}
 
-    t_eager1, _ = time_stream(torch, s1, max(3, args.steps // 4), 1, False)
-    gu_s = gateup_event_timing(torch, s1, max(2, args.steps // 4))
-    gu_bytes = layers[0].gate.nbytes + layers[0].up.nbytes
-    gu_gbs = gu_bytes / gu_s / 1e9
-    log(f"gate/up kernel: {gu_s * 1e6:.2f} us/launch, {gu_gbs:.1f} GB/s (events, back to back)")
+    use_graph = not args.no_graph
+    paths = {}
+    tf, pf = time_stream(torch, f1, args.steps, args.warmup, False)
+    f1.check()
+    paths["fused"] = summary(tf, pf)
+    log(f"fused M=1: {tf / args.layers * 1e6:.2f} us/layer, {step_bytes / tf / 1e9:.1f} GB/s")
+    ts, ps = time_stream(torch, s1, args.steps, args.warmup, use_graph)
+    paths["separate"] = summary(ts, ps)
+    log(f"separate calls M=1 ({'graph' if use_graph else 'eager'}): {ts / args.layers * 1e6:.2f} "
+        f"us/layer, {step_bytes / ts / 1e9:.1f} GB/s")
+    te, pe = time_stream(torch, s1, max(3, args.steps // 4), 1, False)
+    paths["separate_eager"] = summary(te, pe)
+    log(f"separate calls M=1 (eager): {te / args.layers * 1e6:.2f} us/layer")
+    head = "fused" if tf <= ts else "separate"
+    t1 = tf if head == "fused" else ts
+
+    # roofline of the dominant kernel of the headline path, timed with HIP events on the
+    # stream it is launched on (the current stream)
+    if head == "fused":
+        launch_layers = min(32, args.layers)
+        k_s = fused_event_timing(torch, f1, max(3, args.steps // 4))
+        k_bytes = launch_layers * (layer_bytes + 2 * synth.HIDDEN * 4)
+        k_name = "ffn_layers_kernel<1,TERNARY2> (tb_ffn_layers, 32 layers per launch)"
+        k_key = "ffn_layers_kernel<1, 0>"
+    else:
+        k_s = gateup_event_timing(torch, s1, max(2, args.steps // 4))
+        k_bytes = layers[0].gate.nbytes + layers[0].up.nbytes + synth.HIDDEN + 40 * 4 + synth.INTER * 4
+        k_name = "gemv_ring_kernel<1,TERNARY2,GATEUP> (tb_ffn_gateup_silu)"
+        k_key = "gemv_ring_kernel<1, 0, 1>"
+    k_gbs = k_bytes / k_s / 1e9
+    log(f"dominant kernel {k_name}: {k_s * 1e6:.2f} us/launch, {k_gbs:.1f} GB/s")
+    del f1, s1
 
     res_m8 = None
     if not args.skip_m8:
+        m8 = {}
+        f8 = Fused64(tb, dev_layers, xs, 8, torch)
+        t8, p8 = time_stream(torch, f8, args.steps, args.warmup, False)
+        f8.check()
+        m8["fused"] = summary(t8, p8)
+        del f8
         s8 = Stream64(tb, dev_layers, xs, 8, torch)
-        t8, _ = time_stream(torch, s8, args.steps, args.warmup, use_graph)
-        gb8 = step_bytes / t8 / 1e9
-        gu8 = gateup_event_timing(torch, s8, max(2, args.steps // 4))
-        res_m8 = {"value": round(gb8, 2), "unit": "GB/s", "ms_per_step": round(t8 * 1e3, 4),
-                  "us_per_layer": round(t8 / args.layers * 1e6, 3),
-                  "pct_hbm_peak": round(100 * gb8 / HBM_PEAK_GBS, 2),
-                  "gateup_us": round(gu8 * 1e6, 3)}
-        log(f"M=8: {t8 * 1e3:.3f} ms/step, {t8 / args.layers * 1e6:.2f} us/layer, {gb8:.1f} GB/s")
+        t8s, p8s = time_stream(torch, s8, args.steps, args.warmup, use_graph)
+        m8["separate"] = summary(t8s, p8s)
         del s8
+        best = "fused" if t8 <= t8s else "separate"
+        res_m8 = dict(m8[best], entry_point=best, paths=m8)
+        log(f"M=8: fused {t8 / args.layers * 1e6:.2f} us/layer, separate "
+            f"{t8s / args.layers * 1e6:.2f} us/layer")
 
     res_sign = None
     if not args.skip_sign:
-        del dev_layers, s1
+        del dev_layers
         torch.cuda.empty_cache()
         sl = synth.ffn_stream(SEED + 100, args.layers, synth.FMT_SIGN1, threads=16)
         sbytes = sl[0].nbytes * args.layers
         sdev = upload(sl)
         res_sign = {"bytes_per_step": sbytes}
         for m in (1, 8):
+            row = {}
+            fs = Fused64(tb, sdev, xs, m, torch)
+            tfs, _ = time_stream(torch, fs, args.steps, args.warmup, False)
+            fs.check()
+            row["fused_us_per_layer"] = round(tfs / args.layers * 1e6, 3)
+            del fs
             ss = Stream64(tb, sdev, xs, m, torch)
-            ts, _ = time_stream(torch, ss, args.steps, args.warmup, use_graph)
-            res_sign[f"m{m}"] = {"value": round(sbytes / ts / 1e9, 2), "unit": "GB/s",
-                                 "us_per_layer": round(ts / args.layers * 1e6, 3),
-                                 "pct_hbm_peak": round(100 * sbytes / ts / 1e9 / HBM_PEAK_GBS, 2)}
-            log(f"sign M={m}: {ts / args.layers * 1e6:.2f} us/layer, {sbytes / ts / 1e9:.1f} GB/s")
+            tss, _ = time_stream(torch, ss, args.steps, args.warmup, use_graph)
+            row["separate_us_per_layer"] = round(tss / args.layers * 1e6, 3)
             del ss
+            tb_ = min(tfs, tss)
+            row.update({"value": round(sbytes / tb_ / 1e9, 2), "unit": "GB/s",
+                        "us_per_layer": round(tb_ / args.layers * 1e6, 3),
+                        "pct_hbm_peak": round(100 * sbytes / tb_ / 1e9 / HBM_PEAK_GBS, 2),
+                        "entry_point": "fused" if tfs <= tss else "separate"})
+            res_sign[f"m{m}"] = row
+            log(f"sign M={m}: fused {tfs / args.layers * 1e6:.2f}, separate "
+                f"{tss / args.layers * 1e6:.2f} us/layer")
         del sdev, sl
+        torch.cuda.empty_cache()
+
+    probe = read_probe(torch, 4 << 30)
+    log(f"read probe (4 GiB): {probe:.1f} GB/s")
+    gb1 = step_bytes / t1 / 1e9
 
     cpu = cpu_baseline(layers[:4], xs, args.cpu_seconds)
     log(f"cpu oracle: {cpu['value']} GB/s ({cpu['sample']})")
@@ -254,16 +413,23 @@ def main():
                    "layers": args.layers, "hidden": synth.HIDDEN, "intermediate": synth.INTER,
                    "rows": 1, "format": "ternary 2-bit, 128-weight blocks, fp16 scales",
                    "bytes_per_step": step_bytes,
-                   "launch": "hip graph replay" if use_graph else "eager"},
+                   "entry_point": {"fused": "tb_ffn_layers (one persistent launch per 32 layers)",
+                                   "separate": "tb_rotate_quant_i8 + tb_ffn_gateup_silu + "
+                                               "tb_ffn_down per layer, "
+                                               + ("hip graph replay" if use_graph else "eager")}[head],
+                   "layer_order": "strict: layer l+1 starts after layer l's outputs are written"},
         "us_per_layer": round(t1 / args.layers * 1e6, 3),
         "pct_hbm_peak": round(100 * gb1 / HBM_PEAK_GBS, 2),
-        "eager_us_per_layer": round(t_eager1 / args.layers * 1e6, 3),
+        "read_probe_gbs": round(probe, 1),
+        "pct_of_read_probe": round(100 * gb1 / probe, 2),
+        "paths_m1": paths,
         "m8": res_m8,
         "sign1_stream": res_sign,
-        "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_ring_kernel<1,TERNARY2,GATEUP> (tb_ffn_gateup_silu)",
-                     "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_s * 1e6, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(k_key),
+                     "kernel": k_name, "bytes_per_launch": k_bytes,
+                     "us_per_launch": round(k_s * 1e6, 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

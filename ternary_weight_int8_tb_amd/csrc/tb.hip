@@ -114,7 +114,8 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     // Row tiles are dealt round-robin over workgroups first, then over the waves of a
     // workgroup: tile t goes to workgroup t % G, wave (t / G) % W. Every CU gets the same
     // number of tiles (to within one).
-    const int gw = blockIdx.x + gridDim.x * (tid >> 6);   // this wave's first tile
+    // this wave's first tile; the wave index is uniform, so the schedule stays scalar
+    const int gw = blockIdx.x + gridDim.x * __builtin_amdgcn_readfirstlane(tid >> 6);
     const int GW = gridDim.x * kRingWaves;                 // tile stride between its tiles
     const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
     const int NT = gw < T ? (T - gw + GW - 1) / GW : 0;

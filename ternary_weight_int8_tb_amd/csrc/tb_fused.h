@@ -208,7 +208,10 @@ __global__ __launch_bounds__(kFusedThreads) void ffn_layers_kernel(FusedArgs a)
     const int C0 = H / kWpc, C1 = N / kWpc;
     const int I0 = (C0 + kChunkLanes - 1) / kChunkLanes, I1 = (C1 + kChunkLanes - 1) / kChunkLanes;
     const int T0 = N / kRowsPerWave, T1 = H / kRowsPerWave;
-    const int tid = threadIdx.x, lane = tid & 63, cl = lane & 15, rl = lane >> 4, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, cl = lane & 15, rl = lane >> 4;
+    // the wave index is the same in every lane; saying so lets the compiler keep the whole
+    // item schedule (and the weight descriptors built from it) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = gridDim.x, GW = G * kFusedWaves;
     const int t0 = blockIdx.x + G * wave;   // first tile of this wave (both phases)
     const int NT0 = t0 < T0 ? (T0 - t0 + GW - 1) / GW : 0;
