@@ -35,6 +35,7 @@
 #include "tb.h"
 #include "tb_device.h"
 #include "tb_fused.h"
+#include "tb_fused_lr.h"
 
 namespace {
 
@@ -594,6 +595,33 @@ FusedFn fused_pick_m(int m)
     }
 }
 
+using FusedLrFn = void (*)(FusedArgs, int);
+
+// The sign format's gate/up decode needs more than the 128 registers a 16-wave workgroup
+// allows from m = 2 on: those shapes run the register-ring kernel (not instantiated here).
+template <int M, int FMT>
+FusedLrFn fused_lr_entry()
+{
+    if constexpr (FMT == TB_FMT_SIGN1 && M > 1)
+        return nullptr;
+    else
+        return ffn_layers_lr_kernel<M, FMT>;
+}
+
+template <int FMT>
+FusedLrFn fused_lr_pick_m(int m)
+{
+    switch (m) {
+    case 1: return fused_lr_entry<1, FMT>();
+    case 2: return fused_lr_entry<2, FMT>();
+    case 3: return fused_lr_entry<3, FMT>();
+    case 4: return fused_lr_entry<4, FMT>();
+    case 5: return fused_lr_entry<5, FMT>();
+    case 6: return fused_lr_entry<6, FMT>();
+    default: return nullptr;
+    }
+}
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
@@ -613,16 +641,39 @@ WsLayout ws_layout(int m, int inter)
     return w;
 }
 
-// LDS bytes of the fused kernel (must match ffn_layers_kernel's carve-up).
-size_t fused_lds_bytes(int fmt, int m, int hidden, int inter)
+// Activation and block-term bytes of the fused kernels' LDS (must match their carve-up).
+void fused_lds_parts(int fmt, int m, int hidden, int inter, size_t *act, size_t *nbmax)
 {
     const int wpc = fmt == TB_FMT_TERNARY2 ? 64 : 128;
     const int step = (fmt == TB_FMT_TERNARY2 ? 1024 : 2048) * m;
     const int I0 = (hidden / wpc + kChunkLanes - 1) / kChunkLanes;
     const int I1 = (inter / wpc + kChunkLanes - 1) / kChunkLanes;
-    const size_t act = std::max((size_t)I1 * step, (size_t)I0 * step + (size_t)m * hidden);
+    *act = std::max((size_t)I1 * step, (size_t)I0 * step + (size_t)m * hidden);
     const int bps = kChunkLanes / (fmt == TB_FMT_TERNARY2 ? 2 : 1);
-    const size_t nbmax = (size_t)std::max(hidden, inter) / kBlock + bps;
+    *nbmax = (size_t)std::max(hidden, inter) / kBlock + bps;
+}
+
+// Loader-wave kernel: ring units per consumer that fit in `limit` bytes of LDS (0 if
+// fewer than kMinRingUnits), and the LDS bytes it then uses.
+int fused_lr_units(int fmt, int m, int hidden, int inter, size_t limit, size_t *lds)
+{
+    size_t act, nbmax;
+    fused_lds_parts(fmt, m, hidden, inter, &act, &nbmax);
+    const size_t off = (size_t)lr_ring_offset((int)act, (int)nbmax, m);
+    if (off >= limit)
+        return 0;
+    const int u = (int)std::min<size_t>(kMaxRingUnits, (limit - off) / ((size_t)kLrConsumers * kUnitBytes));
+    if (u < kMinRingUnits)
+        return 0;
+    *lds = off + (size_t)u * kLrConsumers * kUnitBytes;
+    return u;
+}
+
+// LDS bytes of the register-ring fused kernel (must match ffn_layers_kernel's carve-up).
+size_t fused_lds_bytes(int fmt, int m, int hidden, int inter)
+{
+    size_t act, nbmax;
+    fused_lds_parts(fmt, m, hidden, inter, &act, &nbmax);
     return act + 2 * nbmax * m * 4 + 16;
 }
 
@@ -837,15 +888,25 @@ int tb_ffn_layers(const tb_ffn_weights *layers, int num_layers, const float *x, 
     DeviceInfo info;
     if ((rc = device_info(&info)))
         return rc;
-    const size_t lds = fused_lds_bytes(F, m, H, N);
-    if (lds > (size_t)info.lds_limit)
-        return TB_EUNSUPPORTED;
-    FusedFn fn = F == TB_FMT_TERNARY2 ? fused_pick_m<TB_FMT_TERNARY2>(m) : fused_pick_m<TB_FMT_SIGN1>(m);
-    if (!fn)
-        return TB_EINVAL;
+    // the loader-wave kernel when its LDS rings fit (small m), else the register-ring one
+    size_t lds = 0;
+    const int units = fused_lr_units(F, m, H, N, (size_t)info.lds_limit, &lds);
+    FusedLrFn lr_fn = nullptr;
+    FusedFn fn = nullptr;
+    if (units > 0)
+        lr_fn = F == TB_FMT_TERNARY2 ? fused_lr_pick_m<TB_FMT_TERNARY2>(m)
+                                     : fused_lr_pick_m<TB_FMT_SIGN1>(m);
+    if (!lr_fn) {
+        lds = fused_lds_bytes(F, m, H, N);
+        if (lds > (size_t)info.lds_limit)
+            return TB_EUNSUPPORTED;
+        fn = F == TB_FMT_TERNARY2 ? fused_pick_m<TB_FMT_TERNARY2>(m) : fused_pick_m<TB_FMT_SIGN1>(m);
+        if (!fn)
+            return TB_EINVAL;
+    }
+    const void *kern = lr_fn ? reinterpret_cast<const void *>(lr_fn) : reinterpret_cast<const void *>(fn);
     if (lds > 65536 &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return TB_EHIP;
 
     uint8_t *wsb = static_cast<uint8_t *>(ws);
@@ -879,7 +940,10 @@ int tb_ffn_layers(const tb_ffn_weights *layers, int num_layers, const float *x, 
         a.chain = chain ? 1 : 0;
         a.x = chain ? (start == 0 ? x : y + (size_t)(start - 1) * m * H) : x + (size_t)start * m * H;
         a.y = y + (size_t)start * m * H;
-        hipLaunchKernelGGL(fn, dim3(info.cus), dim3(kFusedThreads), lds, s, a);
+        if (lr_fn)
+            hipLaunchKernelGGL(lr_fn, dim3(info.cus), dim3(kLrThreads), lds, s, a, units);
+        else
+            hipLaunchKernelGGL(fn, dim3(info.cus), dim3(kFusedThreads), lds, s, a);
         if (hipGetLastError() != hipSuccess)
             return TB_EHIP;
     }

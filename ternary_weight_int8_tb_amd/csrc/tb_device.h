@@ -447,6 +447,92 @@ __device__ __forceinline__ void chunk_sums_step(const uint4 &w0, const uint4 &w1
     }
 }
 
+// The same sums with the step's activations already in registers (av[plane][m], read with
+// load_act from the lane's slot address), so a caller can read the next step while it
+// computes this one.
+template <int M, int FMT>
+__device__ __forceinline__ void load_act(const uint8_t *lds,
+                                         uint4 (&av)[StepLayout<M, FMT>::kPlanes][M])
+{
+    using L = StepLayout<M, FMT>;
+#pragma unroll
+    for (int p = 0; p < L::kPlanes; ++p)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            av[p][m] = *reinterpret_cast<const uint4 *>(lds + L::offset(p, m));
+}
+
+template <int M, int FMT, bool TWO>
+__device__ __forceinline__ void chunk_sums_act(const uint4 &w0, const uint4 &w1,
+                                               const uint4 (&av)[StepLayout<M, FMT>::kPlanes][M],
+                                               int (&is0)[M], int (&is1)[M])
+{
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        is0[m] = 0;
+        is1[m] = 0;
+    }
+    const uint32_t cw0[4] = {w0.x, w0.y, w0.z, w0.w};
+    const uint32_t cw1[4] = {w1.x, w1.y, w1.z, w1.w};
+    if (FMT == TB_FMT_TERNARY2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t d0, d1, d2, d3, e0 = 0, e1 = 0, e2 = 0, e3 = 0;
+            decode_ternary(cw0[j], d0, d1, d2, d3);
+            if (TWO)
+                decode_ternary(cw1[j], e0, e1, e2, e3);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint4 a = av[j][m];
+                is0[m] = dot4(d0, a.x, is0[m]);
+                is0[m] = dot4(d1, a.y, is0[m]);
+                is0[m] = dot4(d2, a.z, is0[m]);
+                is0[m] = dot4(d3, a.w, is0[m]);
+                if (TWO) {
+                    is1[m] = dot4(e0, a.x, is1[m]);
+                    is1[m] = dot4(e1, a.y, is1[m]);
+                    is1[m] = dot4(e2, a.z, is1[m]);
+                    is1[m] = dot4(e3, a.w, is1[m]);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            is0[m] = pair_add(is0[m]);
+            if (TWO)
+                is1[m] = pair_add(is1[m]);
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t b0[4], b1[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    b0[j] = (cw0[d] >> (4 * h + j)) & 0x01010101u;
+                    if (TWO)
+                        b1[j] = (cw1[d] >> (4 * h + j)) & 0x01010101u;
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const uint4 a = av[d * 2 + h][m];
+                    is0[m] = dot4(b0[0], a.x, is0[m]);
+                    is0[m] = dot4(b0[1], a.y, is0[m]);
+                    is0[m] = dot4(b0[2], a.z, is0[m]);
+                    is0[m] = dot4(b0[3], a.w, is0[m]);
+                    if (TWO) {
+                        is1[m] = dot4(b1[0], a.x, is1[m]);
+                        is1[m] = dot4(b1[1], a.y, is1[m]);
+                        is1[m] = dot4(b1[2], a.z, is1[m]);
+                        is1[m] = dot4(b1[3], a.w, is1[m]);
+                    }
+                }
+            }
+        }
+    }
+}
+
 // dq[M][nb] -> LDS; for the sign format also sum(q) per block -> LDS (int).
 template <int M, int FMT, bool COHERENT>
 __device__ __forceinline__ void stage_block_terms(float *dq_s, int *qsum_s, const float *dq,
