@@ -540,7 +540,10 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     const size_t pad_blocks = (size_t)(kChunkLanes / (w0->fmt == TB_FMT_TERNARY2 ? 2 : 1));
     const size_t ring_terms = (size_t)m * (nb + pad_blocks) * 4 * (w0->fmt == TB_FMT_TERNARY2 ? 1 : 2);
     const size_t ring_lds = (size_t)steps * step_bytes + ring_terms;
-    if (ring_lds <= (size_t)info.lds_limit) {
+    // (the sign format's ring kernels need more than 256 registers from m = 6 on: those
+    // shapes take the sliced kernel below)
+    const bool ring_fits_registers = !(w0->fmt == TB_FMT_SIGN1 && m >= 6);
+    if (ring_lds <= (size_t)info.lds_limit && ring_fits_registers) {
         GemvFn fn = gemv_ring_kernel_pick(w0->fmt, mode, m);
         if (!fn)
             return TB_EINVAL;

@@ -170,6 +170,9 @@ __device__ __forceinline__ void stage_from_lds(uint8_t *act, const int8_t *qnat,
 }
 
 // Stage int8 activations written by other workgroups (global [m][k]) into the step layout.
+// Each thread issues the loads of up to kStageBatch units before it stores any, so the
+// staging costs about one memory round trip per batch instead of one per unit.
+constexpr int kStageBatch = 4;
 template <int M, int FMT>
 __device__ __forceinline__ void stage_from_global_coherent(uint8_t *act, const int8_t *q, int k,
                                                            uint32_t q_bytes)
@@ -177,18 +180,67 @@ __device__ __forceinline__ void stage_from_global_coherent(uint8_t *act, const i
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(q, q_bytes);
     const int per_row = (FMT == TB_FMT_TERNARY2 ? k / 64 : k / 128) * 4;
     const int units = M * per_row;
-    for (int u = threadIdx.x; u < units; u += kFusedThreads) {
-        const int m = u / per_row, g = u % per_row;
-        const int c = g >> 2, j = g & 3;
-        StageUnit<FMT> su;
-        if (FMT == TB_FMT_TERNARY2) {
-            su.lo = buffer_load16_coherent(r, (uint32_t)(m * k + c * 64 + j * 16));
-        } else {
-            const uint32_t off = (uint32_t)(m * k + c * 128 + j * 32);
-            su.lo = buffer_load16_coherent(r, off);
-            su.hi = buffer_load16_coherent(r, off + 16);
+    for (int u0 = threadIdx.x; u0 < units; u0 += kStageBatch * kFusedThreads) {
+        StageUnit<FMT> su[kStageBatch];
+#pragma unroll
+        for (int i = 0; i < kStageBatch; ++i) {
+            const int u = u0 + i * kFusedThreads;
+            const int m = u / per_row, g = u % per_row;
+            const int c = g >> 2, j = g & 3;
+            const bool in = u < units;
+            if (FMT == TB_FMT_TERNARY2) {
+                su[i].lo = buffer_load16_coherent(r, in ? (uint32_t)(m * k + c * 64 + j * 16) : kOutOfRange);
+            } else {
+                const uint32_t off = in ? (uint32_t)(m * k + c * 128 + j * 32) : kOutOfRange;
+                su[i].lo = buffer_load16_coherent(r, off);
+                su[i].hi = buffer_load16_coherent(r, in ? off + 16 : kOutOfRange);
+            }
         }
-        stage_unit_store_step<M, FMT>(su, act, k, u);
+#pragma unroll
+        for (int i = 0; i < kStageBatch; ++i) {
+            const int u = u0 + i * kFusedThreads;
+            if (u < units)
+                stage_unit_store_step<M, FMT>(su[i], act, k, u);
+        }
+    }
+}
+
+// Rotate + quantise x ([M][H], read device-coherently) into LDS: q in natural order,
+// dq and the code sums as block terms [b][m]. One 16-lane group per 128-block; a group
+// loads up to kXBatch blocks before it computes any, so the loads share one round trip.
+constexpr int kXBatch = 3;
+template <int M>
+__device__ __forceinline__ void rotquant_x_to_lds(__amdgpu_buffer_rsrc_t r_x, int H, float unit,
+                                                  int8_t *qnat, float *dq_s, int *qs_s)
+{
+    const int nbh = H / kBlock, total = M * nbh;
+    const int lane16 = threadIdx.x & 15;
+    for (int p0 = threadIdx.x >> 4; p0 < total; p0 += kXBatch * kFusedGroups) {
+        float v[kXBatch][8];
+#pragma unroll
+        for (int i = 0; i < kXBatch; ++i) {
+            const int p = p0 + i * kFusedGroups;
+            const uint32_t off =
+                p < total ? (uint32_t)(((p / nbh) * H + (p % nbh) * kBlock + lane16 * 8) * 4) : kOutOfRange;
+            load8_coherent(r_x, off, v[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kXBatch; ++i) {
+            const int p = p0 + i * kFusedGroups;
+            if (p < total) {   // the same for the 16 lanes of a group
+                const int m = p / nbh, b = p % nbh;
+                uint32_t packed[2];
+                float dq;
+                int qsum;
+                rotquant_regs(v[i], lane16, unit, packed, dq, qsum);
+                *reinterpret_cast<uint2 *>(qnat + m * H + b * kBlock + lane16 * 8) =
+                    make_uint2(packed[0], packed[1]);
+                if (lane16 == 0) {
+                    dq_s[b * M + m] = dq;
+                    qs_s[b * M + m] = qsum;
+                }
+            }
+        }
     }
 }
 
@@ -332,22 +384,7 @@ __global__ __launch_bounds__(kFusedThreads) void ffn_layers_kernel(FusedArgs a)
                                                : a.x + (size_t)(a.chain ? 0 : l) * M * H;
             // read coherently: with chaining, x is the previous layer's y from other workgroups
             const __amdgpu_buffer_rsrc_t r_x = buffer_rsrc(xl, (uint32_t)(M * H * 4));
-            for (int p = tid >> 4; p < M * nbh; p += kFusedGroups) {
-                const int m = p / nbh, b = p % nbh;
-                const uint32_t off = (uint32_t)((m * H + b * kBlock + (lane & 15) * 8) * 4);
-                float v[8];
-                load8_coherent(r_x, off, v);
-                uint32_t packed[2];
-                float dq;
-                int qsum;
-                rotquant_regs(v, lane & 15, a.unit, packed, dq, qsum);
-                *reinterpret_cast<uint2 *>(qnat + m * H + b * kBlock + (lane & 15) * 8) =
-                    make_uint2(packed[0], packed[1]);
-                if ((lane & 15) == 0) {
-                    dq_s[b * M + m] = dq;
-                    qs_s[b * M + m] = qsum;
-                }
-            }
+            rotquant_x_to_lds<M>(r_x, H, a.unit, qnat, dq_s, qs_s);
             for (int i = tid; i < kBps * M; i += kFusedThreads) {   // zero padding blocks
                 dq_s[nbh * M + i] = 0.0f;
                 qs_s[nbh * M + i] = 0;

@@ -394,22 +394,7 @@ __global__ __launch_bounds__(kLrThreads) void ffn_layers_lr_kernel(FusedArgs a, 
                                                : a.x + (size_t)(a.chain ? 0 : l) * M * H;
             // read coherently: with chaining, x is the previous layer's y from other workgroups
             const __amdgpu_buffer_rsrc_t r_x = buffer_rsrc(xl, (uint32_t)(M * H * 4));
-            for (int p = tid >> 4; p < M * nbh; p += kFusedGroups) {
-                const int m = p / nbh, b = p % nbh;
-                const uint32_t off = (uint32_t)((m * H + b * kBlock + (lane & 15) * 8) * 4);
-                float v[8];
-                load8_coherent(r_x, off, v);
-                uint32_t packed[2];
-                float dq;
-                int qsum;
-                rotquant_regs(v, lane & 15, a.unit, packed, dq, qsum);
-                *reinterpret_cast<uint2 *>(qnat + m * H + b * kBlock + (lane & 15) * 8) =
-                    make_uint2(packed[0], packed[1]);
-                if ((lane & 15) == 0) {
-                    dq_s[b * M + m] = dq;
-                    qs_s[b * M + m] = qsum;
-                }
-            }
+            rotquant_x_to_lds<M>(r_x, H, a.unit, qnat, dq_s, qs_s);
             for (int i = tid; i < kBps * M; i += kFusedThreads) {   // zero padding blocks
                 dq_s[nbh * M + i] = 0.0f;
                 qs_s[nbh * M + i] = 0;
