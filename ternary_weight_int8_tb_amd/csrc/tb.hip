@@ -14,14 +14,14 @@
 //   * wave64. A wave covers 4 weight rows x 16 "chunk lanes". A chunk is 16 bytes of codes:
 //     64 ternary weights (half a block) or 128 sign weights (one block). In each step the
 //     16 lanes of a row read 256 contiguous bytes: coalesced 16-byte non-temporal loads.
-//   * Persistent streaming (gemv_ring_kernel): one workgroup of 8 waves per CU stages the
-//     int8 activation once, then every wave walks a flat list of (row tile, chunk step)
-//     items. Loads run 8 items ahead through a register ring, so each CU keeps about
-//     64 KB of weights in flight, across row-tile boundaries too.
+//   * Streaming (gemv_ring_kernel): one workgroup of 16 waves per CU stages the int8
+//     activation once; each CU owns an equal share of the row tiles, and its waves take
+//     (tile, step) items from an LDS counter, loads running two or three items ahead in a
+//     register ring. Each step's partial sums meet in LDS and are added in step order.
 //   * 2-bit decode with v_perm_b32 (9 VALU ops per 16 weights, shared by all M rows),
 //     v_dot4c_i32_i8 against the LDS-staged transposed activation, one DPP add to join the
-//     two half-block sums, an fp32 fold per block and a fixed shuffle tree per row
-//     (tb_device.h).
+//     two half-block sums, an fp32 term per block, a fixed DPP tree per row and step, and
+//     the step partials summed in step order (tb_device.h).
 //   * No MFMA: with M <= 8 rows this is not a dense contraction. No floating-point atomics.
 #include <hip/hip_runtime.h>
 
@@ -43,9 +43,19 @@ using namespace tbk;
 
 constexpr int kRotThreads = 256;
 constexpr int kSlicedThreads = 256;
-constexpr int kRingWaves = 8;
+#ifndef TB_RING_WAVES
+#define TB_RING_WAVES 16
+#endif
+#ifndef TB_RING_DEPTH_TWO
+#define TB_RING_DEPTH_TWO 2
+#endif
+#ifndef TB_RING_DEPTH_ONE
+#define TB_RING_DEPTH_ONE 3
+#endif
+constexpr int kRingWaves = TB_RING_WAVES;
 constexpr int kRingThreads = 64 * kRingWaves;
-constexpr int kRingDepth = 4;
+constexpr int kRingDepthTwo = TB_RING_DEPTH_TWO;   // items in flight per wave, gate + up
+constexpr int kRingDepthOne = TB_RING_DEPTH_ONE;   // one matrix
 
 enum Mode { kModeY = 0, kModeGateUp = 1, kModeIsum = 2 };
 
@@ -86,17 +96,24 @@ __device__ __forceinline__ void store_row(const GemvArgs &a, int row, const floa
 }
 
 // ------------------------------------------------------------------------------------
-// Persistent ring GEMV: the whole activation is staged once per workgroup (step-major
-// layout); waves walk their (tile, step) items with loads kRingDepth items ahead.
-// A wave owns row tiles t0, t0 + GW, t0 + 2 GW, ... (4 rows each); in step i of a tile,
-// lane cl reads chunk 16 i + cl of its row. The per-row arithmetic is the same as in every
-// other kernel here: lane cl folds its chunks in order of i, then the fixed row tree.
+// Streaming GEMV: one workgroup per CU, the whole activation staged once in LDS
+// (step-major layout).
+//   * A row tile is 4 rows; workgroup c owns the contiguous tiles [tA, tB) of a near-equal
+//     split of all tiles over the grid, so every CU streams the same bytes.
+//   * An item is one step of one tile: in step i, lane cl of a row reads chunk 16 i + cl.
+//     The waves of a workgroup share its items through an LDS counter: a wave takes the
+//     next item when it refills a ring slot, so waves that the SIMD arbiter serves less
+//     often simply take fewer items (the older wave on a SIMD is favoured).
+//   * Loads run a few items ahead of the math in a register ring.
+// Fold order (the same in every kernel here, and independent of M, of the grid and of
+// which wave took which item; so a batched row is bit-identical to the row run alone):
+// a step's partial is the fixed 16-lane row tree of the lanes' terms (s * dq) * isum; a
+// row's output is the sum of its step partials in step order, starting from +0. The step
+// partials meet in LDS.
 //
 // The loop is written for the VALU budget: at M = 1 one 1 KB wave item needs 52 VALU ops
-// of decode and dot products, so the rest is kept to a handful. All addresses advance
-// incrementally (no multiplies); rows past n, items past the wave's work and ragged
-// chunks use out-of-range buffer offsets, which read zeros; the fold runs unconditionally
-// (an invalid lane has zero codes and a zero scale, so it adds zero).
+// of decode and dot products, so the rest is kept to a handful. Rows past n, empty slots
+// and ragged chunks use out-of-range buffer offsets, which read zeros.
 // ------------------------------------------------------------------------------------
 template <int M, int FMT, int MODE>
 __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
@@ -107,26 +124,26 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     constexpr int kWpc = Fmt<FMT>::kWeightsPerChunk;
     constexpr int kCpb = Fmt<FMT>::kChunksPerBlock;
     constexpr int kBlocksPerStep = kChunkLanes / kCpb;   // 8 ternary, 16 sign
+    constexpr int kDepth = kTwo ? kRingDepthTwo : kRingDepthOne;
 
     const int k = a.k, n = a.n, nb = k / kBlock;
     const int C = k / kWpc;                 // chunks per row
-    const int I = (C + kChunkLanes - 1) / kChunkLanes;
+    const int I = (C + kChunkLanes - 1) / kChunkLanes;   // steps per tile
     const int tid = threadIdx.x, lane = tid & 63, cl = lane & 15, rl = lane >> 4;
-    // Row tiles are dealt round-robin over workgroups first, then over the waves of a
-    // workgroup: tile t goes to workgroup t % G, wave (t / G) % W. Every CU gets the same
-    // number of tiles (to within one).
-    // this wave's first tile; the wave index is uniform, so the schedule stays scalar
-    const int gw = blockIdx.x + gridDim.x * __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int GW = gridDim.x * kRingWaves;                 // tile stride between its tiles
+    const int G = gridDim.x, c = blockIdx.x;
     const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
-    const int NT = gw < T ? (T - gw + GW - 1) / GW : 0;
-    const int J = NT * I;
+    const int tA = part_lo(T, G, c), tB = part_lo(T, G, c + 1);
+    const int J = (tB - tA) * I;            // this workgroup's items
     const uint32_t row_bytes = (uint32_t)C * 16u;
 
     uint8_t *act = lds;
-    // block terms, zero padded by one step of blocks so invalid lanes read zeros
+    // block terms, zero padded by one step of blocks so ragged lanes read zeros
     float *dq_s = reinterpret_cast<float *>(lds + (size_t)I * L::kStepBytes);
     int *qsum_s = reinterpret_cast<int *>(dq_s + (size_t)(nb + kBlocksPerStep) * M);
+    int *ctr_s = qsum_s + (FMT == TB_FMT_SIGN1 ? (nb + kBlocksPerStep) * M : 0);   // item counter
+    // step partials [item][row in tile][m][gate, up] (gate only for one matrix)
+    constexpr int kParts = kTwo ? 2 : 1;
+    float *part_s = reinterpret_cast<float *>(ctr_s + 4);
 
     const __amdgpu_buffer_rsrc_t rout =
         MODE == kModeIsum ? buffer_rsrc(a.isum, (uint32_t)((size_t)M * n * nb * 4))
@@ -136,176 +153,203 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     const __amdgpu_buffer_rsrc_t rc1 = buffer_rsrc(kTwo ? a.codes1 : a.codes0, a.codes_bytes);
     const __amdgpu_buffer_rsrc_t rsc1 = buffer_rsrc(kTwo ? a.scales1 : a.scales0, a.scales_bytes);
 
-    // ---- load-side cursor: per-lane byte offsets of the next item ---------------------
+    if (tid == 0)
+        *ctr_s = kRingWaves;   // wave w starts with item w
+    if (FMT == TB_FMT_SIGN1)
+        for (int i = tid; i < (nb + kBlocksPerStep) * M; i += kRingThreads)
+            qsum_s[i] = 0;
+    __syncthreads();
+
+    // ---- issue side ------------------------------------------------------------------
+    // The wave's items increase, so (tile, step) follow by carrying the step over.
     // Lanes whose chunk is past C in the last step of a row (ragged k) read zeros.
     const uint32_t ragged = (C % kChunkLanes != 0 && cl >= C % kChunkLanes) ? kOutOfRange : 0u;
-    int ltile = 0, lstep = 0;
-    uint32_t lrow = (uint32_t)(gw * kRowsPerWave + rl);
-    uint32_t loff = lrow * row_bytes + (uint32_t)cl * 16u;               // codes
-    uint32_t lsoff = (lrow * (uint32_t)nb + (uint32_t)(cl / kCpb)) * 2u;  // scales
-    if (NT == 0) {
-        loff = kOutOfRange;
-        lsoff = kOutOfRange;
-    }
-
-    uint4 rb0[kRingDepth], rb1[kRingDepth];
+    int gidx = 0, gtile = 0, gstep = 0;   // the wave's last taken item and its (tile, step)
+    auto advance_to = [&](int idx) {
+        gstep += idx - gidx;
+        gidx = idx;
+        while (gstep >= I) {
+            gstep -= I;
+            ++gtile;
+        }
+    };
+    uint4 rb0[kDepth], rb1[kDepth];
     // scales travel as 32-bit values: 16-bit ring entries would be packed in pairs, and
     // packing waits for the loads
-    uint32_t rs0[kRingDepth], rs1[kRingDepth];
-    auto issue = [&](uint4 &w0, uint4 &w1, uint32_t &s0, uint32_t &s1) {
-        const uint32_t extra = lstep == I - 1 ? ragged : 0u;
-        w0 = buffer_load16_nt(rc0, loff + extra);
-        s0 = buffer_load_u32(rsc0, (lsoff & ~3u) + extra);
+    uint32_t rs0[kDepth], rs1[kDepth];
+    int rit[kDepth];   // the slot's item as tile << 16 | step, or -1
+    int pending = tid >> 6;   // the next item, taken one issue ahead (LDS add in flight)
+    auto issue = [&](uint4 &w0, uint4 &w1, uint32_t &s0, uint32_t &s1, int &it) {
+        const int idx = __builtin_amdgcn_readfirstlane(pending);
+        uint32_t off = kOutOfRange, soff = kOutOfRange;
+        it = -1;
+        if (idx < J) {
+            advance_to(idx);
+            it = gtile << 16 | gstep;
+            const uint32_t row = (uint32_t)((tA + gtile) * kRowsPerWave + rl);
+            const uint32_t extra = gstep == I - 1 ? ragged : 0u;
+            if (row < (uint32_t)n) {
+                off = (row * row_bytes + (uint32_t)cl * 16u + (uint32_t)gstep * 256u) | extra;
+                soff = (((row * (uint32_t)nb + (uint32_t)(gstep * kBlocksPerStep + cl / kCpb)) * 2u) & ~3u) | extra;
+            }
+            // take the next item now; the add completes while this one streams
+            int v = 0;
+            if (lane == 0)
+                v = atomicAdd(ctr_s, 1);
+            pending = v;
+        }
+        w0 = buffer_load16_nt(rc0, off);
+        s0 = buffer_load_u32(rsc0, soff);
         if (kTwo) {
-            w1 = buffer_load16_nt(rc1, loff + extra);
-            s1 = buffer_load_u32(rsc1, (lsoff & ~3u) + extra);
+            w1 = buffer_load16_nt(rc1, off);
+            s1 = buffer_load_u32(rsc1, soff);
         } else {
             w1 = make_uint4(0, 0, 0, 0);
             s1 = 0;
         }
-        if (++lstep == I) {
-            lstep = 0;
-            ++ltile;
-            lrow += (uint32_t)(GW * kRowsPerWave);
-            if (ltile < NT) {
-                loff = lrow * row_bytes + (uint32_t)cl * 16u;
-                lsoff = (lrow * (uint32_t)nb + (uint32_t)(cl / kCpb)) * 2u;
-            } else {
-                loff = kOutOfRange;
-                lsoff = kOutOfRange;
-            }
-        } else {
-            loff += 16u * kChunkLanes;
-            lsoff += 2u * kBlocksPerStep;
-        }
     };
 
-    // ---- first staging round, ring prologue, rest of the staging -------------------
-    constexpr int kStageRound = 4;
+    // ---- staging: the small loads (q and the block terms) go first, then the ring
+    // prologue, then the LDS stores, so that the activation is not queued behind the
+    // weight stream. The sign format's sum(q) per block is accumulated with LDS integer
+    // adds from the staged units (exact, any order).
+    constexpr int kStageRound = 4, kTermRound = 2;
     const int units = M * C * 4;
+    const int nterm = (nb + kBlocksPerStep) * M;
     StageUnit<FMT> su[kStageRound];
 #pragma unroll
     for (int r = 0; r < kStageRound; ++r)
         if (tid + r * kRingThreads < units)
             stage_unit_load_step<M, FMT, false>(su[r], a.q, k, tid + r * kRingThreads);
+    // block terms [b][m] (transposed from the [m][b] input) plus zero padding
+    float dv[kTermRound];
 #pragma unroll
-    for (int d = 0; d < kRingDepth; ++d)
-        issue(rb0[d], rb1[d], rs0[d], rs1[d]);
+    for (int r = 0; r < kTermRound; ++r) {
+        const int i = tid + r * kRingThreads, b = i / M, m = i % M;
+        dv[r] = (MODE != kModeIsum && i < nterm && b < nb) ? a.dq[m * nb + b] : 0.0f;
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+        issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
+    auto qsum_add = [&](const StageUnit<FMT> &u, int unit) {
+        if (FMT == TB_FMT_SIGN1) {
+            const int per_row = C * 4, m = unit / per_row, b = (unit % per_row) >> 2;
+            const uint32_t w[8] = {u.lo.x, u.lo.y, u.lo.z, u.lo.w, u.hi.x, u.hi.y, u.hi.z, u.hi.w};
+            int sum = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sum = dot4(w[e], 0x01010101u, sum);
+            atomicAdd(qsum_s + b * M + m, sum);
+        }
+    };
 #pragma unroll
     for (int r = 0; r < kStageRound; ++r)
-        if (tid + r * kRingThreads < units)
+        if (tid + r * kRingThreads < units) {
             stage_unit_store_step<M, FMT>(su[r], act, k, tid + r * kRingThreads);
+            qsum_add(su[r], tid + r * kRingThreads);
+        }
+#pragma unroll
+    for (int r = 0; r < kTermRound; ++r)
+        if (tid + r * kRingThreads < nterm)
+            dq_s[tid + r * kRingThreads] = dv[r];
     for (int u = tid + kStageRound * kRingThreads; u < units; u += kRingThreads) {
         StageUnit<FMT> one;
         stage_unit_load_step<M, FMT, false>(one, a.q, k, u);
         stage_unit_store_step<M, FMT>(one, act, k, u);
+        qsum_add(one, u);
     }
-    // block terms [b][m] (transposed from the [m][b] input) plus zero padding
-    for (int i = tid; i < (nb + kBlocksPerStep) * M; i += kRingThreads) {
+    for (int i = tid + kTermRound * kRingThreads; i < nterm; i += kRingThreads) {
         const int b = i / M, m = i % M;
         dq_s[i] = (MODE != kModeIsum && b < nb) ? a.dq[m * nb + b] : 0.0f;
-        if (FMT == TB_FMT_SIGN1) {
-            int s = 0;
-            if (b < nb) {
-                const int8_t *src = a.q + (size_t)m * k + (size_t)b * kBlock;
-                for (int j = 0; j < kBlock; j += 16) {
-                    const uint4 g = *reinterpret_cast<const uint4 *>(src + j);
-                    s = dot4(g.x, 0x01010101u, s);
-                    s = dot4(g.y, 0x01010101u, s);
-                    s = dot4(g.z, 0x01010101u, s);
-                    s = dot4(g.w, 0x01010101u, s);
-                }
-            }
-            qsum_s[i] = s;
-        }
     }
     __syncthreads();
 
-    // ---- compute-side cursor ----------------------------------------------------------
+    // ---- compute side -----------------------------------------------------------------
     const uint8_t *lds_lane = act + cl * 16;
     const int blk_lane = cl / kCpb;                 // block of this lane within a step
-    int cstep = 0, ctile = 0;
-    int crow = gw * kRowsPerWave + rl;
-    const uint8_t *cact = lds_lane;
-    const float *cdq = dq_s + blk_lane * M;
-    const int *cqs = qsum_s + blk_lane * M;
-    uint32_t cisum = ((uint32_t)crow * (uint32_t)nb + (uint32_t)blk_lane) * 4u;   // isum export
-    // which half of a scale word belongs to this lane: the parity of its block index,
-    // fixed within a row tile because a step advances the block by an even count
-    uint32_t cshift = (((uint32_t)crow * (uint32_t)nb + (uint32_t)blk_lane) & 1u) * 16u;
-
-    float acc0[M], acc1[M];
+    auto consume = [&](const uint4 &w0, const uint4 &w1, uint32_t sw0, uint32_t sw1, int it) {
+        const int tile = it >> 16, step = it & 0xffff;
+        const uint32_t row = (uint32_t)((tA + tile) * kRowsPerWave + rl);
+        const int blk = step * kBlocksPerStep + blk_lane;
+        int is0[M], is1[M];
+        chunk_sums_step<M, FMT, kTwo>(w0, w1, lds_lane + (size_t)step * L::kStepBytes, is0, is1);
+        const int *cqs = qsum_s + blk * M;
+        if (MODE == kModeIsum) {
+            // the export writes every valid block once (even lane of a ternary pair)
+            const bool wr = row < (uint32_t)n && step * kChunkLanes + cl < C && (kCpb == 1 || !(cl & 1));
+            const uint32_t o = (row * (uint32_t)nb + (uint32_t)blk) * 4u;
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        acc0[m] = 0.0f;
-        acc1[m] = 0.0f;
-    }
-    const int Jpad = (J + kRingDepth - 1) / kRingDepth * kRingDepth;
-    for (int j0 = 0; j0 < Jpad; j0 += kRingDepth) {
+            for (int m = 0; m < M; ++m) {
+                const int v = FMT == TB_FMT_SIGN1 ? 2 * is0[m] - cqs[m] : is0[m];
+                __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, rout, wr ? o : kOutOfRange,
+                                                      m * n * nb * 4, 0);
+            }
+            return;
+        }
+        // the scale is the half of the loaded word at bit 16 * (block index parity)
+        const uint32_t cshift = ((row * (uint32_t)nb + (uint32_t)blk_lane) & 1u) * 16u;
+        const float s0 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(sw0, cshift, 16));
+        const float s1 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(sw1, cshift, 16));
+        const float *cdq = dq_s + blk * M;
+        float p0[M], p1[M];
 #pragma unroll
-        for (int d = 0; d < kRingDepth; ++d) {
+        for (int m = 0; m < M; ++m) {
+            int v0 = is0[m], v1 = is1[m];
+            if (FMT == TB_FMT_SIGN1) {
+                v0 = 2 * v0 - cqs[m];
+                v1 = 2 * v1 - cqs[m];
+            }
+            const float dqv = cdq[m];
+            p0[m] = (s0 * dqv) * (float)v0;
+            p1[m] = kTwo ? (s1 * dqv) * (float)v1 : 0.0f;
+        }
+        row_tree<M, FMT, kTwo>(p0, p1);
+        if (cl == 0) {
+            float *ps = part_s + ((size_t)((tile * I + step) * kRowsPerWave + rl) * M) * kParts;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                ps[kParts * m] = p0[m];
+                if (kTwo)
+                    ps[kParts * m + 1] = p1[m];
+            }
+        }
+    };
+    for (;;) {
+        bool any = false;
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
             // Consume the slot first, then refill it: the refill reuses the slot's
             // registers (no copy at the loop latch, which would wait for every load), and
             // the scheduling barrier keeps consume/refill interleaved slot by slot.
-            int is0[M], is1[M];
-            chunk_sums_step<M, FMT, kTwo>(rb0[d], rb1[d], cact, is0, is1);
-            // the scale is the half of the loaded word at bit cshift (0 or 16)
-            const float s0 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(rs0[d], cshift, 16));
-            const float s1 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(rs1[d], cshift, 16));
-            if (MODE == kModeIsum) {
-                // the export writes every valid block once (even lane of a ternary pair)
-                const bool wr = ctile < NT && crow < n &&
-                                cstep * kChunkLanes + cl < C && (kCpb == 1 || !(cl & 1));
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    const int v = FMT == TB_FMT_SIGN1 ? 2 * is0[m] - cqs[m] : is0[m];
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        (uint32_t)v, rout, wr ? cisum : kOutOfRange, m * n * nb * 4, 0);
-                }
-            } else {
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    int v0 = is0[m], v1 = is1[m];
-                    if (FMT == TB_FMT_SIGN1) {
-                        v0 = 2 * v0 - cqs[m];
-                        v1 = 2 * v1 - cqs[m];
-                    }
-                    const float dqv = cdq[m];
-                    acc0[m] += (s0 * dqv) * (float)v0;
-                    if (kTwo)
-                        acc1[m] += (s1 * dqv) * (float)v1;
-                }
+            if (rit[d] >= 0) {
+                consume(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
+                any = true;
             }
-            issue(rb0[d], rb1[d], rs0[d], rs1[d]);
-            if (++cstep == I) {
-                // end of a row tile: tree, store, reset (wave-uniform branch)
-                if (MODE != kModeIsum) {
-                    row_tree<M, FMT, kTwo>(acc0, acc1);
-                    const bool wr = ctile < NT && cl == 0 && crow < n;
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        buffer_store_f32(rout, wr ? (uint32_t)crow * 4u : kOutOfRange,
-                                         kTwo ? silu_gate(acc0[m], acc1[m]) : acc0[m], m * n * 4);
-                        acc0[m] = 0.0f;
-                        acc1[m] = 0.0f;
-                    }
-                }
-                cstep = 0;
-                ++ctile;
-                crow += GW * kRowsPerWave;
-                cact = lds_lane;
-                cdq = dq_s + blk_lane * M;
-                cqs = qsum_s + blk_lane * M;
-                cisum = ((uint32_t)crow * (uint32_t)nb + (uint32_t)blk_lane) * 4u;
-                cshift = (((uint32_t)crow * (uint32_t)nb + (uint32_t)blk_lane) & 1u) * 16u;
-            } else {
-                cact += L::kStepBytes;
-                cdq += kBlocksPerStep * M;
-                cqs += kBlocksPerStep * M;
-                cisum += kBlocksPerStep * 4u;
-            }
+            issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if (!any)
+            break;
+    }
+    if (MODE == kModeIsum)
+        return;
+
+    // ---- every row: its step partials in step order, from +0 ------------------------
+    __syncthreads();
+    const int ntl = tB - tA;
+    for (int i = tid; i < ntl * kRowsPerWave * M; i += kRingThreads) {
+        const int tl = i / (kRowsPerWave * M), r = (i / M) % kRowsPerWave, m = i % M;
+        const int row = (tA + tl) * kRowsPerWave + r;
+        if (row >= n)
+            continue;
+        const float *ps = part_s + ((size_t)(tl * I * kRowsPerWave + r) * M + m) * kParts;
+        float g = 0.0f, u = 0.0f;
+        for (int s = 0; s < I; ++s) {
+            g += ps[(size_t)s * kRowsPerWave * M * kParts];
+            if (kTwo)
+                u += ps[(size_t)s * kRowsPerWave * M * kParts + 1];
+        }
+        a.out[(size_t)m * n + row] = kTwo ? silu_gate(g, u) : g;
     }
 }
 
@@ -336,11 +380,12 @@ __global__ __launch_bounds__(kSlicedThreads) void gemv_sliced_kernel(GemvArgs a)
     stage_block_terms<M, FMT, false>(dq_s, qsum_s, a.dq, a.q, nb, MODE != kModeIsum, tid,
                                      kSlicedThreads);
 
-    float acc0[M], acc1[M];
+    // the row's sum of step partials (the streaming kernel's fold order)
+    float tot0[M], tot1[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        acc0[m] = 0.0f;
-        acc1[m] = 0.0f;
+        tot0[m] = 0.0f;
+        tot1[m] = 0.0f;
     }
     const uint8_t *rp0 = a.codes0 + (size_t)(row_ok ? row : 0) * row_bytes;
     const uint8_t *rp1 = kTwo ? a.codes1 + (size_t)(row_ok ? row : 0) * row_bytes : nullptr;
@@ -352,7 +397,7 @@ __global__ __launch_bounds__(kSlicedThreads) void gemv_sliced_kernel(GemvArgs a)
         __syncthreads();   // previous slice consumed
         stage_act<M, FMT, false>(act, S, a.q, k, c0, sc, tid, kSlicedThreads);
         __syncthreads();
-        for (int cc = cl; cc < ((sc + 15) & ~15); cc += kChunkLanes) {
+        for (int cc = cl; cc < ((sc + 15) & ~15); cc += kChunkLanes) {   // one step
             const int c = c0 + cc;
             const bool ok = row_ok && cc < sc;
             const int b = c / kCpb;
@@ -362,10 +407,8 @@ __global__ __launch_bounds__(kSlicedThreads) void gemv_sliced_kernel(GemvArgs a)
             const float s1 = (kTwo && ok) ? half_bits_to_float(sp1[b]) : 0.0f;
             int is0[M], is1[M];
             chunk_sums<M, FMT, kTwo>(w0, w1, act, S, ok ? cc : 0, is0, is1);
-            if (!ok)
-                continue;
             if (MODE == kModeIsum) {
-                if (kCpb == 1 || !(cl & 1)) {
+                if (ok && (kCpb == 1 || !(cl & 1))) {
 #pragma unroll
                     for (int m = 0; m < M; ++m)
                         a.isum[((size_t)m * n + row) * nb + b] =
@@ -373,14 +416,32 @@ __global__ __launch_bounds__(kSlicedThreads) void gemv_sliced_kernel(GemvArgs a)
                 }
                 continue;
             }
-            fold_chunk<M, FMT, kTwo>(is0, is1, s0, s1, dq_s, qsum_s, nb, b, acc0, acc1);
+            // the step partial: row tree of the lanes' terms (zero for lanes without a chunk)
+            const int bb = ok ? b : 0;
+            float p0[M], p1[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                int v0 = is0[m], v1 = is1[m];
+                if (FMT == TB_FMT_SIGN1) {
+                    v0 = 2 * v0 - qsum_s[m * nb + bb];
+                    v1 = 2 * v1 - qsum_s[m * nb + bb];
+                }
+                const float dqv = dq_s[m * nb + bb];
+                p0[m] = ok ? (s0 * dqv) * (float)v0 : 0.0f;
+                p1[m] = (kTwo && ok) ? (s1 * dqv) * (float)v1 : 0.0f;
+            }
+            row_tree<M, FMT, kTwo>(p0, p1);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                tot0[m] += p0[m];
+                tot1[m] += p1[m];
+            }
         }
     }
     if (MODE == kModeIsum)
         return;
-    row_tree<M, FMT, kTwo>(acc0, acc1);
     if (cl == 0 && row_ok)
-        store_row<M, MODE>(a, row, acc0, acc1);
+        store_row<M, MODE>(a, row, tot0, tot1);
 }
 
 // ------------------------------------------------------------------------------------
@@ -532,6 +593,8 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     a.scales_bytes = (uint32_t)((scales_bytes(w0) + 3) & ~(size_t)3);
     const int wpc = w0->fmt == TB_FMT_TERNARY2 ? 64 : 128;
     const int C = w0->k / wpc, nb = w0->k / kBlock;
+    const long tiles = (w0->n + kRowsPerWave - 1) / kRowsPerWave;
+    const int ring_grid = (int)(tiles < info.cus ? tiles : info.cus);
     const size_t terms = block_terms_bytes(w0->fmt, m, nb);
 
     // whole activation in LDS: the persistent ring kernel, one workgroup per CU
@@ -539,21 +602,20 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     const size_t step_bytes = (size_t)(w0->fmt == TB_FMT_TERNARY2 ? 1024 : 2048) * m;
     const size_t pad_blocks = (size_t)(kChunkLanes / (w0->fmt == TB_FMT_TERNARY2 ? 2 : 1));
     const size_t ring_terms = (size_t)m * (nb + pad_blocks) * 4 * (w0->fmt == TB_FMT_TERNARY2 ? 1 : 2);
-    const size_t ring_lds = (size_t)steps * step_bytes + ring_terms;
-    // (the sign format's ring kernels need more than 256 registers from m = 6 on: those
-    // shapes take the sliced kernel below)
-    const bool ring_fits_registers = !(w0->fmt == TB_FMT_SIGN1 && m >= 6);
-    if (ring_lds <= (size_t)info.lds_limit && ring_fits_registers) {
+    // item counter, then the step partials of the largest workgroup's items
+    const size_t ring_items = (size_t)((tiles + ring_grid - 1) / ring_grid) * steps;
+    const size_t ring_part = 16 + ring_items * kRowsPerWave * m * (mode == kModeGateUp ? 2 : 1) * 4;
+    const size_t ring_lds = (size_t)steps * step_bytes + ring_terms + ring_part;
+    // (both kernels fold every row in the same order, so the choice never changes a result)
+    if (ring_lds <= (size_t)info.lds_limit) {
         GemvFn fn = gemv_ring_kernel_pick(w0->fmt, mode, m);
         if (!fn)
             return TB_EINVAL;
         if ((rc = set_lds(fn, ring_lds)))
             return rc;
         // one workgroup per CU (fewer only if there are fewer row tiles than CUs)
-        const long tiles = (w0->n + kRowsPerWave - 1) / kRowsPerWave;
-        const int grid = (int)(tiles < info.cus ? tiles : info.cus);
         a.slice_chunks = C;
-        hipLaunchKernelGGL(fn, dim3(grid), dim3(kRingThreads), ring_lds, stream, a);
+        hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(kRingThreads), ring_lds, stream, a);
         return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
     }
     // otherwise stage the activation in slices of S chunks (S a multiple of 16)

@@ -1,12 +1,15 @@
 // tb_device.h -- device building blocks of the ternary-weight int8 FFN kernels (gfx950).
 //
 // Included by tb.hip only. Every block here is shared by all entry points, so that
-// one weight row is computed the same way whichever kernel runs it: the same lane walk
-// over its chunks, the same block fold order and the same reduction tree, for every row
-// count M. The pages state this property for the batched kernel ("perf(bonsai): decode and
-// small packed batches read the FFN from a ternary copy through a dp4a GEMV",
-// sparkinfer PR #1154, commit message): each row's lane walk, per-block fold and shuffle
-// tree are unchanged, so a batched row is bit-identical to its single-row run.
+// one weight row is computed the same way whichever kernel runs it. The fold order of a
+// row is fixed by its shape alone: in step i lane cl holds chunk 16 i + cl; the step's
+// partial is the fixed 16-lane row tree of the lanes' terms (scale * dq) * isum; the row's
+// output is the sum of its step partials in step order, starting from +0. Neither the
+// row count M, nor the kernel, nor which wave ran which step changes it. The pages state
+// the property this gives for the batched kernel ("perf(bonsai): decode and small packed
+// batches read the FFN from a ternary copy through a dp4a GEMV", sparkinfer PR #1154,
+// commit message): each row's lane walk, per-block fold and shuffle tree are unchanged,
+// so a batched row is bit-identical to its single-row run.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,6 +39,14 @@ struct Fmt<TB_FMT_SIGN1> {
     static constexpr int kWeightsPerChunk = 128;  // 16 bytes of sign bits, one block
     static constexpr int kChunksPerBlock = 1;
 };
+
+// First index of part i when n items are split into p near-equal contiguous parts.
+__device__ __forceinline__ int part_lo(int n, int p, int i) { return (int)(((long long)n * i) / p); }
+// The part that holds item t (0 <= t < n): the largest i with part_lo(n, p, i) <= t.
+__device__ __forceinline__ int part_of(int n, int p, int t)
+{
+    return (int)((((long long)t + 1) * p - 1) / n);
+}
 
 __device__ __forceinline__ uint32_t byte_at(uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; }
 
@@ -417,32 +428,48 @@ __device__ __forceinline__ void chunk_sums_step(const uint4 &w0, const uint4 &w1
                 is1[m] = pair_add(is1[m]);
         }
     } else {
+        // Planes are taken one at a time with the next plane's reads in flight: left free,
+        // the scheduler hoists the reads of all 8 planes (32 M registers), which spills
+        // from M = 5 on.
+        uint4 nxt[M];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
+        for (int m = 0; m < M; ++m)
+            nxt[m] = *reinterpret_cast<const uint4 *>(lds + L::offset(0, m));
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t b0[4], b1[4] = {0, 0, 0, 0};
+        for (int p = 0; p < 8; ++p) {
+            const int d = p >> 1, h = p & 1;
+            uint4 cur[M];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    b0[j] = (cw0[d] >> (4 * h + j)) & 0x01010101u;
-                    if (TWO)
-                        b1[j] = (cw1[d] >> (4 * h + j)) & 0x01010101u;
-                }
+            for (int m = 0; m < M; ++m)
+                cur[m] = nxt[m];
+            if (p < 7) {
 #pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    const uint4 av = *reinterpret_cast<const uint4 *>(lds + L::offset(d * 2 + h, m));
-                    is0[m] = dot4(b0[0], av.x, is0[m]);
-                    is0[m] = dot4(b0[1], av.y, is0[m]);
-                    is0[m] = dot4(b0[2], av.z, is0[m]);
-                    is0[m] = dot4(b0[3], av.w, is0[m]);
-                    if (TWO) {
-                        is1[m] = dot4(b1[0], av.x, is1[m]);
-                        is1[m] = dot4(b1[1], av.y, is1[m]);
-                        is1[m] = dot4(b1[2], av.z, is1[m]);
-                        is1[m] = dot4(b1[3], av.w, is1[m]);
-                    }
+                for (int m = 0; m < M; ++m)
+                    nxt[m] = *reinterpret_cast<const uint4 *>(lds + L::offset(p + 1, m));
+            }
+            uint32_t b0[4], b1[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b0[j] = (cw0[d] >> (4 * h + j)) & 0x01010101u;
+                if (TWO)
+                    b1[j] = (cw1[d] >> (4 * h + j)) & 0x01010101u;
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint4 av = cur[m];
+                is0[m] = dot4(b0[0], av.x, is0[m]);
+                is0[m] = dot4(b0[1], av.y, is0[m]);
+                is0[m] = dot4(b0[2], av.z, is0[m]);
+                is0[m] = dot4(b0[3], av.w, is0[m]);
+                if (TWO) {
+                    is1[m] = dot4(b1[0], av.x, is1[m]);
+                    is1[m] = dot4(b1[1], av.y, is1[m]);
+                    is1[m] = dot4(b1[2], av.z, is1[m]);
+                    is1[m] = dot4(b1[3], av.w, is1[m]);
                 }
             }
+            if (M >= 4)
+                __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -638,32 +665,22 @@ __device__ __forceinline__ void chunk_sums(const uint4 &w0, const uint4 &w1, con
     }
 }
 
-// Block fold of one chunk: acc += (scale * dq) * float(isum), once per block.
-// Ternary: both lanes of a block hold the same sums and fold the same term; the tree
-// reads only the even lane. Sign: isum = 2 * dot - sum(q) first.
-template <int M, int FMT, bool TWO>
-__device__ __forceinline__ void fold_chunk(int (&is0)[M], int (&is1)[M], float s0, float s1,
-                                           const float *dq_s, const int *qsum_s, int nb, int b,
-                                           float (&acc0)[M], float (&acc1)[M])
+// Lane i + off of the same 16-lane row (DPP row shift; lanes past the row read 0).
+__device__ __forceinline__ float row_down(float v, int off)
 {
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        if (FMT == TB_FMT_SIGN1) {
-            const int qs = qsum_s[m * nb + b];
-            is0[m] = 2 * is0[m] - qs;
-            if (TWO)
-                is1[m] = 2 * is1[m] - qs;
-        }
-        const float d = dq_s[m * nb + b];
-        acc0[m] += (s0 * d) * (float)is0[m];
-        if (TWO)
-            acc1[m] += (s1 * d) * (float)is1[m];
+    int r;
+    switch (off) {
+    case 1: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x102, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x108, 0xF, 0xF, false); break;
     }
+    return __int_as_float(r);
 }
 
-// Fixed shuffle tree over the 16 lanes of a row; lane 0 of the row ends with the total:
+// Fixed tree over the 16 lanes of a row; lane 0 of the row ends with the total:
 // ((a0 + a2) + (a4 + a6)) + ((a8 + a10) + (a12 + a14)) for ternary (odd lanes hold
-// copies), or the same over all 16 lanes for sign.
+// copies), or the same over all 16 lanes for sign. DPP row shifts: no LDS traffic.
 template <int M, int FMT, bool TWO>
 __device__ __forceinline__ void row_tree(float (&acc0)[M], float (&acc1)[M])
 {
@@ -671,9 +688,9 @@ __device__ __forceinline__ void row_tree(float (&acc0)[M], float (&acc1)[M])
     for (int off = FMT == TB_FMT_TERNARY2 ? 2 : 1; off < kChunkLanes; off <<= 1) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            acc0[m] += __shfl_down(acc0[m], off, kChunkLanes);
+            acc0[m] += row_down(acc0[m], off);
             if (TWO)
-                acc1[m] += __shfl_down(acc1[m], off, kChunkLanes);
+                acc1[m] += row_down(acc1[m], off);
         }
     }
 }

@@ -446,6 +446,8 @@ __global__ __launch_bounds__(kLrThreads) void ffn_layers_lr_kernel(FusedArgs a, 
                     chunk_sums_step<M, FMT, true>(it.w0, it.w1, cact, is0, is1);
                 const float s0 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(it.s0, cshift, 16));
                 const float s1 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(it.s1, cshift, 16));
+                // the step partial: row tree of the lanes' terms, added in step order
+                float p0[M], p1[M];
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     int v0 = is0[m], v1 = is1[m];
@@ -454,11 +456,16 @@ __global__ __launch_bounds__(kLrThreads) void ffn_layers_lr_kernel(FusedArgs a, 
                         v1 = 2 * v1 - qs_s[cblk * M + m];
                     }
                     const float dqv = dq_s[cblk * M + m];
-                    acc0[m] += (s0 * dqv) * (float)v0;
-                    acc1[m] += (s1 * dqv) * (float)v1;
+                    p0[m] = (s0 * dqv) * (float)v0;
+                    p1[m] = (s1 * dqv) * (float)v1;
+                }
+                row_tree<M, FMT, true>(p0, p1);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    acc0[m] += p0[m];
+                    acc1[m] += p1[m];
                 }
                 if (++cstep == I0) {
-                    row_tree<M, FMT, true>(acc0, acc1);
                     const bool wr = cl == 0;
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
@@ -565,15 +572,21 @@ __global__ __launch_bounds__(kLrThreads) void ffn_layers_lr_kernel(FusedArgs a, 
                 else
                     chunk_sums_step<M, FMT, false>(it.w0, it.w0, cact, is0, is1);
                 const float s0 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(it.s0, cshift, 16));
+                // the step partial: row tree of the lanes' terms, added in step order
+                float p0[M], p1[M];
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     int v0 = is0[m];
                     if (FMT == TB_FMT_SIGN1)
                         v0 = 2 * v0 - qs_s[cblk * M + m];
-                    acc0[m] += (s0 * dq_s[cblk * M + m]) * (float)v0;
+                    p0[m] = (s0 * dq_s[cblk * M + m]) * (float)v0;
+                    p1[m] = 0.0f;
                 }
+                row_tree<M, FMT, false>(p0, p1);
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    acc0[m] += p0[m];
                 if (++cstep == I1) {
-                    row_tree<M, FMT, false>(acc0, acc1);
                     const bool wr = cl == 0;
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
