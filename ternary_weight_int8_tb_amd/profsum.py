@@ -1,0 +1,185 @@
+"""Summaries of rocprofv3 output for profiles/: kernel statistics and calibrated HBM traffic.
+
+    python -m ternary_weight_int8_tb_amd.profsum --stats DIR --pmc DIR --bench FILE --out profiles
+
+--stats: the directory of a `rocprofv3 --kernel-trace --stats --output-format csv -o bench`
+run of bench.py; --pmc: the parent directory of the four counter runs pmc_FETCH_SIZE,
+pmc_WRITE_SIZE (bench.py --profile-only) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE
+(bench.py --copy-probe-mib 1024); --bench: bench.py's stdout (the JSON line) from the same
+box. Writes ffn64_stream_kernel_stats.md, ffn64_stream_traffic.md and
+ffn64_stream_traffic.json. The traffic file carries a sha256 of the kernel sources, and
+bench.py reports the traffic figure only while the sources still hash to it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SOURCES = ["ternary_weight_int8_tb_amd/csrc/tb.hip", "ternary_weight_int8_tb_amd/csrc/tb_device.h",
+           "ternary_weight_int8_tb_amd/csrc/tb_fused.h", "ternary_weight_int8_tb_amd/csrc/tb_fused_lr.h"]
+COPY_BYTES = 1 << 30
+
+HIDDEN, INTER, LAYERS = 5120, 17408, 64
+NB_H, NB_N = HIDDEN // 128, INTER // 128
+MATRIX_BYTES = INTER * HIDDEN // 4 + INTER * NB_H * 2   # codes + fp16 scales, ternary
+
+
+def source_sha256() -> str:
+    h = hashlib.sha256()
+    for f in SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str:
+    """'void (anonymous namespace)::gemv_ring_kernel<1, 0, 1>(GemvArgs)' -> 'gemv_ring_kernel<1, 0, 1>'."""
+    m = re.search(r"(\w+_kernel)(<[^>]*>)?", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name
+
+
+# Algorithmic bytes per launch at M=1 (weights + activations read + outputs written).
+ALGORITHMIC = {
+    "gemv_ring_kernel<1, 0, 1>": 2 * MATRIX_BYTES + HIDDEN + NB_H * 4 + INTER * 4,
+    "gemv_ring_kernel<1, 0, 0>": MATRIX_BYTES + INTER + NB_N * 4 + HIDDEN * 4,
+    "ffn_layers_kernel<1, 0>": 32 * (3 * MATRIX_BYTES + 2 * HIDDEN * 4),
+}
+WHAT = {
+    "gemv_ring_kernel<1, 0, 1>": "tb_ffn_gateup_silu at M=1 (gate and up, 47,349,760 weight bytes)",
+    "gemv_ring_kernel<1, 0, 0>": "the GEMV of tb_ffn_down at M=1 (23,674,880 weight bytes)",
+    "ffn_layers_kernel<1, 0>": "one tb_ffn_layers launch of 32 layers at M=1",
+}
+
+
+def read_stats(d: str):
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = []
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            rows.append({"name": r["Name"], "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                         "max_us": float(r["MaxNs"]) / 1e3, "pct": float(r["Percentage"])})
+    rows.sort(key=lambda r: -r["pct"])
+    return rows
+
+
+def read_counter(d: str, counter: str):
+    """Per kernel (short name): list of the counter's value per dispatch (KiB)."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return per
+
+
+def copy_factor(d: str, counter: str, true_bytes: int) -> float:
+    """Counter bytes over true bytes for the largest dispatches of the copy probe."""
+    per = read_counter(d, counter)
+    best = max(((sum(v) / len(v), k) for k, v in per.items()), key=lambda t: t[0])
+    return best[0] * 1024 / true_bytes
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--stats", required=True)
+    p.add_argument("--pmc", required=True)
+    p.add_argument("--bench", required=True)
+    p.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    a = p.parse_args()
+
+    bench = None
+    with open(a.bench) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith("{"):
+                bench = json.loads(line)
+    stats = read_stats(a.stats)
+
+    cmd_stats = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+                 "-d <out>/prof -o bench -- python3 /root/repo/bench.py")
+    lines = ["# FFN 64-layer weight stream (hidden 5120, intermediate 17408): kernel statistics",
+             "", "Command (on the GPU box; /root/repo is the repository):", "", "```", cmd_stats, "```",
+             "", "Kernel statistics (all dispatches of the run: both paths, M=1 and M=8, ternary and sign):",
+             "", "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in stats[:16]:
+        lines.append(f"| `{r['name']}` | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | "
+                     f"{r['max_us']:.2f} | {r['pct']:.1f} |")
+    lines += ["", "Template arguments: gemv_ring_kernel<M, FMT, MODE>, FMT 0 = ternary, 1 = sign; "
+              "MODE 0 = single GEMV (down), 1 = gate/up + SiLU, 2 = block-sum export. "
+              "ffn_layers_kernel<M, FMT> is one tb_ffn_layers launch of up to 32 whole layers. "
+              "stream_read_kernel is the 4 GiB read probe."]
+    if bench:
+        keep = {k: bench.get(k) for k in ("value", "unit", "ms_per_step", "us_per_layer", "pct_hbm_peak",
+                                           "read_probe_gbs")}
+        keep["entry_point"] = bench.get("config", {}).get("entry_point")
+        lines += ["", "Bench line of a run on the same box (headline fields and roofline):", "", "```",
+                  json.dumps(keep), json.dumps(bench.get("roofline")), "```"]
+    os.makedirs(a.out, exist_ok=True)
+    with open(os.path.join(a.out, "ffn64_stream_kernel_stats.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    ff = copy_factor(os.path.join(a.pmc, "pmc_copy_FETCH_SIZE"), "FETCH_SIZE", COPY_BYTES)
+    wf = copy_factor(os.path.join(a.pmc, "pmc_copy_WRITE_SIZE"), "WRITE_SIZE", COPY_BYTES)
+    fetch = read_counter(os.path.join(a.pmc, "pmc_FETCH_SIZE"), "FETCH_SIZE")
+    write = read_counter(os.path.join(a.pmc, "pmc_WRITE_SIZE"), "WRITE_SIZE")
+    doc = {"source_sha256": source_sha256(), "source_files": SOURCES,
+           "calibration": {"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "kernels": {}}
+    rows = []
+    for key, alg in ALGORITHMIC.items():
+        if key not in fetch or key not in write:
+            continue
+        fk = sum(fetch[key]) / len(fetch[key])
+        wk = sum(write[key]) / len(write[key])
+        fb = int(fk * 1024 / ff)
+        wb = int(wk * 1024 / wf)
+        doc["kernels"][key] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                               "traffic_bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": alg,
+                               "traffic_over_algorithmic": round((fb + wb) / alg, 4),
+                               "fetch_raw_kib": round(fk, 1), "write_raw_kib": round(wk, 1),
+                               "dispatches": len(fetch[key])}
+        rows.append(f"| `{key}` | {fk:.1f} | {wk:.1f} | {fb} | {wb} | {alg} | {(fb + wb) / alg:.4f} |")
+    with open(os.path.join(a.out, "ffn64_stream_traffic.json"), "w") as fh:
+        json.dump(doc, fh, indent=1)
+        fh.write("\n")
+    cmds = []
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmds.append(f"rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_{c} -o run -- "
+                    "python3 /root/repo/bench.py --profile-only")
+        cmds.append(f"rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_copy_{c} -o run -- "
+                    "python3 /root/repo/bench.py --copy-probe-mib 1024")
+    md = ["# HBM traffic per launch: 64-layer FFN stream at M=1 (hidden 5120, intermediate 17408)", "",
+          "Commands (on the GPU box, from /tmp with TMPDIR=/tmp; one counter per run; the copy runs "
+          "calibrate the counters):", "", "```", *cmds, "```", "",
+          f"Calibration: a device copy of 1 GiB (reads 1 GiB, writes 1 GiB) reads FETCH_SIZE x{ff:.4f} "
+          f"and WRITE_SIZE x{wf:.4f} of its true bytes; the factors below scale the counters.", "",
+          "| kernel | FETCH raw KiB | WRITE raw KiB | fetched B (scaled) | written B | algorithmic B | "
+          "traffic / algorithmic |", "|---|---|---|---|---|---|---|", *rows, ""]
+    for key in doc["kernels"]:
+        md.append(f"- `{key}`: {WHAT[key]}.")
+    md += ["", "Algorithmic bytes: weights + activations read + outputs written. Per-dispatch averages "
+           "over every dispatch of the kernel in the run.", "",
+           f"Kernel sources hashed (sha256 over {', '.join(SOURCES)}): `{doc['source_sha256']}`. "
+           "bench.py reports these bytes as `roofline.traffic` only while the sources hash to this value."]
+    with open(os.path.join(a.out, "ffn64_stream_traffic.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print(f"wrote {a.out}/ffn64_stream_kernel_stats.md, ffn64_stream_traffic.md/.json")
+
+
+if __name__ == "__main__":
+    main()
