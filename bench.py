@@ -223,7 +223,10 @@ def measured_traffic(kernel_key: str):
     doc = json.load(open(path))
     h = hashlib.sha256()
     for f in doc["source_files"]:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+        path_f = os.path.join(ROOT, f)
+        if not os.path.exists(path_f):
+            return None
+        with open(path_f, "rb") as fh:
             h.update(fh.read())
     if h.hexdigest() != doc["source_sha256"] or kernel_key not in doc["kernels"]:
         return None

@@ -150,10 +150,13 @@ int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum
  *            TB_FFN_CHAIN float [m][hidden]: layer l+1 then takes layer l's y.
  *   y        float [num_layers][m][hidden] outputs.
  *   ws       device workspace of at least tb_ffn_workspace_bytes(m, hidden,
- *            inter) bytes, 16-byte aligned, initialised once with
- *            tb_ffn_workspace_init before its first use. It holds h, rotquant(h)
- *            and the synchronisation words; every call leaves it ready for the
- *            next. Calls that share a workspace must not overlap in time.
+ *            inter) bytes, 16-byte aligned, initialised with
+ *            tb_ffn_workspace_init before its first use and again whenever m,
+ *            hidden or inter change. It holds the data exchanged between
+ *            workgroups (h, rotquant(h) and y, each value stored with a tag
+ *            naming its launch and layer) and the synchronisation words; every
+ *            call leaves it ready for the next. Calls that share a workspace
+ *            must not overlap in time.
  * Synchronisation between workgroups waits a bounded time (the spin limit of
  * tb_ffn_workspace_init; 0 selects 100 ms). If a wait runs out, for instance
  * because other work occupies compute units so that not all workgroups can

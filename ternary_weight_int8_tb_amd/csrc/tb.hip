@@ -34,8 +34,7 @@
 
 #include "tb.h"
 #include "tb_device.h"
-#include "tb_fused.h"
-#include "tb_fused_lr.h"
+#include "tb_layers.h"
 
 namespace {
 
@@ -642,104 +641,43 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
 // ------------------------------------------------------------------------------------
 // Fused FFN layers
 // ------------------------------------------------------------------------------------
-using FusedFn = void (*)(FusedArgs);
+using LayersFn = void (*)(tbl::LArgs);
 
 template <int FMT>
-FusedFn fused_pick_m(int m)
+LayersFn layers_pick_m(int m)
 {
     switch (m) {
-    case 1: return ffn_layers_kernel<1, FMT>;
-    case 2: return ffn_layers_kernel<2, FMT>;
-    case 3: return ffn_layers_kernel<3, FMT>;
-    case 4: return ffn_layers_kernel<4, FMT>;
-    case 5: return ffn_layers_kernel<5, FMT>;
-    case 6: return ffn_layers_kernel<6, FMT>;
-    case 7: return ffn_layers_kernel<7, FMT>;
-    case 8: return ffn_layers_kernel<8, FMT>;
-    default: return nullptr;
-    }
-}
-
-using FusedLrFn = void (*)(FusedArgs, int);
-
-// The sign format's gate/up decode needs more than the 128 registers a 16-wave workgroup
-// allows from m = 2 on: those shapes run the register-ring kernel (not instantiated here).
-template <int M, int FMT>
-FusedLrFn fused_lr_entry()
-{
-    if constexpr (FMT == TB_FMT_SIGN1 && M > 1)
-        return nullptr;
-    else
-        return ffn_layers_lr_kernel<M, FMT>;
-}
-
-template <int FMT>
-FusedLrFn fused_lr_pick_m(int m)
-{
-    switch (m) {
-    case 1: return fused_lr_entry<1, FMT>();
-    case 2: return fused_lr_entry<2, FMT>();
-    case 3: return fused_lr_entry<3, FMT>();
-    case 4: return fused_lr_entry<4, FMT>();
-    case 5: return fused_lr_entry<5, FMT>();
-    case 6: return fused_lr_entry<6, FMT>();
+    case 1: return tbl::ffn_layers_kernel<1, FMT>;
+    case 2: return tbl::ffn_layers_kernel<2, FMT>;
+    case 3: return tbl::ffn_layers_kernel<3, FMT>;
+    case 4: return tbl::ffn_layers_kernel<4, FMT>;
+    case 5: return tbl::ffn_layers_kernel<5, FMT>;
+    case 6: return tbl::ffn_layers_kernel<6, FMT>;
+    case 7: return tbl::ffn_layers_kernel<7, FMT>;
+    case 8: return tbl::ffn_layers_kernel<8, FMT>;
     default: return nullptr;
     }
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Workspace: sync words, then the tagged arrays (8-byte entries).
 struct WsLayout {
-    size_t sync, h, qh, dqh, qsumh, total;
+    size_t sync, hp, qp, dp, sp, yp, total;
 };
 
-WsLayout ws_layout(int m, int inter)
+WsLayout ws_layout(int m, int hidden, int inter)
 {
     WsLayout w;
     const size_t nbi = (size_t)inter / kBlock;
     w.sync = 0;
-    w.h = align256((size_t)kSyncWords * 4);
-    w.qh = align256(w.h + (size_t)m * inter * 4);
-    w.dqh = align256(w.qh + (size_t)m * inter);
-    w.qsumh = align256(w.dqh + (size_t)m * nbi * 4);
-    w.total = align256(w.qsumh + (size_t)m * nbi * 4);
+    w.hp = align256((size_t)tbl::kSyncWords * 4);
+    w.qp = align256(w.hp + (size_t)m * inter * 8);
+    w.dp = align256(w.qp + (size_t)m * inter / 4 * 8);
+    w.sp = align256(w.dp + (size_t)m * nbi * 8);
+    w.yp = align256(w.sp + (size_t)m * nbi * 8);
+    w.total = align256(w.yp + (size_t)m * hidden * 8);
     return w;
-}
-
-// Activation and block-term bytes of the fused kernels' LDS (must match their carve-up).
-void fused_lds_parts(int fmt, int m, int hidden, int inter, size_t *act, size_t *nbmax)
-{
-    const int wpc = fmt == TB_FMT_TERNARY2 ? 64 : 128;
-    const int step = (fmt == TB_FMT_TERNARY2 ? 1024 : 2048) * m;
-    const int I0 = (hidden / wpc + kChunkLanes - 1) / kChunkLanes;
-    const int I1 = (inter / wpc + kChunkLanes - 1) / kChunkLanes;
-    *act = std::max((size_t)I1 * step, (size_t)I0 * step + (size_t)m * hidden);
-    const int bps = kChunkLanes / (fmt == TB_FMT_TERNARY2 ? 2 : 1);
-    *nbmax = (size_t)std::max(hidden, inter) / kBlock + bps;
-}
-
-// Loader-wave kernel: ring units per consumer that fit in `limit` bytes of LDS (0 if
-// fewer than kMinRingUnits), and the LDS bytes it then uses.
-int fused_lr_units(int fmt, int m, int hidden, int inter, size_t limit, size_t *lds)
-{
-    size_t act, nbmax;
-    fused_lds_parts(fmt, m, hidden, inter, &act, &nbmax);
-    const size_t off = (size_t)lr_ring_offset((int)act, (int)nbmax, m);
-    if (off >= limit)
-        return 0;
-    const int u = (int)std::min<size_t>(kMaxRingUnits, (limit - off) / ((size_t)kLrConsumers * kUnitBytes));
-    if (u < kMinRingUnits)
-        return 0;
-    *lds = off + (size_t)u * kLrConsumers * kUnitBytes;
-    return u;
-}
-
-// LDS bytes of the register-ring fused kernel (must match ffn_layers_kernel's carve-up).
-size_t fused_lds_bytes(int fmt, int m, int hidden, int inter)
-{
-    size_t act, nbmax;
-    fused_lds_parts(fmt, m, hidden, inter, &act, &nbmax);
-    return act + 2 * nbmax * m * 4 + 16;
 }
 
 int check_ffn_shapes(const tb_ffn_weights *L, int n, int *hidden, int *inter, int *fmt)
@@ -893,20 +831,21 @@ int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum
 
 size_t tb_ffn_workspace_bytes(int m, int hidden, int inter)
 {
-    (void)hidden;
-    if (check_rows(m) || inter < kBlock || inter % kBlock)
+    if (check_rows(m) || inter < kBlock || inter % kBlock || hidden < kBlock || hidden % kBlock)
         return 0;
-    return ws_layout(m, inter).total;
+    return ws_layout(m, hidden, inter).total;
 }
 
 int tb_ffn_workspace_init(void *ws, size_t ws_bytes, uint32_t spin_ticks, void *stream)
 {
-    if (!ws || ws_bytes < (size_t)kSyncWords * 4)
+    if (!ws || ws_bytes < (size_t)tbl::kSyncWords * 4)
         return TB_EINVAL;
     if (!aligned16(ws))
         return TB_EALIGN;
-    hipLaunchKernelGGL(ffn_workspace_init_kernel, dim3(1), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<uint32_t *>(ws), spin_ticks);
+    const size_t words = ws_bytes / 4;
+    const int grid = (int)std::min<size_t>(1024, (words + 1023) / 1024);
+    hipLaunchKernelGGL(tbl::layers_ws_init_kernel, dim3(grid), dim3(1024), 0,
+                       static_cast<hipStream_t>(stream), static_cast<uint32_t *>(ws), words, spin_ticks);
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
@@ -915,7 +854,7 @@ int tb_ffn_workspace_error(const void *ws, int *error)
     if (!ws || !error)
         return TB_EINVAL;
     uint32_t v = 0;
-    if (hipMemcpy(&v, static_cast<const uint32_t *>(ws) + kSyncError, 4, hipMemcpyDeviceToHost) !=
+    if (hipMemcpy(&v, static_cast<const uint32_t *>(ws) + tbl::kWErr, 4, hipMemcpyDeviceToHost) !=
         hipSuccess)
         return TB_EHIP;
     *error = (int)v;
@@ -933,7 +872,7 @@ int tb_ffn_layers(const tb_ffn_weights *layers, int num_layers, const float *x, 
         return rc;
     if (!aligned16(x) || !aligned16(y) || !aligned16(ws))
         return TB_EALIGN;
-    const WsLayout wl = ws_layout(m, N);
+    const WsLayout wl = ws_layout(m, H, N);
     if (ws_bytes < wl.total)
         return TB_EINVAL;
     const bool chain = (flags & TB_FFN_CHAIN) != 0;
@@ -950,50 +889,50 @@ int tb_ffn_layers(const tb_ffn_weights *layers, int num_layers, const float *x, 
                 overlaps(rw, range_of(w->scales, scales_bytes(w))))
                 return TB_EINVAL;
     }
+    // tagged entries are addressed with 32-bit buffer offsets
+    if (wl.total >= ((size_t)1 << 31))
+        return TB_EUNSUPPORTED;
     DeviceInfo info;
     if ((rc = device_info(&info)))
         return rc;
-    // the loader-wave kernel when its LDS rings fit (small m), else the register-ring one
-    size_t lds = 0;
-    const int units = fused_lr_units(F, m, H, N, (size_t)info.lds_limit, &lds);
-    FusedLrFn lr_fn = nullptr;
-    FusedFn fn = nullptr;
-    if (units > 0)
-        lr_fn = F == TB_FMT_TERNARY2 ? fused_lr_pick_m<TB_FMT_TERNARY2>(m)
-                                     : fused_lr_pick_m<TB_FMT_SIGN1>(m);
-    if (!lr_fn) {
-        lds = fused_lds_bytes(F, m, H, N);
-        if (lds > (size_t)info.lds_limit)
-            return TB_EUNSUPPORTED;
-        fn = F == TB_FMT_TERNARY2 ? fused_pick_m<TB_FMT_TERNARY2>(m) : fused_pick_m<TB_FMT_SIGN1>(m);
-        if (!fn)
-            return TB_EINVAL;
-    }
-    const void *kern = lr_fn ? reinterpret_cast<const void *>(lr_fn) : reinterpret_cast<const void *>(fn);
-    if (lds > 65536 &&
-        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    // one workgroup per CU, all resident at once
+    const int G = info.cus;
+    const tbl::LdsPlan plan = tbl::lds_plan(m, F, H, N, G);
+    if (plan.total > info.lds_limit)
+        return TB_EUNSUPPORTED;
+    // item tags: tile < 2^13 and step < 2^10 per CU
+    if ((N / kRowsPerWave + G - 1) / G >= (1 << 13) || (H / kRowsPerWave + G - 1) / G >= (1 << 13) ||
+        N / (F == TB_FMT_TERNARY2 ? 64 : 128) / 16 >= (1 << 10))
+        return TB_EUNSUPPORTED;
+    LayersFn fn = F == TB_FMT_TERNARY2 ? layers_pick_m<TB_FMT_TERNARY2>(m) : layers_pick_m<TB_FMT_SIGN1>(m);
+    if (!fn)
+        return TB_EINVAL;
+    if (plan.total > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            plan.total) != hipSuccess)
         return TB_EHIP;
 
     uint8_t *wsb = static_cast<uint8_t *>(ws);
-    FusedArgs a;
-    a.hidden = H;
-    a.inter = N;
+    tbl::LArgs a;
+    a.H = H;
+    a.N = N;
     a.sync = reinterpret_cast<uint32_t *>(wsb + wl.sync);
-    a.h = reinterpret_cast<float *>(wsb + wl.h);
-    a.qh = reinterpret_cast<int8_t *>(wsb + wl.qh);
-    a.dqh = reinterpret_cast<float *>(wsb + wl.dqh);
-    a.qsumh = reinterpret_cast<int *>(wsb + wl.qsumh);
-    a.gu_codes_bytes = (uint32_t)codes_bytes(&layers[0].gate);
-    a.gu_scales_bytes = (uint32_t)((scales_bytes(&layers[0].gate) + 3) & ~(size_t)3);
-    a.d_codes_bytes = (uint32_t)codes_bytes(&layers[0].down);
-    a.d_scales_bytes = (uint32_t)((scales_bytes(&layers[0].down) + 3) & ~(size_t)3);
+    a.hp = reinterpret_cast<uint64_t *>(wsb + wl.hp);
+    a.qp = reinterpret_cast<uint64_t *>(wsb + wl.qp);
+    a.dp = reinterpret_cast<uint64_t *>(wsb + wl.dp);
+    a.sp = reinterpret_cast<uint64_t *>(wsb + wl.sp);
+    a.yp = reinterpret_cast<uint64_t *>(wsb + wl.yp);
+    a.gu_cb = (uint32_t)codes_bytes(&layers[0].gate);
+    a.gu_sb = (uint32_t)((scales_bytes(&layers[0].gate) + 3) & ~(size_t)3);
+    a.d_cb = (uint32_t)codes_bytes(&layers[0].down);
+    a.d_sb = (uint32_t)((scales_bytes(&layers[0].down) + 3) & ~(size_t)3);
     a.unit = dq_unit();
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // at most kMaxFusedLayers per launch; a chained sequence continues from the last y
-    for (int start = 0; start < num_layers; start += kMaxFusedLayers) {
-        const int cnt = std::min(kMaxFusedLayers, num_layers - start);
+    // at most kMaxLayers per launch; a chained sequence continues from the last y
+    for (int start = 0; start < num_layers; start += tbl::kMaxLayers) {
+        const int cnt = std::min(tbl::kMaxLayers, num_layers - start);
         a.L = cnt;
-        for (int i = 0; i < kMaxFusedLayers; ++i) {
+        for (int i = 0; i < tbl::kMaxLayers; ++i) {
             const tb_ffn_weights &w = layers[start + (i < cnt ? i : 0)];
             a.layer[i].codes[0] = static_cast<const uint8_t *>(w.gate.codes);
             a.layer[i].codes[1] = static_cast<const uint8_t *>(w.up.codes);
@@ -1005,10 +944,7 @@ int tb_ffn_layers(const tb_ffn_weights *layers, int num_layers, const float *x, 
         a.chain = chain ? 1 : 0;
         a.x = chain ? (start == 0 ? x : y + (size_t)(start - 1) * m * H) : x + (size_t)start * m * H;
         a.y = y + (size_t)start * m * H;
-        if (lr_fn)
-            hipLaunchKernelGGL(lr_fn, dim3(info.cus), dim3(kLrThreads), lds, s, a, units);
-        else
-            hipLaunchKernelGGL(fn, dim3(info.cus), dim3(kFusedThreads), lds, s, a);
+        hipLaunchKernelGGL(fn, dim3(G), dim3(tbl::kThreads), plan.total, s, a);
         if (hipGetLastError() != hipSuccess)
             return TB_EHIP;
     }

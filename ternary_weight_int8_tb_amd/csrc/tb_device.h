@@ -385,6 +385,59 @@ __device__ __forceinline__ void stage_unit_store_step(const StageUnit<FMT> &u, u
     }
 }
 
+// One rotated-quantised block into the step-major layout. The 16-lane group holds block b
+// of row m; lane L has codes 8L .. 8L+7 packed little-endian in pk[0], pk[1] (the
+// registers rotquant_regs returns). Lanes exchange codes so that each writes 8 bytes of
+// the layout that stage_unit_store_step writes from global memory.
+template <int M, int FMT>
+__device__ __forceinline__ void store_block_step(uint8_t *act, int m, int b, int lane16,
+                                                 const uint32_t (&pk)[2])
+{
+    using L = StepLayout<M, FMT>;
+    uint32_t o[2];
+    int c, plane, half;
+    if (FMT == TB_FMT_TERNARY2) {
+        // 16-code group g = lane16 / 2 is code word g % 4 of chunk 2b + g / 4; its even lane
+        // has codes 0..7, the odd lane 8..15. Word e of the group is codes {e, e+4, e+8,
+        // e+12}; the even lane writes words 0, 1, the odd lane words 2, 3.
+        const uint32_t q0 = __shfl_xor(pk[0], 1, 16), q1 = __shfl_xor(pk[1], 1, 16);
+        const bool odd = lane16 & 1;
+        const uint32_t lo0 = odd ? q0 : pk[0], lo1 = odd ? q1 : pk[1];
+        const uint32_t hi0 = odd ? pk[0] : q0, hi1 = odd ? pk[1] : q1;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int e = (odd ? 2 : 0) + t;
+            o[t] = byte_at(lo0, e) | byte_at(lo1, e) << 8 | byte_at(hi0, e) << 16 | byte_at(hi1, e) << 24;
+        }
+        const int g = lane16 >> 1;
+        c = 2 * b + (g >> 2);
+        plane = g & 3;
+        half = lane16 & 1;
+    } else {
+        // 32-code unit u = lane16 / 4: lane i = lane16 % 4 of it has codes 8i .. 8i+7. Word w
+        // (0..7) of the unit is codes {w, w+8, w+16, w+24}: words 0..3 go to plane 2u,
+        // words 4..7 to plane 2u + 1. Lane i writes words 2i, 2i + 1.
+        const int i = lane16 & 3, base = lane16 & ~3;
+        uint32_t src[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t w0 = __shfl(pk[0], base + t, 16), w1 = __shfl(pk[1], base + t, 16);
+            src[t] = (i >> 1) ? w1 : w0;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int e = (2 * i + t) & 3;
+            o[t] = byte_at(src[0], e) | byte_at(src[1], e) << 8 | byte_at(src[2], e) << 16 |
+                   byte_at(src[3], e) << 24;
+        }
+        c = b;
+        plane = 2 * (lane16 >> 2) + (i >> 1);
+        half = i & 1;
+    }
+    *reinterpret_cast<uint2 *>(act + (size_t)(c >> 4) * L::kStepBytes + (c & 15) * 16 +
+                               L::offset(plane, m) + half * 8) = make_uint2(o[0], o[1]);
+}
+
 // Integer sums of one chunk against all M rows, step-major layout; `lds` is this lane's
 // slot address in the current step. Same arithmetic as chunk_sums.
 template <int M, int FMT, bool TWO>

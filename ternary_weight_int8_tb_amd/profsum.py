@@ -23,7 +23,7 @@ import re
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = ["ternary_weight_int8_tb_amd/csrc/tb.hip", "ternary_weight_int8_tb_amd/csrc/tb_device.h",
-           "ternary_weight_int8_tb_amd/csrc/tb_fused.h", "ternary_weight_int8_tb_amd/csrc/tb_fused_lr.h"]
+           "ternary_weight_int8_tb_amd/csrc/tb_layers.h"]
 COPY_BYTES = 1 << 30
 
 HIDDEN, INTER, LAYERS = 5120, 17408, 64
