@@ -108,6 +108,25 @@ def test_block_sums_and_gemv(o, fmt, n, k, m):
     assert ok
 
 
+@pytest.mark.parametrize("fmt", [TERN, SIGN])
+def test_sliced_and_streaming_kernels_fold_alike(o, fmt):
+    # k = 24576: at M=8 the activation does not fit in LDS, so the sliced kernel runs; the
+    # row alone (M=1) runs on the streaming kernel. Both fold every row in the same order,
+    # so the batched rows must equal the rows alone bit for bit.
+    n, k = 96, 24576
+    say(f"sliced vs streaming fmt={fmt} n={n} k={k}")
+    w = synth.matrix(fmt, n, k, 11, 0, synth.T_GATE)
+    x = synth.normal_rows(8, k, 11, 0)
+    q, dq = o.rotate_quant(x)
+    wd = tb.Matrix.upload(w)
+    y8 = gu.gemv(wd, q, dq)
+    yo, sabs = o.gemv(w, q, dq)
+    assert bounds.gemv_ok(y8, yo, sabs)[0]
+    for r in range(8):
+        y1 = gu.gemv(wd, q[r:r + 1], dq[r:r + 1])
+        assert y1[0].tobytes() == y8[r].tobytes(), r
+
+
 def test_code3_and_zero_cases(o):
     rng = np.random.default_rng(5)
     codes = rng.integers(0, 4, (130, 384)).astype(np.uint8)     # includes the unused code 3
