@@ -718,22 +718,24 @@ __device__ __forceinline__ void chunk_sums(const uint4 &w0, const uint4 &w1, con
     }
 }
 
-// Lane i + off of the same 16-lane row (DPP row shift; lanes past the row read 0).
+// Lane (i + off) mod 16 of the same 16-lane row (DPP row rotate). Lane 0 of a row, the
+// only lane whose tree result is used, reads lane off; a rotate has no out-of-row lanes,
+// so the compiler folds it into the add (v_add_f32_dpp) at every level.
 __device__ __forceinline__ float row_down(float v, int off)
 {
     int r;
     switch (off) {
-    case 1: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xF, 0xF, false); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x102, 0xF, 0xF, false); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xF, 0xF, false); break;
-    default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x108, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false); break;
     }
     return __int_as_float(r);
 }
 
 // Fixed tree over the 16 lanes of a row; lane 0 of the row ends with the total:
 // ((a0 + a2) + (a4 + a6)) + ((a8 + a10) + (a12 + a14)) for ternary (odd lanes hold
-// copies), or the same over all 16 lanes for sign. DPP row shifts: no LDS traffic.
+// copies), or the same over all 16 lanes for sign. DPP row rotates: no LDS traffic.
 template <int M, int FMT, bool TWO>
 __device__ __forceinline__ void row_tree(float (&acc0)[M], float (&acc1)[M])
 {
@@ -745,6 +747,14 @@ __device__ __forceinline__ void row_tree(float (&acc0)[M], float (&acc1)[M])
             if (TWO)
                 acc1[m] += row_down(acc1[m], off);
         }
+    }
+    // Keep the last level here: callers use the totals in lane 0 only, and an add sunk
+    // into that branch could no longer take its DPP operand directly.
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        asm volatile("" : "+v"(acc0[m]));
+        if (TWO)
+            asm volatile("" : "+v"(acc1[m]));
     }
 }
 
