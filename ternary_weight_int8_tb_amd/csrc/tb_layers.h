@@ -41,8 +41,11 @@ using namespace tbk;
 
 constexpr int kWaves = 16;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kDepthTern = 3;        // ring items per wave (ternary; the sign decode needs
-constexpr int kDepthSign = 2;        // more registers)
+#ifndef TBL_DEPTH_TERN
+#define TBL_DEPTH_TERN 2
+#endif
+constexpr int kDepthTern = TBL_DEPTH_TERN;   // ring items per wave (ternary; the sign decode
+constexpr int kDepthSign = 2;                // needs more registers)
 constexpr int kMaxLayers = 32;       // layers per launch (tags: epoch * 32 + layer + 1)
 constexpr int kAuxSc1 = 16;          // device-coherent access
 constexpr uint32_t kSpinDefault = 10000000u;   // 100 ms
