@@ -53,7 +53,11 @@ constexpr uint32_t kSpinDefault = 10000000u;   // 100 ms
 // Workspace sync words (uint32), each on its own 256-byte line.
 constexpr int kLine = 64;
 constexpr int kWErr = 0, kWSpin = kLine, kWExit = 2 * kLine, kWEpoch = 3 * kLine;
-constexpr int kSyncWords = 4 * kLine;
+constexpr int kMaxGrid = 1024;
+// then two arrays of kMaxGrid tagged entries: a workgroup's rotquant(h) blocks stored,
+// its y rows stored (hints that tell consumers when to read; the data's own tags decide)
+constexpr int kWQDone = 4 * kLine, kWYDone = kWQDone + 2 * kMaxGrid;
+constexpr int kSyncWords = kWYDone + 2 * kMaxGrid;
 constexpr int kCtlBytes = 256;       // LDS control block
 
 struct LLayer {
@@ -208,6 +212,39 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_layers_kernel(LArgs a)
         return true;
     };
 
+    // Wave 0 waits until done entry w is current for every workgroup w (16-byte loads, two
+    // entries each, all issued before any is checked); then every thread passes the barrier.
+    auto wait_done = [&](int word, uint32_t tg, uint64_t t0) {
+        if (tid < 64) {
+            const __amdgpu_buffer_rsrc_t rdn = buffer_rsrc(sync + word, (uint32_t)(G * 8));
+            for (int it = 0;; ++it) {
+                bool ok = true;
+                for (int i = lane; i < (G + 1) / 2; i += 64 * 4) {
+                    u32x4 e[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        e[r] = ld_tag2(rdn, i + 64 * r < (G + 1) / 2 ? (uint32_t)(i + 64 * r) * 16u : kOutOfRange);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int w0 = 2 * (i + 64 * r);
+                        if (w0 < G)
+                            ok = ok && e[r].y == tg;
+                        if (w0 + 1 < G)
+                            ok = ok && e[r].w == tg;
+                    }
+                }
+                if (__all(ok) || !keep_waiting(t0, it))
+                    break;
+            }
+        }
+        __syncthreads();
+    };
+    auto mark_done = [&](int word, uint32_t tg) {
+        __syncthreads();   // every thread of the workgroup has issued its data stores
+        if (tid == 0)
+            st_tag(reinterpret_cast<uint64_t *>(sync + word) + c, 0u, tg);
+    };
+
     // ---- phase transitions (all threads) ------------------------------------------------
     // Stage rotquant of layer l's input into the activation region. For l > 0 this waits
     // until every y row of layer l - 1 is current (strict layer order); chained, those
@@ -233,29 +270,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_layers_kernel(LArgs a)
                     xv[r][4] = hi.x; xv[r][5] = hi.y; xv[r][6] = hi.z; xv[r][7] = hi.w;
                 }
             }
-            if (l > 0) {
-                // strict layer order: every y entry of layer l - 1 is current (the loads of
-                // a round are all issued before any tag is checked)
-                constexpr int kYR = 2;
-                for (int i0 = tid; i0 < M * H / 2; i0 += kYR * kThreads) {
-                    for (int it = 0;; ++it) {
-                        u32x4 e[kYR];
-#pragma unroll
-                        for (int r = 0; r < kYR; ++r) {
-                            const int i = i0 + r * kThreads;
-                            e[r] = ld_tag2(ry, i < M * H / 2 ? (uint32_t)i * 16u : kOutOfRange);
-                        }
-                        bool ok = true;
-#pragma unroll
-                        for (int r = 0; r < kYR; ++r)
-                            if (i0 + r * kThreads < M * H / 2)
-                                ok = ok && e[r].y == tprev && e[r].w == tprev;
-                        if (ok || !keep_waiting(t0, it))
-                            break;
-                    }
-                }
-            }
         }
+        // strict layer order: every workgroup has stored its y rows of layer l - 1
+        if (l > 0)
+            wait_done(kWYDone, tprev, t0);
         auto block = [&](float (&v)[8], int z) {
             const int m = z / nbH, b = z % nbH;
             uint32_t pk[2];
@@ -364,6 +382,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_layers_kernel(LArgs a)
                     st_tag(a.sp + m * nbN + b, (uint32_t)qsum, tg);
             }
         }
+        mark_done(kWQDone, tg);
+        wait_done(kWQDone, tg, __builtin_amdgcn_s_memrealtime());
         // stage all of rotquant(h): units of 16 codes (ternary) or 32 (sign), kR units per
         // thread and round, the block terms in the first round; every load of a round is
         // issued before any tag is checked
@@ -463,6 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_layers_kernel(LArgs a)
             yl[(size_t)m * H + row] = yv;
             st_tag(a.yp + (size_t)m * H + row, __float_as_uint(yv), tg);
         }
+        mark_done(kWYDone, tg);
     };
 
     // ---- the item stream ---------------------------------------------------------------
