@@ -251,11 +251,20 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     for (int r = 0; r < kTermRound; ++r)
         if (tid + r * kRingThreads < nterm)
             dq_s[tid + r * kRingThreads] = dv[r];
-    for (int u = tid + kStageRound * kRingThreads; u < units; u += kRingThreads) {
-        StageUnit<FMT> one;
-        stage_unit_load_step<M, FMT, false>(one, a.q, k, u);
-        stage_unit_store_step<M, FMT>(one, act, k, u);
-        qsum_add(one, u);
+    // the rest in rounds of kStageRound units per thread, every load of a round issued
+    // before its stores (a large M * k takes several rounds: 8 at M = 8, k = 17408)
+    for (int u0 = tid + kStageRound * kRingThreads; u0 - tid < units; u0 += kStageRound * kRingThreads) {
+        StageUnit<FMT> more[kStageRound];
+#pragma unroll
+        for (int r = 0; r < kStageRound; ++r)
+            if (u0 + r * kRingThreads < units)
+                stage_unit_load_step<M, FMT, false>(more[r], a.q, k, u0 + r * kRingThreads);
+#pragma unroll
+        for (int r = 0; r < kStageRound; ++r)
+            if (u0 + r * kRingThreads < units) {
+                stage_unit_store_step<M, FMT>(more[r], act, k, u0 + r * kRingThreads);
+                qsum_add(more[r], u0 + r * kRingThreads);
+            }
     }
     for (int i = tid + kTermRound * kRingThreads; i < nterm; i += kRingThreads) {
         const int b = i / M, m = i % M;
