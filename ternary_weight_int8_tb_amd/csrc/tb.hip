@@ -178,18 +178,29 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     uint32_t rs0[kDepth], rs1[kDepth];
     int rit[kDepth];   // the slot's item as tile << 16 | step, or -1
     int pending = tid >> 6;   // the next item, taken one issue ahead (LDS add in flight)
+    // Offsets split into a per-lane part (row in tile, chunk lane) and a wave-uniform part
+    // (tile, step) passed as the buffer soffset, so an issue costs almost no VALU. The
+    // uniform part of a scale offset is a multiple of 4, so aligning the lane part to the
+    // 4-byte word gives the word of (row, block).
+    const uint32_t lane_off = (uint32_t)rl * row_bytes + (uint32_t)cl * 16u;
+    const uint32_t lane_soff = (((uint32_t)rl * (uint32_t)nb + (uint32_t)(cl / kCpb)) * 2u) & ~3u;
     auto issue = [&](uint4 &w0, uint4 &w1, uint32_t &s0, uint32_t &s1, int &it) {
         const int idx = __builtin_amdgcn_readfirstlane(pending);
         uint32_t off = kOutOfRange, soff = kOutOfRange;
+        int so = 0, sso = 0;
         it = -1;
         if (idx < J) {
             advance_to(idx);
             it = gtile << 16 | gstep;
-            const uint32_t row = (uint32_t)((tA + gtile) * kRowsPerWave + rl);
+            const int row0 = (tA + gtile) * kRowsPerWave;
+            so = row0 * (int)row_bytes + gstep * 256;
+            sso = (row0 * nb + gstep * kBlocksPerStep) * 2;
             const uint32_t extra = gstep == I - 1 ? ragged : 0u;
-            if (row < (uint32_t)n) {
-                off = (row * row_bytes + (uint32_t)cl * 16u + (uint32_t)gstep * 256u) | extra;
-                soff = (((row * (uint32_t)nb + (uint32_t)(gstep * kBlocksPerStep + cl / kCpb)) * 2u) & ~3u) | extra;
+            off = lane_off | extra;
+            soff = lane_soff | extra;
+            if (row0 + kRowsPerWave > n && rl >= n - row0) {   // rows past n (last tile)
+                off = kOutOfRange;
+                soff = kOutOfRange;
             }
             // take the next item now; the add completes while this one streams
             int v = 0;
@@ -197,11 +208,11 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
                 v = atomicAdd(ctr_s, 1);
             pending = v;
         }
-        w0 = buffer_load16_nt(rc0, off);
-        s0 = buffer_load_u32(rsc0, soff);
+        w0 = buffer_load16_nt(rc0, off, so);
+        s0 = buffer_load_u32(rsc0, soff, sso);
         if (kTwo) {
-            w1 = buffer_load16_nt(rc1, off);
-            s1 = buffer_load_u32(rsc1, soff);
+            w1 = buffer_load16_nt(rc1, off, so);
+            s1 = buffer_load_u32(rsc1, soff, sso);
         } else {
             w1 = make_uint4(0, 0, 0, 0);
             s1 = 0;

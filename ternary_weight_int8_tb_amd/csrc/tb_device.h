@@ -76,9 +76,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
                                              (int)kBufWord3);
 }
 
-__device__ __forceinline__ uint4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
+// soffset: a wave-uniform byte offset added to off. Only off is range-checked, so a lane
+// that must read zeros sets off to kOutOfRange; every other lane's off + soffset must lie
+// inside the buffer.
+__device__ __forceinline__ uint4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                  int soffset = 0)
 {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNonTemporal);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soffset, kAuxNonTemporal);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -90,9 +94,10 @@ __device__ __forceinline__ uint16_t buffer_load_u16(__amdgpu_buffer_rsrc_t r, ui
 // The 4-byte word holding the 2-byte value at byte offset off (off & ~3). A 32-bit ring
 // entry needs no zero-extension, which the compiler would otherwise place at the loop
 // latch, where it waits for every outstanding load.
-__device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off)
+__device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                   int soffset = 0)
 {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soffset, 0);
 }
 
 // soffset: a wave-uniform byte offset added to off (not part of the range check).
@@ -116,6 +121,36 @@ __device__ __forceinline__ float silu_gate(float g, float u)
 __device__ __forceinline__ int pair_add(int v)
 {
     return v + __builtin_amdgcn_update_dpp(0, v, 0xB1 /* quad_perm [1,0,3,2] */, 0xF, 0xF, false);
+}
+
+// The value of lane L ^ s of the lane's 16-lane DPP row (s = 1, 2, 4 or 8, a constant
+// once loops are unrolled), moved by DPP instead of an LDS permute. Every lane of the row
+// must be active.
+__device__ __forceinline__ int row_xor(int v, int s)
+{
+    switch (s) {
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0xB1 /* quad_perm [1,0,3,2] */, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x4E /* quad_perm [2,3,0,1] */, 0xF, 0xF, false);
+    case 4: {
+        // L ^ 7 (row_half_mirror), then ^ 3 (quad_perm [3,2,1,0])
+        const int t = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+        return __builtin_amdgcn_update_dpp(0, t, 0x1B, 0xF, 0xF, false);
+    }
+    default: return __builtin_amdgcn_update_dpp(0, v, 0x128 /* row_ror:8 */, 0xF, 0xF, false);
+    }
+}
+__device__ __forceinline__ float row_xor(float v, int s) { return __int_as_float(row_xor(__float_as_int(v), s)); }
+__device__ __forceinline__ uint32_t row_xor(uint32_t v, int s) { return (uint32_t)row_xor((int)v, s); }
+
+// The value of lane t (0..3, a constant once unrolled) of the lane's quad.
+__device__ __forceinline__ uint32_t quad_lane(uint32_t v, int t)
+{
+    switch (t) {
+    case 0: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x00, 0xF, 0xF, false);
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x55, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xAA, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xFF, 0xF, 0xF, false);
+    }
 }
 
 // Ternary decode of one 32-bit code word (16 weights) into four int8x4 words; word j
@@ -164,7 +199,7 @@ __device__ __forceinline__ void rotquant_regs(float (&v)[8], int lane16, float u
         const bool upper = (lane16 & s) != 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float other = __shfl_xor(v[e], s, 16);
+            const float other = row_xor(v[e], s);
             v[e] = upper ? (other - v[e]) : (v[e] + other);
         }
     }
@@ -174,7 +209,7 @@ __device__ __forceinline__ void rotquant_regs(float (&v)[8], int lane16, float u
         amax = fmaxf(amax, fabsf(v[e]));
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, s, 16));
+        amax = fmaxf(amax, row_xor(amax, s));
 
     packed[0] = 0u;
     packed[1] = 0u;
@@ -192,7 +227,7 @@ __device__ __forceinline__ void rotquant_regs(float (&v)[8], int lane16, float u
     }
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1)
-        sum += __shfl_xor(sum, s, 16);
+        sum += row_xor(sum, s);
     dq = amax != 0.0f ? amax * unit : 0.0f;
     qsum = sum;
 }
@@ -400,7 +435,7 @@ __device__ __forceinline__ void store_block_step(uint8_t *act, int m, int b, int
         // 16-code group g = lane16 / 2 is code word g % 4 of chunk 2b + g / 4; its even lane
         // has codes 0..7, the odd lane 8..15. Word e of the group is codes {e, e+4, e+8,
         // e+12}; the even lane writes words 0, 1, the odd lane words 2, 3.
-        const uint32_t q0 = __shfl_xor(pk[0], 1, 16), q1 = __shfl_xor(pk[1], 1, 16);
+        const uint32_t q0 = row_xor(pk[0], 1), q1 = row_xor(pk[1], 1);
         const bool odd = lane16 & 1;
         const uint32_t lo0 = odd ? q0 : pk[0], lo1 = odd ? q1 : pk[1];
         const uint32_t hi0 = odd ? pk[0] : q0, hi1 = odd ? pk[1] : q1;
@@ -417,11 +452,11 @@ __device__ __forceinline__ void store_block_step(uint8_t *act, int m, int b, int
         // 32-code unit u = lane16 / 4: lane i = lane16 % 4 of it has codes 8i .. 8i+7. Word w
         // (0..7) of the unit is codes {w, w+8, w+16, w+24}: words 0..3 go to plane 2u,
         // words 4..7 to plane 2u + 1. Lane i writes words 2i, 2i + 1.
-        const int i = lane16 & 3, base = lane16 & ~3;
+        const int i = lane16 & 3;
         uint32_t src[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint32_t w0 = __shfl(pk[0], base + t, 16), w1 = __shfl(pk[1], base + t, 16);
+            const uint32_t w0 = quad_lane(pk[0], t), w1 = quad_lane(pk[1], t);
             src[t] = (i >> 1) ? w1 : w0;
         }
 #pragma unroll
