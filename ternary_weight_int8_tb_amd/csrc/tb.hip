@@ -224,13 +224,32 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     // weight stream. The sign format's sum(q) per block is accumulated with LDS integer
     // adds from the staged units (exact, any order).
     constexpr int kStageRound = 4, kTermRound = 2;
-    const int units = M * C * 4;
+    const int per_row = C * 4, units = M * per_row;
     const int nterm = (nb + kBlocksPerStep) * M;
+    auto unit_load = [&](StageUnit<FMT> &u, int unit) {
+        int m, g;
+        unit_split<M>(unit, per_row, m, g);
+        stage_unit_load_step<M, FMT, false>(u, a.q, k, m, g);
+    };
+    // the LDS store of a unit, and for the sign format its sum(q) into its block's term
+    auto unit_store = [&](const StageUnit<FMT> &u, int unit) {
+        int m, g;
+        unit_split<M>(unit, per_row, m, g);
+        stage_unit_store_step<M, FMT>(u, act, m, g);
+        if (FMT == TB_FMT_SIGN1) {
+            const uint32_t w[8] = {u.lo.x, u.lo.y, u.lo.z, u.lo.w, u.hi.x, u.hi.y, u.hi.z, u.hi.w};
+            int sum = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sum = dot4(w[e], 0x01010101u, sum);
+            atomicAdd(qsum_s + (g >> 2) * M + m, sum);
+        }
+    };
     StageUnit<FMT> su[kStageRound];
 #pragma unroll
     for (int r = 0; r < kStageRound; ++r)
         if (tid + r * kRingThreads < units)
-            stage_unit_load_step<M, FMT, false>(su[r], a.q, k, tid + r * kRingThreads);
+            unit_load(su[r], tid + r * kRingThreads);
     // block terms [b][m] (transposed from the [m][b] input) plus zero padding
     float dv[kTermRound];
 #pragma unroll
@@ -241,23 +260,10 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
         issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
-    auto qsum_add = [&](const StageUnit<FMT> &u, int unit) {
-        if (FMT == TB_FMT_SIGN1) {
-            const int per_row = C * 4, m = unit / per_row, b = (unit % per_row) >> 2;
-            const uint32_t w[8] = {u.lo.x, u.lo.y, u.lo.z, u.lo.w, u.hi.x, u.hi.y, u.hi.z, u.hi.w};
-            int sum = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sum = dot4(w[e], 0x01010101u, sum);
-            atomicAdd(qsum_s + b * M + m, sum);
-        }
-    };
 #pragma unroll
     for (int r = 0; r < kStageRound; ++r)
-        if (tid + r * kRingThreads < units) {
-            stage_unit_store_step<M, FMT>(su[r], act, k, tid + r * kRingThreads);
-            qsum_add(su[r], tid + r * kRingThreads);
-        }
+        if (tid + r * kRingThreads < units)
+            unit_store(su[r], tid + r * kRingThreads);
 #pragma unroll
     for (int r = 0; r < kTermRound; ++r)
         if (tid + r * kRingThreads < nterm)
@@ -269,13 +275,11 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
 #pragma unroll
         for (int r = 0; r < kStageRound; ++r)
             if (u0 + r * kRingThreads < units)
-                stage_unit_load_step<M, FMT, false>(more[r], a.q, k, u0 + r * kRingThreads);
+                unit_load(more[r], u0 + r * kRingThreads);
 #pragma unroll
         for (int r = 0; r < kStageRound; ++r)
-            if (u0 + r * kRingThreads < units) {
-                stage_unit_store_step<M, FMT>(more[r], act, k, u0 + r * kRingThreads);
-                qsum_add(more[r], u0 + r * kRingThreads);
-            }
+            if (u0 + r * kRingThreads < units)
+                unit_store(more[r], u0 + r * kRingThreads);
     }
     for (int i = tid + kTermRound * kRingThreads; i < nterm; i += kRingThreads) {
         const int b = i / M, m = i % M;

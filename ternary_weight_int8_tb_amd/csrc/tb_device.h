@@ -300,11 +300,24 @@ struct StageUnit {
     uint4 lo, hi;
 };
 
+// A staging unit is (row m, chunk c, part j): 4 parts per chunk (16 activations ternary,
+// 32 sign), numbered unit = m * per_row + 4 c + j with per_row = 4 * chunks per row.
+// unit_split returns m and g = 4 c + j without an integer division (m < M <= 8 rows):
+// a runtime division costs tens of VALU instructions, and staging runs it for every unit.
+template <int M>
+__device__ __forceinline__ void unit_split(int unit, int per_row, int &m, int &g)
+{
+    m = 0;
+#pragma unroll
+    for (int i = 1; i < M; ++i)
+        m += unit >= i * per_row ? 1 : 0;
+    g = unit - m * per_row;
+}
+
 template <int FMT, bool COHERENT>
 __device__ __forceinline__ void stage_unit_load(StageUnit<FMT> &u, const int8_t *q, int k, int c0,
-                                                int sc, int unit)
+                                                int m, int g)
 {
-    const int m = unit / (sc * 4), g = unit % (sc * 4);
     const int c = g >> 2, j = g & 3;
     if (FMT == TB_FMT_TERNARY2) {
         u.lo = load16<COHERENT>(q + (size_t)m * k + (size_t)(c0 + c) * 64 + j * 16);
@@ -317,9 +330,8 @@ __device__ __forceinline__ void stage_unit_load(StageUnit<FMT> &u, const int8_t 
 
 template <int FMT>
 __device__ __forceinline__ void stage_unit_store(const StageUnit<FMT> &u, uint8_t *act, int S,
-                                                 int sc, int unit)
+                                                 int m, int g)
 {
-    const int m = unit / (sc * 4), g = unit % (sc * 4);
     const int c = g >> 2, j = g & 3;
     if (FMT == TB_FMT_TERNARY2) {
         const uint4 r = u.lo;
@@ -352,8 +364,10 @@ __device__ __forceinline__ void stage_act(uint8_t *act, int S, const int8_t *q, 
     const int units = M * sc * 4;
     for (int u = tid; u < units; u += nthreads) {
         StageUnit<FMT> su;
-        stage_unit_load<FMT, COHERENT>(su, q, k, c0, sc, u);
-        stage_unit_store<FMT>(su, act, S, sc, u);
+        int m, g;
+        unit_split<M>(u, sc * 4, m, g);
+        stage_unit_load<FMT, COHERENT>(su, q, k, c0, m, g);
+        stage_unit_store<FMT>(su, act, S, m, g);
     }
 }
 
@@ -376,11 +390,8 @@ struct StepLayout {
 
 template <int M, int FMT, bool COHERENT>
 __device__ __forceinline__ void stage_unit_load_step(StageUnit<FMT> &u, const int8_t *q, int k,
-                                                     int unit)
+                                                     int m, int g)
 {
-    // unit = (m, chunk c, part j): 4 parts per chunk (16 activations ternary, 32 sign)
-    const int per_row = (FMT == TB_FMT_TERNARY2 ? k / 64 : k / 128) * 4;
-    const int m = unit / per_row, g = unit % per_row;
     const int c = g >> 2, j = g & 3;
     if (FMT == TB_FMT_TERNARY2) {
         u.lo = load16<COHERENT>(q + (size_t)m * k + (size_t)c * 64 + j * 16);
@@ -392,12 +403,10 @@ __device__ __forceinline__ void stage_unit_load_step(StageUnit<FMT> &u, const in
 }
 
 template <int M, int FMT>
-__device__ __forceinline__ void stage_unit_store_step(const StageUnit<FMT> &u, uint8_t *act, int k,
-                                                      int unit)
+__device__ __forceinline__ void stage_unit_store_step(const StageUnit<FMT> &u, uint8_t *act, int m,
+                                                      int g)
 {
     using L = StepLayout<M, FMT>;
-    const int per_row = (FMT == TB_FMT_TERNARY2 ? k / 64 : k / 128) * 4;
-    const int m = unit / per_row, g = unit % per_row;
     const int c = g >> 2, j = g & 3;
     uint8_t *base = act + (size_t)(c >> 4) * L::kStepBytes + (c & 15) * 16;
     if (FMT == TB_FMT_TERNARY2) {

@@ -403,7 +403,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_layers_kernel(LArgs a)
 #pragma unroll
                 for (int r = 0; r < kR; ++r) {
                     const int u = u0 + r * kThreads;
-                    const int m = u / per_row, g2 = u % per_row;
+                    int m, g2;
+                    unit_split<M>(u, per_row, m, g2);
                     const uint32_t off = u < units ? (uint32_t)((m * N + (g2 >> 2) * kWpc + (g2 & 3) * (kWpc / 4)) * 2)
                                                    : kOutOfRange;
 #pragma unroll
@@ -437,7 +438,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_layers_kernel(LArgs a)
                 su.lo = make_uint4(e[r][0].x, e[r][0].z, e[r][1].x, e[r][1].z);
                 if (FMT == TB_FMT_SIGN1)
                     su.hi = make_uint4(e[r][kE - 2].x, e[r][kE - 2].z, e[r][kE - 1].x, e[r][kE - 1].z);
-                stage_unit_store_step<M, FMT>(su, act, N, u);
+                int m, g2;
+                unit_split<M>(u, per_row, m, g2);
+                stage_unit_store_step<M, FMT>(su, act, m, g2);
             }
             if (first) {
 #pragma unroll
