@@ -55,6 +55,19 @@ constexpr int kRingWaves = TB_RING_WAVES;
 constexpr int kRingThreads = 64 * kRingWaves;
 constexpr int kRingDepthTwo = TB_RING_DEPTH_TWO;   // items in flight per wave, gate + up
 constexpr int kRingDepthOne = TB_RING_DEPTH_ONE;   // one matrix
+#ifndef TB_MFMA_DEPTH
+#define TB_MFMA_DEPTH 2
+#endif
+#ifndef TB_MFMA_MIN_ROWS
+#define TB_MFMA_MIN_ROWS 6
+#endif
+constexpr int kMfmaDepth = TB_MFMA_DEPTH;         // items in flight per wave (MFMA kernel)
+// M from which gate/up runs on the matrix cores. The MFMA kernel takes about the same time
+// for every M (22 µs for gate/up at the FFN shape, M = 4 or 8), the dot-product kernel
+// grows with M (18 µs at M = 4, 26 µs at M = 8); for the down GEMV, whose 20 rows per CU
+// fill only 20 of 32 MFMA rows, the dot-product kernel is as fast at M = 8.
+constexpr int kMfmaMinRows = TB_MFMA_MIN_ROWS;
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 enum Mode { kModeY = 0, kModeGateUp = 1, kModeIsum = 2 };
 
@@ -92,6 +105,83 @@ __device__ __forceinline__ void store_row(const GemvArgs &a, int row, const floa
 #pragma unroll
     for (int m = 0; m < M; ++m)
         a.out[(size_t)m * a.n + row] = MODE == kModeGateUp ? silu_gate(acc0[m], acc1[m]) : acc0[m];
+}
+
+// ------------------------------------------------------------------------------------
+// Stages the int8 activation q[M][k] into the step-major LDS layout and the block terms
+// dq as [b][m] (zero padded by one step of blocks, so ragged lanes read zeros). For the
+// sign format it also adds sum(q) per block into qsum_s (LDS integer adds: exact in any
+// order; qsum_s starts at zero). The loads of the first round go out before `prologue`
+// (the weight stream's first loads) and their LDS stores after it, so the activation is
+// not queued behind the weights: one vmcnt counts a wave's loads in issue order.
+// ------------------------------------------------------------------------------------
+template <int M, int FMT, int MODE, int NTHREADS, bool MFMA_LAYOUT, class Prologue>
+__device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act, float *dq_s,
+                                                 int *qsum_s, Prologue &&prologue)
+{
+    constexpr int kBlocksPerStep = kChunkLanes / Fmt<FMT>::kChunksPerBlock;
+    constexpr int kStageRound = 4, kTermRound = 2;
+    const int tid = threadIdx.x, k = a.k, nb = k / kBlock;
+    const int per_row = (k / Fmt<FMT>::kWeightsPerChunk) * 4, units = M * per_row;
+    const int nterm = (nb + kBlocksPerStep) * M;
+    auto unit_load = [&](StageUnit<FMT> &u, int unit) {
+        int m, g;
+        unit_split<M>(unit, per_row, m, g);
+        stage_unit_load_step<M, FMT, false>(u, a.q, k, m, g);
+    };
+    auto unit_store = [&](const StageUnit<FMT> &u, int unit) {
+        int m, g;
+        unit_split<M>(unit, per_row, m, g);
+        if constexpr (MFMA_LAYOUT)
+            stage_unit_store_mfma<M>(u, act, m, g);
+        else
+            stage_unit_store_step<M, FMT>(u, act, m, g);
+        if (FMT == TB_FMT_SIGN1) {
+            const uint32_t w[8] = {u.lo.x, u.lo.y, u.lo.z, u.lo.w, u.hi.x, u.hi.y, u.hi.z, u.hi.w};
+            int sum = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sum = dot4(w[e], 0x01010101u, sum);
+            atomicAdd(qsum_s + (g >> 2) * M + m, sum);
+        }
+    };
+    StageUnit<FMT> su[kStageRound];
+#pragma unroll
+    for (int r = 0; r < kStageRound; ++r)
+        if (tid + r * NTHREADS < units)
+            unit_load(su[r], tid + r * NTHREADS);
+    float dv[kTermRound];
+#pragma unroll
+    for (int r = 0; r < kTermRound; ++r) {
+        const int i = tid + r * NTHREADS, b = i / M, m = i % M;
+        dv[r] = (MODE != kModeIsum && i < nterm && b < nb) ? a.dq[m * nb + b] : 0.0f;
+    }
+    prologue();
+#pragma unroll
+    for (int r = 0; r < kStageRound; ++r)
+        if (tid + r * NTHREADS < units)
+            unit_store(su[r], tid + r * NTHREADS);
+#pragma unroll
+    for (int r = 0; r < kTermRound; ++r)
+        if (tid + r * NTHREADS < nterm)
+            dq_s[tid + r * NTHREADS] = dv[r];
+    // the rest in rounds of kStageRound units per thread, every load of a round issued
+    // before its stores (a large M * k takes several rounds: 3 at M = 8, k = 17408)
+    for (int u0 = tid + kStageRound * NTHREADS; u0 - tid < units; u0 += kStageRound * NTHREADS) {
+        StageUnit<FMT> more[kStageRound];
+#pragma unroll
+        for (int r = 0; r < kStageRound; ++r)
+            if (u0 + r * NTHREADS < units)
+                unit_load(more[r], u0 + r * NTHREADS);
+#pragma unroll
+        for (int r = 0; r < kStageRound; ++r)
+            if (u0 + r * NTHREADS < units)
+                unit_store(more[r], u0 + r * NTHREADS);
+    }
+    for (int i = tid + kTermRound * NTHREADS; i < nterm; i += NTHREADS) {
+        const int b = i / M, m = i % M;
+        dq_s[i] = (MODE != kModeIsum && b < nb) ? a.dq[m * nb + b] : 0.0f;
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -219,72 +309,12 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
         }
     };
 
-    // ---- staging: the small loads (q and the block terms) go first, then the ring
-    // prologue, then the LDS stores, so that the activation is not queued behind the
-    // weight stream. The sign format's sum(q) per block is accumulated with LDS integer
-    // adds from the staged units (exact, any order).
-    constexpr int kStageRound = 4, kTermRound = 2;
-    const int per_row = C * 4, units = M * per_row;
-    const int nterm = (nb + kBlocksPerStep) * M;
-    auto unit_load = [&](StageUnit<FMT> &u, int unit) {
-        int m, g;
-        unit_split<M>(unit, per_row, m, g);
-        stage_unit_load_step<M, FMT, false>(u, a.q, k, m, g);
-    };
-    // the LDS store of a unit, and for the sign format its sum(q) into its block's term
-    auto unit_store = [&](const StageUnit<FMT> &u, int unit) {
-        int m, g;
-        unit_split<M>(unit, per_row, m, g);
-        stage_unit_store_step<M, FMT>(u, act, m, g);
-        if (FMT == TB_FMT_SIGN1) {
-            const uint32_t w[8] = {u.lo.x, u.lo.y, u.lo.z, u.lo.w, u.hi.x, u.hi.y, u.hi.z, u.hi.w};
-            int sum = 0;
+    // ---- staging (q and the block terms; the ring prologue between loads and stores)
+    stage_activation<M, FMT, MODE, kRingThreads, false>(a, act, dq_s, qsum_s, [&]() {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sum = dot4(w[e], 0x01010101u, sum);
-            atomicAdd(qsum_s + (g >> 2) * M + m, sum);
-        }
-    };
-    StageUnit<FMT> su[kStageRound];
-#pragma unroll
-    for (int r = 0; r < kStageRound; ++r)
-        if (tid + r * kRingThreads < units)
-            unit_load(su[r], tid + r * kRingThreads);
-    // block terms [b][m] (transposed from the [m][b] input) plus zero padding
-    float dv[kTermRound];
-#pragma unroll
-    for (int r = 0; r < kTermRound; ++r) {
-        const int i = tid + r * kRingThreads, b = i / M, m = i % M;
-        dv[r] = (MODE != kModeIsum && i < nterm && b < nb) ? a.dq[m * nb + b] : 0.0f;
-    }
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d)
-        issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
-#pragma unroll
-    for (int r = 0; r < kStageRound; ++r)
-        if (tid + r * kRingThreads < units)
-            unit_store(su[r], tid + r * kRingThreads);
-#pragma unroll
-    for (int r = 0; r < kTermRound; ++r)
-        if (tid + r * kRingThreads < nterm)
-            dq_s[tid + r * kRingThreads] = dv[r];
-    // the rest in rounds of kStageRound units per thread, every load of a round issued
-    // before its stores (a large M * k takes several rounds: 8 at M = 8, k = 17408)
-    for (int u0 = tid + kStageRound * kRingThreads; u0 - tid < units; u0 += kStageRound * kRingThreads) {
-        StageUnit<FMT> more[kStageRound];
-#pragma unroll
-        for (int r = 0; r < kStageRound; ++r)
-            if (u0 + r * kRingThreads < units)
-                unit_load(more[r], u0 + r * kRingThreads);
-#pragma unroll
-        for (int r = 0; r < kStageRound; ++r)
-            if (u0 + r * kRingThreads < units)
-                unit_store(more[r], u0 + r * kRingThreads);
-    }
-    for (int i = tid + kTermRound * kRingThreads; i < nterm; i += kRingThreads) {
-        const int b = i / M, m = i % M;
-        dq_s[i] = (MODE != kModeIsum && b < nb) ? a.dq[m * nb + b] : 0.0f;
-    }
+        for (int d = 0; d < kDepth; ++d)
+            issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
+    });
     __syncthreads();
 
     // ---- compute side -----------------------------------------------------------------
@@ -373,6 +403,196 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
                 u += ps[(size_t)s * kRowsPerWave * M * kParts + 1];
         }
         a.out[(size_t)m * n + row] = kTwo ? silu_gate(g, u) : g;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Batched streaming GEMV on the matrix cores: ternary weights, M >= kMfmaMinRows rows.
+// With M rows the dot products cost M VALU instructions per 4 weights and lane; here
+// v_mfma_i32_16x16x64_i8 takes them, and the VALU keeps the decode and the fold.
+//   * Workgroup c owns the rows of the same 4-row tiles [tA, tB) as in gemv_ring_kernel
+//     and covers them with 16-row tiles; rows past its range read zeros and are not written.
+//   * An item is one step (8 blocks) of one 16-row tile. Lane (i, g) = (lane % 16, lane / 16)
+//     loads 8 code bytes of row i per block: weights 32 g .. 32 g + 31 of the block. Their
+//     two decoded code words are the A operands of two MFMAs (16 weights per lane each);
+//     the B operands are the matching transposed 16-byte activation groups (column j =
+//     activation row j), so the two MFMAs leave the block's exact integer sums in D: lane
+//     l holds rows 4 (l / 16) + r, r = 0..3, of activation row l % 16. The activation is
+//     staged as [step][chunk][code word][row] so that the 16 lanes of a B operand read
+//     consecutive 16-byte slots; the step-major layout of the other kernels has the rows
+//     256 bytes apart, and its 8-way bank conflicts made this kernel slower than the VALU
+//     one.
+//   * The block term (s * dq) * isum, the step tree over the step's 8 blocks, and the step
+//     sum in step order from +0 are those of the other kernels (row_tree reads lane L - off,
+//     so lane 0 of a row ends with ((t0 + t7) + (t6 + t5)) + ((t4 + t3) + (t2 + t1)) over
+//     the block terms t), so every row is bit-identical to the row computed alone.
+//   * A block's scales reach the fold lanes with ds_bpermute from the lanes that loaded
+//     them (one 32-bit word: the block pair 2 g, 2 g + 1 of row i; nb must be even).
+// ------------------------------------------------------------------------------------
+template <int M, int MODE>
+__global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    constexpr int FMT = TB_FMT_TERNARY2;
+    using L = StepLayout<M, FMT>;
+    constexpr bool kTwo = MODE == kModeGateUp;
+    constexpr int kParts = kTwo ? 2 : 1;
+    constexpr int kMatShift = kTwo ? 1 : 0;   // gate/up: item = ((tile, step), matrix)
+    constexpr int kBps = 8;   // blocks per step
+    constexpr int kDepth = kMfmaDepth;
+
+    const int k = a.k, n = a.n, nb = k / kBlock;
+    const int C = k / 64, I = (C + kChunkLanes - 1) / kChunkLanes;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int G = gridDim.x, c = blockIdx.x;
+    const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
+    const int R0 = part_lo(T, G, c) * kRowsPerWave;
+    const int R1 = min(part_lo(T, G, c + 1) * kRowsPerWave, n);
+    const int J = (((R1 - R0 + 15) / 16) * I) << kMatShift;   // this workgroup's items
+    const uint32_t row_bytes = (uint32_t)C * 16u;
+
+    uint8_t *act = lds;
+    float *dq_s = reinterpret_cast<float *>(lds + (size_t)I * L::kStepBytes);
+    int *ctr_s = reinterpret_cast<int *>(dq_s + (size_t)(nb + kBps) * M);
+    float *part_s = reinterpret_cast<float *>(ctr_s + 4);   // [row - R0][step][m][part]
+
+    if (tid == 0)
+        *ctr_s = kRingWaves;   // wave w starts with item w
+    __syncthreads();
+
+    // ---- issue side: as in gemv_ring_kernel, with a per-lane and a wave-uniform offset
+    int gidx = 0, gtile = 0, gstep = 0;
+    auto advance_to = [&](int idx) {
+        gstep += idx - gidx;
+        gidx = idx;
+        while (gstep >= I) {
+            gstep -= I;
+            ++gtile;
+        }
+    };
+    const uint32_t lane_off = (uint32_t)li * row_bytes + (uint32_t)lg * 8u;
+    const uint32_t lane_soff = ((uint32_t)li * (uint32_t)nb + (uint32_t)lg * 2u) * 2u;
+    u32x2 rc[kDepth][kBps];
+    uint32_t rs[kDepth];
+    int rit[kDepth];   // matrix << 30 | tile << 16 | step, or -1
+    int pending = tid >> 6;
+    auto issue = [&](int d) {
+        const int idx = __builtin_amdgcn_readfirstlane(pending);
+        uint32_t off = kOutOfRange, soff = kOutOfRange;
+        int so = 0, sso = 0, nbk = 0, mat = 0;
+        rit[d] = -1;
+        if (idx < J) {
+            advance_to(idx >> kMatShift);
+            mat = idx & (kTwo ? 1 : 0);
+            rit[d] = mat << 30 | gtile << 16 | gstep;
+            const int row0 = R0 + gtile * 16;
+            so = row0 * (int)row_bytes + gstep * 256;
+            sso = (row0 * nb + gstep * kBps) * 2;
+            nbk = min(kBps, nb - gstep * kBps);   // blocks of this step inside the row
+            if (row0 + li < R1) {
+                off = lane_off;
+                soff = gstep * kBps + 2 * lg < nb ? lane_soff : kOutOfRange;
+            }
+            int v = 0;
+            if (lane == 0)
+                v = atomicAdd(ctr_s, 1);
+            pending = v;
+        }
+        // (the descriptors are built per issue from wave-uniform values: arrays of them
+        // would live in scratch)
+        const __amdgpu_buffer_rsrc_t rcm = buffer_rsrc(mat ? a.codes1 : a.codes0, a.codes_bytes);
+        const __amdgpu_buffer_rsrc_t rsm = buffer_rsrc(mat ? a.scales1 : a.scales0, a.scales_bytes);
+#pragma unroll
+        for (int kb = 0; kb < kBps; ++kb)
+            rc[d][kb] = __builtin_amdgcn_raw_buffer_load_b64(
+                rcm, kb < nbk ? off + (uint32_t)kb * 32u : kOutOfRange, so, 0);
+        rs[d] = buffer_load_u32(rsm, soff, sso);
+    };
+
+    stage_activation<M, FMT, MODE, kRingThreads, true>(a, act, dq_s, nullptr, [&]() {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+            issue(d);
+    });
+    __syncthreads();
+
+    // ---- compute side
+    const int mB = li < M ? li : M - 1;   // activation row of this lane's B and D column
+    auto consume = [&](int d) {
+        const int mat = rit[d] >> 30, tile = (rit[d] >> 16) & 0x3fff, step = rit[d] & 0xffff;
+        // B: chunk 2 kb + (lg >> 1), code words 2 (lg & 1) and + 1, row mB
+        const uint8_t *sact = act + (size_t)step * L::kStepBytes +
+                              (((lg >> 1) * 4 + 2 * (lg & 1)) * M + mB) * 16;
+        float t01[4], t23[4], tot[4];
+#pragma unroll
+        for (int o = 0; o < kBps; ++o) {
+            const int kb = o == 0 ? 0 : kBps - o;   // tree order 0, 7, 6, 5, 4, 3, 2, 1
+            const int blk = step * kBps + kb;
+            const v4i b0 = *reinterpret_cast<const v4i *>(sact + kb * 2 * 4 * M * 16);
+            const v4i b1 = *reinterpret_cast<const v4i *>(sact + kb * 2 * 4 * M * 16 + M * 16);
+            const float dqv = dq_s[blk * M + mB];
+            uint32_t w[8];
+            decode_ternary(rc[d][kb].x, w[0], w[1], w[2], w[3]);
+            decode_ternary(rc[d][kb].y, w[4], w[5], w[6], w[7]);
+            const v4i a0 = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+            const v4i a1 = {(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+            v4i acc = {0, 0, 0, 0};
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // the scale word of row 4 lg + r, blocks (kb & ~1, kb | 1) of the step
+                const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                    (16 * (kb >> 1) + 4 * lg + r) * 4, (int)rs[d]);
+                const float sv = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(sw, (kb & 1) * 16, 16));
+                const float t = (sv * dqv) * (float)acc[r];
+                // ((t0 + t7) + (t6 + t5)) + ((t4 + t3) + (t2 + t1))
+                if (o == 0 || o == 2 || o == 4 || o == 6)
+                    t01[r] = t;
+                else if (o == 1 || o == 5)
+                    t23[r] = t01[r] + t;
+                else if (o == 3)
+                    tot[r] = t23[r] + (t01[r] + t);
+                else
+                    tot[r] = tot[r] + (t23[r] + (t01[r] + t));
+            }
+        }
+        if (li < M) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int lrow = tile * 16 + 4 * lg + r;   // row - R0
+                if (R0 + lrow < R1)
+                    part_s[((size_t)(lrow * I + step) * M + li) * kParts + mat] = tot[r];
+            }
+        }
+    };
+    for (;;) {
+        bool any = false;
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            if (rit[d] >= 0) {
+                consume(d);
+                any = true;
+            }
+            issue(d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!any)
+            break;
+    }
+
+    // ---- every row: its step partials in step order, from +0
+    __syncthreads();
+    for (int i = tid; i < (R1 - R0) * M; i += kRingThreads) {
+        const int lrow = i / M, m = i % M;
+        const float *ps = part_s + ((size_t)lrow * I * M + m) * kParts;
+        float g = 0.0f, u = 0.0f;
+        for (int st = 0; st < I; ++st) {
+            g += ps[(size_t)st * M * kParts];
+            if (kTwo)
+                u += ps[(size_t)st * M * kParts + 1];
+        }
+        a.out[(size_t)m * n + R0 + lrow] = kTwo ? silu_gate(g, u) : g;
     }
 }
 
@@ -503,6 +723,18 @@ using GemvFn = void (*)(GemvArgs);
 TB_KERNEL_TABLE(gemv_ring_kernel)
 TB_KERNEL_TABLE(gemv_sliced_kernel)
 
+template <int MODE>
+GemvFn gemv_mfma_pick_m(int m)
+{
+    switch (m) {
+    case 6: return gemv_mfma_kernel<6, MODE>;
+    case 7: return gemv_mfma_kernel<7, MODE>;
+    case 8: return gemv_mfma_kernel<8, MODE>;
+    default: return nullptr;
+    }
+}
+static_assert(kMfmaMinRows >= 6, "gemv_mfma_kernel is instantiated for M = 6 .. 8");
+
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
     int lds_limit = 0;   // 0 = not queried yet
@@ -619,10 +851,27 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     const long tiles = (w0->n + kRowsPerWave - 1) / kRowsPerWave;
     const int ring_grid = (int)(tiles < info.cus ? tiles : info.cus);
     const size_t terms = block_terms_bytes(w0->fmt, m, nb);
-
-    // whole activation in LDS: the persistent ring kernel, one workgroup per CU
     const int steps = (C + kChunkLanes - 1) / kChunkLanes;
     const size_t step_bytes = (size_t)(w0->fmt == TB_FMT_TERNARY2 ? 1024 : 2048) * m;
+
+    // batched ternary rows: the matrix-core kernel, when its LDS plan fits (it needs an
+    // even number of blocks per row: a lane's scale word holds a block pair)
+    if (w0->fmt == TB_FMT_TERNARY2 && mode == kModeGateUp && m >= kMfmaMinRows && nb % 2 == 0) {
+        const size_t rows_cu = (size_t)((tiles + ring_grid - 1) / ring_grid) * kRowsPerWave;
+        const size_t mfma_lds = (size_t)steps * step_bytes + (size_t)m * (nb + 8) * 4 + 16 +
+                                rows_cu * steps * m * (mode == kModeGateUp ? 2 : 1) * 4;
+        if (mfma_lds <= (size_t)info.lds_limit) {
+            GemvFn fn = gemv_mfma_pick_m<kModeGateUp>(m);
+            if (!fn)
+                return TB_EINVAL;
+            if ((rc = set_lds(fn, mfma_lds)))
+                return rc;
+            hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(kRingThreads), mfma_lds, stream, a);
+            return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+        }
+    }
+
+    // whole activation in LDS: the persistent ring kernel, one workgroup per CU
     const size_t pad_blocks = (size_t)(kChunkLanes / (w0->fmt == TB_FMT_TERNARY2 ? 2 : 1));
     const size_t ring_terms = (size_t)m * (nb + pad_blocks) * 4 * (w0->fmt == TB_FMT_TERNARY2 ? 1 : 2);
     // item counter, then the step partials of the largest workgroup's items

@@ -26,6 +26,7 @@ constexpr int kChunkLanes = 16;   // lanes that share one weight row
 constexpr int kRowsPerWave = 4;   // 64 lanes / 16
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int FMT>
 struct Fmt;
@@ -429,6 +430,25 @@ __device__ __forceinline__ void stage_unit_store_step(const StageUnit<FMT> &u, u
     }
 }
 
+// The same 16-byte groups in the layout of the matrix-core kernel (ternary): per step
+// [chunk (16)][code word (4)][row m (M)], so that the 16 lanes of an MFMA B operand, which
+// hold the M rows of one group, read consecutive 16-byte slots (no bank conflicts).
+template <int M>
+__device__ __forceinline__ void stage_unit_store_mfma(const StageUnit<TB_FMT_TERNARY2> &u, uint8_t *act,
+                                                      int m, int g)
+{
+    using L = StepLayout<M, TB_FMT_TERNARY2>;
+    const int c = g >> 2, j = g & 3;
+    const uint4 r = u.lo;
+    uint4 o;
+    o.x = byte_at(r.x, 0) | byte_at(r.y, 0) << 8 | byte_at(r.z, 0) << 16 | byte_at(r.w, 0) << 24;
+    o.y = byte_at(r.x, 1) | byte_at(r.y, 1) << 8 | byte_at(r.z, 1) << 16 | byte_at(r.w, 1) << 24;
+    o.z = byte_at(r.x, 2) | byte_at(r.y, 2) << 8 | byte_at(r.z, 2) << 16 | byte_at(r.w, 2) << 24;
+    o.w = byte_at(r.x, 3) | byte_at(r.y, 3) << 8 | byte_at(r.z, 3) << 16 | byte_at(r.w, 3) << 24;
+    *reinterpret_cast<uint4 *>(act + (size_t)(c >> 4) * L::kStepBytes +
+                               ((((c & 15) * 4 + j) * M + m) * 16)) = o;
+}
+
 // One rotated-quantised block into the step-major layout. The 16-lane group holds block b
 // of row m; lane L has codes 8L .. 8L+7 packed little-endian in pk[0], pk[1] (the
 // registers rotquant_regs returns). Lanes exchange codes so that each writes 8 bytes of
@@ -777,9 +797,11 @@ __device__ __forceinline__ float row_down(float v, int off)
     return __int_as_float(r);
 }
 
-// Fixed tree over the 16 lanes of a row; lane 0 of the row ends with the total:
-// ((a0 + a2) + (a4 + a6)) + ((a8 + a10) + (a12 + a14)) for ternary (odd lanes hold
-// copies), or the same over all 16 lanes for sign. DPP row rotates: no LDS traffic.
+// Fixed tree over the 16 lanes of a row; lane 0 of the row ends with the total. Each
+// level adds the value of lane L - off (row_ror reads the lane off places below, mod 16),
+// so for ternary (odd lanes hold copies) lane 0 gets
+// ((a0 + a14) + (a12 + a10)) + ((a8 + a6) + (a4 + a2)), and for sign the same pattern
+// over all 16 lanes with offsets 1, 2, 4, 8. DPP row rotates: no LDS traffic.
 template <int M, int FMT, bool TWO>
 __device__ __forceinline__ void row_tree(float (&acc0)[M], float (&acc1)[M])
 {

@@ -126,7 +126,6 @@ __device__ __forceinline__ u32x4 ld_tag2(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxSc1);
 }
 // One tagged entry (8 bytes, one load): .x value, .y tag.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 ld_tag1(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAuxSc1);

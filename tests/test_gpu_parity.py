@@ -127,6 +127,34 @@ def test_sliced_and_streaming_kernels_fold_alike(o, fmt):
         assert y1[0].tobytes() == y8[r].tobytes(), r
 
 
+@pytest.mark.parametrize("n,k", [(100, 1280), (2180, 1280), (1152, 5120)])
+def test_matrix_core_and_dot_kernels_fold_alike(o, n, k):
+    # Ternary gate/up from M = 6 on runs on the matrix cores (16-row tiles, rows past a
+    # CU's range masked; k = 1280 has a ragged second step of 2 blocks); a row alone runs on
+    # the dot-product kernel. Both fold every row in the same order, so the batched rows
+    # must equal the rows alone bit for bit.
+    say(f"matrix-core vs dot-product gate/up n={n} k={k}")
+    wg = synth.matrix(TERN, n, k, 13, 0, synth.T_GATE)
+    wu = synth.matrix(TERN, n, k, 13, 0, synth.T_UP)
+    dg, du = tb.Matrix.upload(wg), tb.Matrix.upload(wu)
+
+    def gateup(qm, dqm):
+        h = gu.f32_out(qm.shape[0], n)
+        tb.tb_ffn_gateup_silu(dg, du, gu.dev(qm), gu.dev(dqm), h)
+        return gu.host(h)
+
+    x = synth.normal_rows(8, k, 13, 0)
+    q, dq = o.rotate_quant(x)
+    alone = [gateup(q[r:r + 1], dq[r:r + 1])[0].tobytes() for r in range(8)]
+    for m in (6, 7, 8):
+        h = gateup(q[:m], dq[:m])
+        for r in range(m):
+            assert h[r].tobytes() == alone[r], f"M={m} row {r}"
+    r = o.gateup_silu(wg, wu, q, dq)
+    tol = bounds.h_tolerance(r["g"], r["u"], r["sg"], r["su"])
+    assert np.all(np.abs(h.astype(np.float64) - r["h"]) <= tol)
+
+
 def test_code3_and_zero_cases(o):
     rng = np.random.default_rng(5)
     codes = rng.integers(0, 4, (130, 384)).astype(np.uint8)     # includes the unused code 3
