@@ -124,14 +124,25 @@ __device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act
     const int tid = threadIdx.x, k = a.k, nb = k / kBlock;
     const int per_row = (k / Fmt<FMT>::kWeightsPerChunk) * 4, units = M * per_row;
     const int nterm = (nb + kBlocksPerStep) * M;
+    // Unit numbering: row-major (m, g) for the step-major layout; (g, m) for the MFMA
+    // layout, whose slot of unit (g, m) is g * M + m, so that consecutive threads store
+    // consecutive 16-byte slots (the other order makes 32-way LDS bank conflicts).
+    auto split = [&](int unit, int &m, int &g) {
+        if constexpr (MFMA_LAYOUT) {
+            m = unit % M;
+            g = unit / M;
+        } else {
+            unit_split<M>(unit, per_row, m, g);
+        }
+    };
     auto unit_load = [&](StageUnit<FMT> &u, int unit) {
         int m, g;
-        unit_split<M>(unit, per_row, m, g);
+        split(unit, m, g);
         stage_unit_load_step<M, FMT, false>(u, a.q, k, m, g);
     };
     auto unit_store = [&](const StageUnit<FMT> &u, int unit) {
         int m, g;
-        unit_split<M>(unit, per_row, m, g);
+        split(unit, m, g);
         if constexpr (MFMA_LAYOUT)
             stage_unit_store_mfma<M>(u, act, m, g);
         else
@@ -145,6 +156,26 @@ __device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act
             atomicAdd(qsum_s + (g >> 2) * M + m, sum);
         }
     };
+    // Beyond the first round (a large M * k), in rounds of kStageRound units per thread,
+    // before the prologue: the compiler waits for every outstanding load at the exit of a
+    // loop that loads, so such a loop between the prologue and the barrier would hold the
+    // barrier until the whole weight prologue has arrived.
+    for (int u0 = tid + kStageRound * NTHREADS; u0 - tid < units; u0 += kStageRound * NTHREADS) {
+        StageUnit<FMT> more[kStageRound];
+#pragma unroll
+        for (int r = 0; r < kStageRound; ++r)
+            if (u0 + r * NTHREADS < units)
+                unit_load(more[r], u0 + r * NTHREADS);
+#pragma unroll
+        for (int r = 0; r < kStageRound; ++r)
+            if (u0 + r * NTHREADS < units)
+                unit_store(more[r], u0 + r * NTHREADS);
+    }
+    for (int i = tid + kTermRound * NTHREADS; i < nterm; i += NTHREADS) {
+        const int b = i / M, m = i % M;
+        dq_s[i] = (MODE != kModeIsum && b < nb) ? a.dq[m * nb + b] : 0.0f;
+    }
+    // the first round: loads, the prologue, stores (straight-line code, exact waits)
     StageUnit<FMT> su[kStageRound];
 #pragma unroll
     for (int r = 0; r < kStageRound; ++r)
@@ -165,23 +196,6 @@ __device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act
     for (int r = 0; r < kTermRound; ++r)
         if (tid + r * NTHREADS < nterm)
             dq_s[tid + r * NTHREADS] = dv[r];
-    // the rest in rounds of kStageRound units per thread, every load of a round issued
-    // before its stores (a large M * k takes several rounds: 3 at M = 8, k = 17408)
-    for (int u0 = tid + kStageRound * NTHREADS; u0 - tid < units; u0 += kStageRound * NTHREADS) {
-        StageUnit<FMT> more[kStageRound];
-#pragma unroll
-        for (int r = 0; r < kStageRound; ++r)
-            if (u0 + r * NTHREADS < units)
-                unit_load(more[r], u0 + r * NTHREADS);
-#pragma unroll
-        for (int r = 0; r < kStageRound; ++r)
-            if (u0 + r * NTHREADS < units)
-                unit_store(more[r], u0 + r * NTHREADS);
-    }
-    for (int i = tid + kTermRound * NTHREADS; i < nterm; i += NTHREADS) {
-        const int b = i / M, m = i % M;
-        dq_s[i] = (MODE != kModeIsum && b < nb) ? a.dq[m * nb + b] : 0.0f;
-    }
 }
 
 // ------------------------------------------------------------------------------------
