@@ -22,7 +22,10 @@
 //     v_dot4c_i32_i8 against the LDS-staged transposed activation, one DPP add to join the
 //     two half-block sums, an fp32 term per block, a fixed DPP tree per row and step, and
 //     the step partials summed in step order (tb_device.h).
-//   * No MFMA: with M <= 8 rows this is not a dense contraction. No floating-point atomics.
+//   * With M <= 8 rows this is not a dense contraction: the roof is HBM. From M = 6 on,
+//     gate/up hands its integer dot products to v_mfma_i32_16x16x64_i8
+//     (gemv_mfma_kernel), where M dot products per 4 weights would bind the VALU.
+//   * No floating-point atomics.
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
