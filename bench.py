@@ -252,6 +252,23 @@ def cpu_baseline(layers_host, xs, seconds: float):
                       f"({nbytes} weight bytes, {dt:.1f} s, 1 thread)"}
 
 
+def gpu_clocks():
+    """The GPU's clock lines from `amd-smi metric --clock`, run as a child process after the
+    timed region (None when the tool is missing or refuses)."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock"], capture_output=True, text=True,
+                           timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    if r.returncode != 0:
+        return None
+    lines = [" ".join(x.split()) for x in r.stdout.splitlines()
+             if re.search(r"CLK|MHz|GFX|MEM", x)]
+    return lines[:24] or None
+
+
 def copy_probe(torch, mib: int):
     n = mib * (1 << 20) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -398,6 +415,8 @@ def main():
 
     cpu = cpu_baseline(layers[:4], xs, args.cpu_seconds)
     log(f"cpu oracle: {cpu['value']} GB/s ({cpu['sample']})")
+    clocks = gpu_clocks()
+    log("clocks: " + (" | ".join(clocks) if clocks else "amd-smi unavailable"))
 
     out = {
         "metric": METRIC,
@@ -434,6 +453,7 @@ def main():
                      "kernel": k_name, "bytes_per_launch": k_bytes,
                      "us_per_launch": round(k_s * 1e6, 3)},
         "cpu_baseline": cpu,
+        "gpu_clocks": clocks,
     }
     print(json.dumps(out), flush=True)
 

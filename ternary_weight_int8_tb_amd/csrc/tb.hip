@@ -66,10 +66,16 @@ constexpr int kRingDepthOne = TB_RING_DEPTH_ONE;   // one matrix
 #endif
 constexpr int kMfmaDepth = TB_MFMA_DEPTH;         // items in flight per wave (MFMA kernel)
 // M from which gate/up runs on the matrix cores. The MFMA kernel takes about the same time
-// for every M (22 µs for gate/up at the FFN shape, M = 4 or 8), the dot-product kernel
-// grows with M (18 µs at M = 4, 26 µs at M = 8); for the down GEMV, whose 20 rows per CU
-// fill only 20 of 32 MFMA rows, the dot-product kernel is as fast at M = 8.
+// for every M (21 µs for gate/up at the FFN shape, M = 4 or 8), the dot-product kernel
+// grows with M (18 µs at M = 4, 26 µs at M = 8).
 constexpr int kMfmaMinRows = TB_MFMA_MIN_ROWS;
+// The same for one matrix (tb_gemv_ternary, the down GEMV): at the FFN's down shape its 20
+// rows per CU fill 20 of 32 MFMA rows; measured 20.7 µs against 22.4 at M = 8, 21.0
+// against 19.4 at M = 6.
+#ifndef TB_MFMA_MIN_ROWS_ONE
+#define TB_MFMA_MIN_ROWS_ONE 8
+#endif
+constexpr int kMfmaMinRowsOne = TB_MFMA_MIN_ROWS_ONE;
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 enum Mode { kModeY = 0, kModeGateUp = 1, kModeIsum = 2 };
@@ -429,9 +435,11 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
 // v_mfma_i32_16x16x64_i8 takes them, and the VALU keeps the decode and the fold.
 //   * Workgroup c owns the rows of the same 4-row tiles [tA, tB) as in gemv_ring_kernel
 //     and covers them with 16-row tiles; rows past its range read zeros and are not written.
-//   * An item is one step (8 blocks) of one 16-row tile. Lane (i, g) = (lane % 16, lane / 16)
-//     loads 8 code bytes of row i per block: weights 32 g .. 32 g + 31 of the block. Their
-//     two decoded code words are the A operands of two MFMAs (16 weights per lane each);
+//   * An item is one step (8 blocks) of one 16-row tile and one matrix. Lane (i, g) =
+//     (lane % 16, lane / 16) loads 16 contiguous code bytes of row i per block pair (the 4
+//     lanes of a row read 64 bytes); v_permlane32_swap then trades two code words between
+//     the lane halves, so that for each block the four lane groups hold 32 of its weights
+//     each. Per block, two decoded code words are the A operands of two MFMAs;
 //     the B operands are the matching transposed 16-byte activation groups (column j =
 //     activation row j), so the two MFMAs leave the block's exact integer sums in D: lane
 //     l holds rows 4 (l / 16) + r, r = 0..3, of activation row l % 16. The activation is
@@ -487,9 +495,11 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
             ++gtile;
         }
     };
-    const uint32_t lane_off = (uint32_t)li * row_bytes + (uint32_t)lg * 8u;
+    // load q of a step: lane g reads bytes 64 q + 16 g .. + 15 of its row, i.e. half
+    // (g & 1) of block 2 q + (g >> 1)
+    const uint32_t lane_off = (uint32_t)li * row_bytes + (uint32_t)lg * 16u;
     const uint32_t lane_soff = ((uint32_t)li * (uint32_t)nb + (uint32_t)lg * 2u) * 2u;
-    u32x2 rc[kDepth][kBps];
+    uint4 rc[kDepth][kBps / 2];
     uint32_t rs[kDepth];
     int rit[kDepth];   // matrix << 30 | tile << 16 | step, or -1
     int pending = tid >> 6;
@@ -520,9 +530,8 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
         const __amdgpu_buffer_rsrc_t rcm = buffer_rsrc(mat ? a.codes1 : a.codes0, a.codes_bytes);
         const __amdgpu_buffer_rsrc_t rsm = buffer_rsrc(mat ? a.scales1 : a.scales0, a.scales_bytes);
 #pragma unroll
-        for (int kb = 0; kb < kBps; ++kb)
-            rc[d][kb] = __builtin_amdgcn_raw_buffer_load_b64(
-                rcm, kb < nbk ? off + (uint32_t)kb * 32u : kOutOfRange, so, 0);
+        for (int q = 0; q < kBps / 2; ++q)   // (nbk is even: a load's two blocks are both in)
+            rc[d][q] = buffer_load16_nt(rcm, 2 * q < nbk ? off + (uint32_t)q * 64u : kOutOfRange, so);
         rs[d] = buffer_load_u32(rsm, soff, sso);
     };
 
@@ -537,9 +546,18 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
     const int mB = li < M ? li : M - 1;   // activation row of this lane's B and D column
     auto consume = [&](int d) {
         const int mat = rit[d] >> 30, tile = (rit[d] >> 16) & 0x3fff, step = rit[d] & 0xffff;
-        // B: chunk 2 kb + (lg >> 1), code words 2 (lg & 1) and + 1, row mB
+        // The lane halves exchange code words so that each MFMA sees one block: after the
+        // swaps, words x, y of load q hold block 2 q and words z, w block 2 q + 1, lane
+        // group g covering weights 64 (g & 1) + 32 (g >> 1) + 0..15 (x, z) and + 16..31
+        // (y, w) of its block. B: chunk 2 kb + (lg & 1), code words 2 (lg >> 1) and + 1.
+#pragma unroll
+        for (int q = 0; q < kBps / 2; ++q) {
+            const u32x2 s0 = __builtin_amdgcn_permlane32_swap(rc[d][q].x, rc[d][q].z, false, false);
+            const u32x2 s1 = __builtin_amdgcn_permlane32_swap(rc[d][q].y, rc[d][q].w, false, false);
+            rc[d][q] = make_uint4(s0.x, s1.x, s0.y, s1.y);
+        }
         const uint8_t *sact = act + (size_t)step * L::kStepBytes +
-                              (((lg >> 1) * 4 + 2 * (lg & 1)) * M + mB) * 16;
+                              (((lg & 1) * 4 + 2 * (lg >> 1)) * M + mB) * 16;
         float t01[4], t23[4], tot[4];
 #pragma unroll
         for (int o = 0; o < kBps; ++o) {
@@ -549,8 +567,9 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
             const v4i b1 = *reinterpret_cast<const v4i *>(sact + kb * 2 * 4 * M * 16 + M * 16);
             const float dqv = dq_s[blk * M + mB];
             uint32_t w[8];
-            decode_ternary(rc[d][kb].x, w[0], w[1], w[2], w[3]);
-            decode_ternary(rc[d][kb].y, w[4], w[5], w[6], w[7]);
+            const uint4 cw = rc[d][kb >> 1];
+            decode_ternary((kb & 1) ? cw.z : cw.x, w[0], w[1], w[2], w[3]);
+            decode_ternary((kb & 1) ? cw.w : cw.y, w[4], w[5], w[6], w[7]);
             const v4i a0 = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
             const v4i a1 = {(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
             v4i acc = {0, 0, 0, 0};
@@ -750,7 +769,8 @@ GemvFn gemv_mfma_pick_m(int m)
     default: return nullptr;
     }
 }
-static_assert(kMfmaMinRows >= 6, "gemv_mfma_kernel is instantiated for M = 6 .. 8");
+static_assert(kMfmaMinRows >= 6 && kMfmaMinRowsOne >= 6,
+              "gemv_mfma_kernel is instantiated for M = 6 .. 8");
 
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
@@ -873,12 +893,14 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
 
     // batched ternary rows: the matrix-core kernel, when its LDS plan fits (it needs an
     // even number of blocks per row: a lane's scale word holds a block pair)
-    if (w0->fmt == TB_FMT_TERNARY2 && mode == kModeGateUp && m >= kMfmaMinRows && nb % 2 == 0) {
+    if (w0->fmt == TB_FMT_TERNARY2 && nb % 2 == 0 &&
+        ((mode == kModeGateUp && m >= kMfmaMinRows) || (mode == kModeY && m >= kMfmaMinRowsOne))) {
         const size_t rows_cu = (size_t)((tiles + ring_grid - 1) / ring_grid) * kRowsPerWave;
         const size_t mfma_lds = (size_t)steps * step_bytes + (size_t)m * (nb + 8) * 4 + 16 +
                                 rows_cu * steps * m * (mode == kModeGateUp ? 2 : 1) * 4;
         if (mfma_lds <= (size_t)info.lds_limit) {
-            GemvFn fn = gemv_mfma_pick_m<kModeGateUp>(m);
+            GemvFn fn = mode == kModeGateUp ? gemv_mfma_pick_m<kModeGateUp>(m)
+                                            : gemv_mfma_pick_m<kModeY>(m);
             if (!fn)
                 return TB_EINVAL;
             if ((rc = set_lds(fn, mfma_lds)))

@@ -129,10 +129,10 @@ def test_sliced_and_streaming_kernels_fold_alike(o, fmt):
 
 @pytest.mark.parametrize("n,k", [(100, 1280), (2180, 1280), (1152, 5120)])
 def test_matrix_core_and_dot_kernels_fold_alike(o, n, k):
-    # Ternary gate/up from M = 6 on runs on the matrix cores (16-row tiles, rows past a
-    # CU's range masked; k = 1280 has a ragged second step of 2 blocks); a row alone runs on
-    # the dot-product kernel. Both fold every row in the same order, so the batched rows
-    # must equal the rows alone bit for bit.
+    # Ternary gate/up from M = 6 on, and a single ternary GEMV at M = 8, run on the matrix
+    # cores (16-row tiles, rows past a CU's range masked; k = 1280 has a ragged second
+    # step of 2 blocks); a row alone runs on the dot-product kernel. Both fold every row in
+    # the same order, so the batched rows must equal the rows alone bit for bit.
     say(f"matrix-core vs dot-product gate/up n={n} k={k}")
     wg = synth.matrix(TERN, n, k, 13, 0, synth.T_GATE)
     wu = synth.matrix(TERN, n, k, 13, 0, synth.T_UP)
@@ -153,6 +153,12 @@ def test_matrix_core_and_dot_kernels_fold_alike(o, n, k):
     r = o.gateup_silu(wg, wu, q, dq)
     tol = bounds.h_tolerance(r["g"], r["u"], r["sg"], r["su"])
     assert np.all(np.abs(h.astype(np.float64) - r["h"]) <= tol)
+    # one matrix (tb_gemv_ternary, the down GEMV's kernel) runs on the matrix cores at M = 8
+    y8 = gu.gemv(dg, q, dq)
+    for row in range(8):
+        assert gu.gemv(dg, q[row:row + 1], dq[row:row + 1])[0].tobytes() == y8[row].tobytes(), row
+    yo, sabs = o.gemv(wg, q, dq)
+    assert bounds.gemv_ok(y8, yo, sabs)[0]
 
 
 def test_code3_and_zero_cases(o):
