@@ -153,7 +153,7 @@ __device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act
         int m, g;
         split(unit, m, g);
         if constexpr (MFMA_LAYOUT)
-            stage_unit_store_mfma<M>(u, act, m, g);
+            stage_unit_store_mfma<M, FMT>(u, act, m, g);
         else
             stage_unit_store_step<M, FMT>(u, act, m, g);
         if (FMT == TB_FMT_SIGN1) {
@@ -429,17 +429,23 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     }
 }
 
+// Threads per workgroup of gemv_mfma_kernel: 16 waves for ternary; 8 for sign, whose
+// 16-block steps need more than the 128 registers a wave has at 16 waves per CU.
+__host__ __device__ constexpr int mfma_threads(int fmt) { return fmt == TB_FMT_TERNARY2 ? 1024 : 512; }
+
 // ------------------------------------------------------------------------------------
-// Batched streaming GEMV on the matrix cores: ternary weights, M >= kMfmaMinRows rows.
+// Batched streaming GEMV on the matrix cores (ternary and sign weights, M >= 6 rows).
 // With M rows the dot products cost M VALU instructions per 4 weights and lane; here
 // v_mfma_i32_16x16x64_i8 takes them, and the VALU keeps the decode and the fold.
 //   * Workgroup c owns the rows of the same 4-row tiles [tA, tB) as in gemv_ring_kernel
 //     and covers them with 16-row tiles; rows past its range read zeros and are not written.
-//   * An item is one step (8 blocks) of one 16-row tile and one matrix. Lane (i, g) =
-//     (lane % 16, lane / 16) loads 16 contiguous code bytes of row i per block pair (the 4
-//     lanes of a row read 64 bytes); v_permlane32_swap then trades two code words between
-//     the lane halves, so that for each block the four lane groups hold 32 of its weights
-//     each. Per block, two decoded code words are the A operands of two MFMAs;
+//   * An item is one step (256 code bytes per row: 8 ternary or 16 sign blocks) of one
+//     16-row tile and one matrix. Lane (i, g) = (lane % 16, lane / 16) loads 16 contiguous
+//     code bytes of row i per load (the 4 lanes of a row read 64 bytes); lane swaps
+//     (v_permlane32_swap, and for sign v_permlane16_swap) then trade code words between
+//     the lane groups, so that for each block the four groups hold 32 of its weights each.
+//     Per block, two decoded 16-byte groups (ternary: two code words; sign: 0/1 bytes of
+//     one 32-bit word, isum = 2 D - sum(q)) are the A operands of two MFMAs;
 //     the B operands are the matching transposed 16-byte activation groups (column j =
 //     activation row j), so the two MFMAs leave the block's exact integer sums in D: lane
 //     l holds rows 4 (l / 16) + r, r = 0..3, of activation row l % 16. The activation is
@@ -452,22 +458,27 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
 //     so lane 0 of a row ends with ((t0 + t7) + (t6 + t5)) + ((t4 + t3) + (t2 + t1)) over
 //     the block terms t), so every row is bit-identical to the row computed alone.
 //   * A block's scales reach the fold lanes with ds_bpermute from the lanes that loaded
-//     them (one 32-bit word: the block pair 2 g, 2 g + 1 of row i; nb must be even).
+//     them (the blocks of row i that the lane's code load covers; nb must be a multiple
+//     of 2 (ternary) or 4 (sign)).
+//   * Sign runs 8 waves per CU: its 16-block steps need more than the 128 registers a
+//     wave has at 16.
 // ------------------------------------------------------------------------------------
-template <int M, int MODE>
-__global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
+template <int M, int FMT, int MODE>
+__global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
-    constexpr int FMT = TB_FMT_TERNARY2;
     using L = StepLayout<M, FMT>;
+    constexpr bool kTern = FMT == TB_FMT_TERNARY2;
     constexpr bool kTwo = MODE == kModeGateUp;
     constexpr int kParts = kTwo ? 2 : 1;
     constexpr int kMatShift = kTwo ? 1 : 0;   // gate/up: item = ((tile, step), matrix)
-    constexpr int kBps = 8;   // blocks per step
+    constexpr int kBps = kTern ? 8 : 16;      // blocks per step (256 code bytes per row)
+    constexpr int kBpl = kBps / 4;            // blocks per 16-byte load of the 4 lanes of a row
     constexpr int kDepth = kMfmaDepth;
+    constexpr int kThreads = mfma_threads(FMT), kWaves = kThreads / 64;
 
     const int k = a.k, n = a.n, nb = k / kBlock;
-    const int C = k / 64, I = (C + kChunkLanes - 1) / kChunkLanes;
+    const int C = k / Fmt<FMT>::kWeightsPerChunk, I = (C + kChunkLanes - 1) / kChunkLanes;
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
     const int G = gridDim.x, c = blockIdx.x;
     const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
@@ -478,11 +489,15 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
 
     uint8_t *act = lds;
     float *dq_s = reinterpret_cast<float *>(lds + (size_t)I * L::kStepBytes);
-    int *ctr_s = reinterpret_cast<int *>(dq_s + (size_t)(nb + kBps) * M);
+    int *qsum_s = reinterpret_cast<int *>(dq_s + (size_t)(nb + kBps) * M);
+    int *ctr_s = qsum_s + (kTern ? 0 : (nb + kBps) * M);
     float *part_s = reinterpret_cast<float *>(ctr_s + 4);   // [row - R0][step][m][part]
 
     if (tid == 0)
-        *ctr_s = kRingWaves;   // wave w starts with item w
+        *ctr_s = kWaves;   // wave w starts with item w
+    if (!kTern)
+        for (int i = tid; i < (nb + kBps) * M; i += kThreads)
+            qsum_s[i] = 0;
     __syncthreads();
 
     // ---- issue side: as in gemv_ring_kernel, with a per-lane and a wave-uniform offset
@@ -495,12 +510,13 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
             ++gtile;
         }
     };
-    // load q of a step: lane g reads bytes 64 q + 16 g .. + 15 of its row, i.e. half
-    // (g & 1) of block 2 q + (g >> 1)
+    // Load q of a step: lane g reads bytes 64 q + 16 g .. + 15 of its row: half g & 1 of
+    // block 2 q + (g >> 1) (ternary) or all of block 4 q + g (sign). Its scale load is the
+    // word (ternary) or the two words (sign) holding the scales of blocks kBpl g .. of row i.
     const uint32_t lane_off = (uint32_t)li * row_bytes + (uint32_t)lg * 16u;
-    const uint32_t lane_soff = ((uint32_t)li * (uint32_t)nb + (uint32_t)lg * 2u) * 2u;
-    uint4 rc[kDepth][kBps / 2];
-    uint32_t rs[kDepth];
+    const uint32_t lane_soff = ((uint32_t)li * (uint32_t)nb + (uint32_t)(lg * kBpl)) * 2u;
+    uint4 rc[kDepth][4];
+    u32x2 rs[kDepth];
     int rit[kDepth];   // matrix << 30 | tile << 16 | step, or -1
     int pending = tid >> 6;
     auto issue = [&](int d) {
@@ -518,7 +534,7 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
             nbk = min(kBps, nb - gstep * kBps);   // blocks of this step inside the row
             if (row0 + li < R1) {
                 off = lane_off;
-                soff = gstep * kBps + 2 * lg < nb ? lane_soff : kOutOfRange;
+                soff = gstep * kBps + lg * kBpl < nb ? lane_soff : kOutOfRange;
             }
             int v = 0;
             if (lane == 0)
@@ -529,13 +545,19 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
         // would live in scratch)
         const __amdgpu_buffer_rsrc_t rcm = buffer_rsrc(mat ? a.codes1 : a.codes0, a.codes_bytes);
         const __amdgpu_buffer_rsrc_t rsm = buffer_rsrc(mat ? a.scales1 : a.scales0, a.scales_bytes);
+        // (nbk is a multiple of kBpl: the blocks of one load are all in or all out)
 #pragma unroll
-        for (int q = 0; q < kBps / 2; ++q)   // (nbk is even: a load's two blocks are both in)
-            rc[d][q] = buffer_load16_nt(rcm, 2 * q < nbk ? off + (uint32_t)q * 64u : kOutOfRange, so);
-        rs[d] = buffer_load_u32(rsm, soff, sso);
+        for (int q = 0; q < 4; ++q)
+            rc[d][q] = buffer_load16_nt(rcm, q * kBpl < nbk ? off + (uint32_t)q * 64u : kOutOfRange, so);
+        if (kTern) {
+            rs[d].x = buffer_load_u32(rsm, soff, sso);
+            rs[d].y = 0u;
+        } else {
+            rs[d] = __builtin_amdgcn_raw_buffer_load_b64(rsm, soff, sso, 0);
+        }
     };
 
-    stage_activation<M, FMT, MODE, kRingThreads, true>(a, act, dq_s, nullptr, [&]() {
+    stage_activation<M, FMT, MODE, kThreads, true>(a, act, dq_s, qsum_s, [&]() {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
             issue(d);
@@ -546,52 +568,94 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
     const int mB = li < M ? li : M - 1;   // activation row of this lane's B and D column
     auto consume = [&](int d) {
         const int mat = rit[d] >> 30, tile = (rit[d] >> 16) & 0x3fff, step = rit[d] & 0xffff;
-        // The lane halves exchange code words so that each MFMA sees one block: after the
-        // swaps, words x, y of load q hold block 2 q and words z, w block 2 q + 1, lane
-        // group g covering weights 64 (g & 1) + 32 (g >> 1) + 0..15 (x, z) and + 16..31
-        // (y, w) of its block. B: chunk 2 kb + (lg & 1), code words 2 (lg >> 1) and + 1.
+        // The lane groups exchange code words so that each MFMA sees one block.
+        //   ternary: after one swap between the lane halves, words x, y of load q hold block
+        //   2 q and z, w block 2 q + 1; group g covers weights 64 (g & 1) + 32 (g >> 1) + 0..15
+        //   (x, z) and + 16..31 (y, w). B: chunk 2 kb + (g & 1), code words 2 (g >> 1), + 1.
+        //   sign: a 4 x 4 transpose of dwords over the lane groups (a swap between the halves,
+        //   then between the 16-lane rows): word t of load q holds dword g (weights
+        //   32 g .. 32 g + 31) of block 4 q + t. B: chunk kb, dword g, halves 0 and 1.
 #pragma unroll
-        for (int q = 0; q < kBps / 2; ++q) {
-            const u32x2 s0 = __builtin_amdgcn_permlane32_swap(rc[d][q].x, rc[d][q].z, false, false);
-            const u32x2 s1 = __builtin_amdgcn_permlane32_swap(rc[d][q].y, rc[d][q].w, false, false);
-            rc[d][q] = make_uint4(s0.x, s1.x, s0.y, s1.y);
+        for (int q = 0; q < 4; ++q) {
+            if (kTern) {
+                const u32x2 s0 = __builtin_amdgcn_permlane32_swap(rc[d][q].x, rc[d][q].z, false, false);
+                const u32x2 s1 = __builtin_amdgcn_permlane32_swap(rc[d][q].y, rc[d][q].w, false, false);
+                rc[d][q] = make_uint4(s0.x, s1.x, s0.y, s1.y);
+            } else {
+                const u32x2 s0 = __builtin_amdgcn_permlane32_swap(rc[d][q].x, rc[d][q].z, false, false);
+                const u32x2 s1 = __builtin_amdgcn_permlane32_swap(rc[d][q].y, rc[d][q].w, false, false);
+                const u32x2 t0 = __builtin_amdgcn_permlane16_swap(s0.x, s1.x, false, false);
+                const u32x2 t1 = __builtin_amdgcn_permlane16_swap(s0.y, s1.y, false, false);
+                rc[d][q] = make_uint4(t0.x, t0.y, t1.x, t1.y);
+            }
         }
         const uint8_t *sact = act + (size_t)step * L::kStepBytes +
-                              (((lg & 1) * 4 + 2 * (lg >> 1)) * M + mB) * 16;
-        float t01[4], t23[4], tot[4];
+                              (kTern ? (((lg & 1) * 4 + 2 * (lg >> 1)) * M + mB) * 16
+                                     : ((2 * lg) * M + mB) * 16);
+        // The step tree in the order row_tree produces (each level adds lane L - off), taken
+        // as a balanced tree over the blocks in the order 0, kBps - 1, .., 1:
+        // ((t0 + t7) + (t6 + t5)) + ((t4 + t3) + (t2 + t1)) for ternary, the same over 16
+        // blocks for sign. lv holds the pending left subtrees per level.
+        float lv[4][4], tot[4];
+        // byte address of this lane's row group for ds_bpermute, made opaque here so the
+        // compiler forms the per-block addresses in the loop instead of keeping all of them
+        // live across it (which spills)
+        int pbase = 16 * lg;
+        asm volatile("" : "+v"(pbase));
 #pragma unroll
         for (int o = 0; o < kBps; ++o) {
-            const int kb = o == 0 ? 0 : kBps - o;   // tree order 0, 7, 6, 5, 4, 3, 2, 1
+            const int kb = o == 0 ? 0 : kBps - o;
             const int blk = step * kBps + kb;
-            const v4i b0 = *reinterpret_cast<const v4i *>(sact + kb * 2 * 4 * M * 16);
-            const v4i b1 = *reinterpret_cast<const v4i *>(sact + kb * 2 * 4 * M * 16 + M * 16);
+            const uint8_t *bp = sact + kb * (kTern ? 2 * 4 : 8) * M * 16;
+            const v4i b0 = *reinterpret_cast<const v4i *>(bp);
+            const v4i b1 = *reinterpret_cast<const v4i *>(bp + M * 16);
             const float dqv = dq_s[blk * M + mB];
             uint32_t w[8];
-            const uint4 cw = rc[d][kb >> 1];
-            decode_ternary((kb & 1) ? cw.z : cw.x, w[0], w[1], w[2], w[3]);
-            decode_ternary((kb & 1) ? cw.w : cw.y, w[4], w[5], w[6], w[7]);
+            if (kTern) {
+                const uint4 cw = rc[d][kb >> 1];
+                decode_ternary((kb & 1) ? cw.z : cw.x, w[0], w[1], w[2], w[3]);
+                decode_ternary((kb & 1) ? cw.w : cw.y, w[4], w[5], w[6], w[7]);
+            } else {
+                const uint4 cw = rc[d][kb >> 2];
+                const uint32_t dw = (kb & 3) == 0 ? cw.x : (kb & 3) == 1 ? cw.y : (kb & 3) == 2 ? cw.z : cw.w;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    w[j] = (dw >> j) & 0x01010101u;
+            }
             const v4i a0 = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
             const v4i a1 = {(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
             v4i acc = {0, 0, 0, 0};
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
+            const int qs = kTern ? 0 : qsum_s[blk * M + mB];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                // the scale word of row 4 lg + r, blocks (kb & ~1, kb | 1) of the step
+                // the scale of row 4 lg + r and block kb, from the lane that loaded it
+                const uint32_t word = (kTern || ((kb >> 1) & 1) == 0) ? rs[d].x : rs[d].y;
                 const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(
-                    (16 * (kb >> 1) + 4 * lg + r) * 4, (int)rs[d]);
+                    pbase + (16 * (kb / kBpl) + r) * 4, (int)word);
                 const float sv = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(sw, (kb & 1) * 16, 16));
-                const float t = (sv * dqv) * (float)acc[r];
-                // ((t0 + t7) + (t6 + t5)) + ((t4 + t3) + (t2 + t1))
-                if (o == 0 || o == 2 || o == 4 || o == 6)
-                    t01[r] = t;
-                else if (o == 1 || o == 5)
-                    t23[r] = t01[r] + t;
-                else if (o == 3)
-                    tot[r] = t23[r] + (t01[r] + t);
-                else
-                    tot[r] = tot[r] + (t23[r] + (t01[r] + t));
+                const int isum = kTern ? acc[r] : 2 * acc[r] - qs;
+                float v = (sv * dqv) * (float)isum;
+                bool done = false;
+#pragma unroll
+                for (int l = 0; l < 4; ++l) {
+                    if (!done) {
+                        if ((o >> l) & 1) {
+                            v = lv[r][l] + v;
+                        } else {
+                            lv[r][l] = v;
+                            done = true;
+                        }
+                    }
+                }
+                if (o == kBps - 1)
+                    tot[r] = v;
             }
+            // sign: one block at a time (hoisting the LDS reads of the 16 blocks of a step
+            // spills)
+            if (!kTern)
+                __builtin_amdgcn_sched_barrier(0);
         }
         if (li < M) {
 #pragma unroll
@@ -619,7 +683,7 @@ __global__ __launch_bounds__(kRingThreads) void gemv_mfma_kernel(GemvArgs a)
 
     // ---- every row: its step partials in step order, from +0
     __syncthreads();
-    for (int i = tid; i < (R1 - R0) * M; i += kRingThreads) {
+    for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
         const int lrow = i / M, m = i % M;
         const float *ps = part_s + ((size_t)lrow * I * M + m) * kParts;
         float g = 0.0f, u = 0.0f;
@@ -759,13 +823,13 @@ using GemvFn = void (*)(GemvArgs);
 TB_KERNEL_TABLE(gemv_ring_kernel)
 TB_KERNEL_TABLE(gemv_sliced_kernel)
 
-template <int MODE>
+template <int FMT, int MODE>
 GemvFn gemv_mfma_pick_m(int m)
 {
     switch (m) {
-    case 6: return gemv_mfma_kernel<6, MODE>;
-    case 7: return gemv_mfma_kernel<7, MODE>;
-    case 8: return gemv_mfma_kernel<8, MODE>;
+    case 6: return gemv_mfma_kernel<6, FMT, MODE>;
+    case 7: return gemv_mfma_kernel<7, FMT, MODE>;
+    case 8: return gemv_mfma_kernel<8, FMT, MODE>;
     default: return nullptr;
     }
 }
@@ -891,21 +955,25 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     const int steps = (C + kChunkLanes - 1) / kChunkLanes;
     const size_t step_bytes = (size_t)(w0->fmt == TB_FMT_TERNARY2 ? 1024 : 2048) * m;
 
-    // batched ternary rows: the matrix-core kernel, when its LDS plan fits (it needs an
-    // even number of blocks per row: a lane's scale word holds a block pair)
-    if (w0->fmt == TB_FMT_TERNARY2 && nb % 2 == 0 &&
+    // batched rows: the matrix-core kernel, when its LDS plan fits (a lane's scale load
+    // holds whole block pairs (ternary) or quads (sign) of one row)
+    const bool tern = w0->fmt == TB_FMT_TERNARY2;
+    if (nb % (tern ? 2 : 4) == 0 &&
         ((mode == kModeGateUp && m >= kMfmaMinRows) || (mode == kModeY && m >= kMfmaMinRowsOne))) {
         const size_t rows_cu = (size_t)((tiles + ring_grid - 1) / ring_grid) * kRowsPerWave;
-        const size_t mfma_lds = (size_t)steps * step_bytes + (size_t)m * (nb + 8) * 4 + 16 +
-                                rows_cu * steps * m * (mode == kModeGateUp ? 2 : 1) * 4;
+        const size_t bps = tern ? 8 : 16;
+        const size_t mfma_lds = (size_t)steps * step_bytes + (size_t)m * (nb + bps) * 4 * (tern ? 1 : 2) +
+                                16 + rows_cu * steps * m * (mode == kModeGateUp ? 2 : 1) * 4;
         if (mfma_lds <= (size_t)info.lds_limit) {
-            GemvFn fn = mode == kModeGateUp ? gemv_mfma_pick_m<kModeGateUp>(m)
-                                            : gemv_mfma_pick_m<kModeY>(m);
+            GemvFn fn = tern ? (mode == kModeGateUp ? gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
+                                                    : gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeY>(m))
+                             : (mode == kModeGateUp ? gemv_mfma_pick_m<TB_FMT_SIGN1, kModeGateUp>(m)
+                                                    : gemv_mfma_pick_m<TB_FMT_SIGN1, kModeY>(m));
             if (!fn)
                 return TB_EINVAL;
             if ((rc = set_lds(fn, mfma_lds)))
                 return rc;
-            hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(kRingThreads), mfma_lds, stream, a);
+            hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(mfma_threads(w0->fmt)), mfma_lds, stream, a);
             return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
         }
     }

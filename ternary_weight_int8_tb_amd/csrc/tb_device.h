@@ -430,23 +430,34 @@ __device__ __forceinline__ void stage_unit_store_step(const StageUnit<FMT> &u, u
     }
 }
 
-// The same 16-byte groups in the layout of the matrix-core kernel (ternary): per step
-// [chunk (16)][code word (4)][row m (M)], so that the 16 lanes of an MFMA B operand, which
-// hold the M rows of one group, read consecutive 16-byte slots (no bank conflicts).
-template <int M>
-__device__ __forceinline__ void stage_unit_store_mfma(const StageUnit<TB_FMT_TERNARY2> &u, uint8_t *act,
-                                                      int m, int g)
+// The same 16-byte groups in the layout of the matrix-core kernel, staged in slot order:
+// unit (g, m) with g = 4 c + j (chunk c, part j) goes to slot g * M + m (ternary: one
+// 16-byte group), or to slots (2 g + h) * M + m, h = 0, 1 (sign: its two groups). Per step
+// that is [chunk][code word][row m] (ternary) or [chunk][dword][half][row m] (sign), so
+// the 16 lanes of an MFMA B operand, which hold the M rows of one group, read consecutive
+// 16-byte slots (no bank conflicts).
+template <int M, int FMT>
+__device__ __forceinline__ void stage_unit_store_mfma(const StageUnit<FMT> &u, uint8_t *act, int m,
+                                                      int g)
 {
-    using L = StepLayout<M, TB_FMT_TERNARY2>;
-    const int c = g >> 2, j = g & 3;
-    const uint4 r = u.lo;
-    uint4 o;
-    o.x = byte_at(r.x, 0) | byte_at(r.y, 0) << 8 | byte_at(r.z, 0) << 16 | byte_at(r.w, 0) << 24;
-    o.y = byte_at(r.x, 1) | byte_at(r.y, 1) << 8 | byte_at(r.z, 1) << 16 | byte_at(r.w, 1) << 24;
-    o.z = byte_at(r.x, 2) | byte_at(r.y, 2) << 8 | byte_at(r.z, 2) << 16 | byte_at(r.w, 2) << 24;
-    o.w = byte_at(r.x, 3) | byte_at(r.y, 3) << 8 | byte_at(r.z, 3) << 16 | byte_at(r.w, 3) << 24;
-    *reinterpret_cast<uint4 *>(act + (size_t)(c >> 4) * L::kStepBytes +
-                               ((((c & 15) * 4 + j) * M + m) * 16)) = o;
+    if (FMT == TB_FMT_TERNARY2) {
+        const uint4 r = u.lo;
+        uint4 o;
+        o.x = byte_at(r.x, 0) | byte_at(r.y, 0) << 8 | byte_at(r.z, 0) << 16 | byte_at(r.w, 0) << 24;
+        o.y = byte_at(r.x, 1) | byte_at(r.y, 1) << 8 | byte_at(r.z, 1) << 16 | byte_at(r.w, 1) << 24;
+        o.z = byte_at(r.x, 2) | byte_at(r.y, 2) << 8 | byte_at(r.z, 2) << 16 | byte_at(r.w, 2) << 24;
+        o.w = byte_at(r.x, 3) | byte_at(r.y, 3) << 8 | byte_at(r.z, 3) << 16 | byte_at(r.w, 3) << 24;
+        *reinterpret_cast<uint4 *>(act + ((size_t)g * M + m) * 16) = o;
+    } else {
+        const uint32_t r[8] = {u.lo.x, u.lo.y, u.lo.z, u.lo.w, u.hi.x, u.hi.y, u.hi.z, u.hi.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            o[i] = byte_at(r[0 + (i >> 2)], i & 3) | byte_at(r[2 + (i >> 2)], i & 3) << 8 |
+                   byte_at(r[4 + (i >> 2)], i & 3) << 16 | byte_at(r[6 + (i >> 2)], i & 3) << 24;
+        *reinterpret_cast<uint4 *>(act + ((size_t)(2 * g) * M + m) * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(act + ((size_t)(2 * g + 1) * M + m) * 16) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
 }
 
 // One rotated-quantised block into the step-major layout. The 16-lane group holds block b

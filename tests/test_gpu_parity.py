@@ -127,15 +127,16 @@ def test_sliced_and_streaming_kernels_fold_alike(o, fmt):
         assert y1[0].tobytes() == y8[r].tobytes(), r
 
 
-@pytest.mark.parametrize("n,k", [(100, 1280), (2180, 1280), (1152, 5120)])
-def test_matrix_core_and_dot_kernels_fold_alike(o, n, k):
-    # Ternary gate/up from M = 6 on, and a single ternary GEMV at M = 8, run on the matrix
-    # cores (16-row tiles, rows past a CU's range masked; k = 1280 has a ragged second
-    # step of 2 blocks); a row alone runs on the dot-product kernel. Both fold every row in
+@pytest.mark.parametrize("fmt,n,k", [(TERN, 100, 1280), (TERN, 2180, 1280), (TERN, 1152, 5120),
+                                     (SIGN, 100, 1536), (SIGN, 2180, 1536), (SIGN, 1152, 5120)])
+def test_matrix_core_and_dot_kernels_fold_alike(o, fmt, n, k):
+    # Gate/up from M = 6 on, and a single GEMV at M = 8, run on the matrix cores (16-row
+    # tiles, rows past a CU's range masked; the k = 1280 ternary and k = 1536 sign rows end
+    # in a ragged step); a row alone runs on the dot-product kernel. Both fold every row in
     # the same order, so the batched rows must equal the rows alone bit for bit.
-    say(f"matrix-core vs dot-product gate/up n={n} k={k}")
-    wg = synth.matrix(TERN, n, k, 13, 0, synth.T_GATE)
-    wu = synth.matrix(TERN, n, k, 13, 0, synth.T_UP)
+    say(f"matrix-core vs dot-product fmt={fmt} n={n} k={k}")
+    wg = synth.matrix(fmt, n, k, 13, 0, synth.T_GATE)
+    wu = synth.matrix(fmt, n, k, 13, 0, synth.T_UP)
     dg, du = tb.Matrix.upload(wg), tb.Matrix.upload(wu)
 
     def gateup(qm, dqm):
