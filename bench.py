@@ -252,21 +252,34 @@ def cpu_baseline(layers_host, xs, seconds: float):
                       f"({nbytes} weight bytes, {dt:.1f} s, 1 thread)"}
 
 
-def gpu_clocks():
+def gpu_clocks(torch, work=None):
     """The GPU's clock lines from `amd-smi metric --clock`, run as a child process after the
-    timed region (None when the tool is missing or refuses)."""
+    timed region; while it runs, `work` (the M=1 stream step) is replayed so the reading is
+    taken under load. None when the tool is missing or refuses."""
     import re
     import subprocess
     try:
-        r = subprocess.run(["amd-smi", "metric", "--clock"], capture_output=True, text=True,
-                           timeout=30)
-    except (OSError, subprocess.SubprocessError):
+        proc = subprocess.Popen(["amd-smi", "metric", "--clock"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
         return None
-    if r.returncode != 0:
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < 30:
+        if work is not None:
+            for _ in range(4):
+                work()
+            torch.cuda.synchronize()
+        else:
+            time.sleep(0.05)
+    try:
+        out, _ = proc.communicate(timeout=5)
+    except subprocess.SubprocessError:
+        proc.kill()
         return None
-    lines = [" ".join(x.split()) for x in r.stdout.splitlines()
-             if re.search(r"CLK|MHz|GFX|MEM", x)]
-    return lines[:24] or None
+    if proc.returncode != 0:
+        return None
+    lines = [" ".join(x.split()) for x in out.splitlines() if re.search(r"GFX_\d|CLK:|MEM", x)]
+    return lines[:16] or None
 
 
 def copy_probe(torch, mib: int):
@@ -415,8 +428,8 @@ def main():
 
     cpu = cpu_baseline(layers[:4], xs, args.cpu_seconds)
     log(f"cpu oracle: {cpu['value']} GB/s ({cpu['sample']})")
-    clocks = gpu_clocks()
-    log("clocks: " + (" | ".join(clocks) if clocks else "amd-smi unavailable"))
+    clocks = gpu_clocks(torch, s1.step)
+    log("clocks (under the M=1 stream): " + (" | ".join(clocks) if clocks else "amd-smi unavailable"))
 
     out = {
         "metric": METRIC,

@@ -120,7 +120,8 @@ def main():
                      f"{r['max_us']:.2f} | {r['pct']:.1f} |")
     lines += ["", "Template arguments: gemv_ring_kernel<M, FMT, MODE>, FMT 0 = ternary, 1 = sign; "
               "MODE 0 = single GEMV (down), 1 = gate/up + SiLU, 2 = block-sum export. "
-              "gemv_mfma_kernel<M, MODE> is ternary gate/up on the matrix cores (M >= 6). "
+              "gemv_mfma_kernel<M, FMT, MODE> runs on the matrix cores (gate/up for M >= 6, "
+              "a single GEMV at M = 8). "
               "ffn_layers_kernel<M, FMT> is one tb_ffn_layers launch of up to 32 whole layers. "
               "stream_read_kernel is the 4 GiB read probe."]
     if bench:
