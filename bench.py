@@ -373,6 +373,8 @@ def main():
         k_key = "gemv_ring_kernel<1, 0, 1>"
     k_gbs = k_bytes / k_s / 1e9
     log(f"dominant kernel {k_name}: {k_s * 1e6:.2f} us/launch, {k_gbs:.1f} GB/s")
+    clocks = gpu_clocks(torch, s1.step)
+    log("clocks (under the M=1 stream): " + (" | ".join(clocks) if clocks else "amd-smi unavailable"))
     del f1, s1
 
     res_m8 = None
@@ -428,8 +430,6 @@ def main():
 
     cpu = cpu_baseline(layers[:4], xs, args.cpu_seconds)
     log(f"cpu oracle: {cpu['value']} GB/s ({cpu['sample']})")
-    clocks = gpu_clocks(torch, s1.step)
-    log("clocks (under the M=1 stream): " + (" | ".join(clocks) if clocks else "amd-smi unavailable"))
 
     out = {
         "metric": METRIC,
@@ -466,7 +466,7 @@ def main():
                      "kernel": k_name, "bytes_per_launch": k_bytes,
                      "us_per_launch": round(k_s * 1e6, 3)},
         "cpu_baseline": cpu,
-        "gpu_clocks": clocks,
+        "gpu_clocks_amd_smi": clocks,
     }
     print(json.dumps(out), flush=True)
 

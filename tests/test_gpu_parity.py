@@ -127,8 +127,9 @@ def test_sliced_and_streaming_kernels_fold_alike(o, fmt):
         assert y1[0].tobytes() == y8[r].tobytes(), r
 
 
-@pytest.mark.parametrize("fmt,n,k", [(TERN, 100, 1280), (TERN, 2180, 1280), (TERN, 1152, 5120),
-                                     (SIGN, 100, 1536), (SIGN, 2180, 1536), (SIGN, 1152, 5120)])
+@pytest.mark.parametrize("fmt,n,k", [(TERN, 1, 256), (TERN, 100, 1280), (TERN, 2180, 1280),
+                                     (TERN, 1152, 5120), (SIGN, 3, 512), (SIGN, 100, 1536),
+                                     (SIGN, 2180, 1536), (SIGN, 1152, 5120)])
 def test_matrix_core_and_dot_kernels_fold_alike(o, fmt, n, k):
     # Gate/up from M = 6 on, and a single GEMV at M = 8, run on the matrix cores (16-row
     # tiles, rows past a CU's range masked; the k = 1280 ternary and k = 1536 sign rows end
