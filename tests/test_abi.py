@@ -174,3 +174,18 @@ def test_ffn_layers_validation(L):
     assert call(a=bad) == tb.TB_EINVAL
     bad = (tb.CFfnWeights * 2)(weights(0), weights(1, k_down=256))  # down does not match
     assert call(a=bad) == tb.TB_EINVAL
+
+
+def test_valid_calls_without_a_device_return_ehip(L):
+    # With no GPU present a valid call must fail with TB_EHIP, not crash. Where a device
+    # exists the fake addresses would reach a kernel, so the test only runs without one.
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present")
+    w, w2 = mat(), mat(codes=ALIGNED + 0x100000, scales=ALIGNED2 + 0x100000)
+    y = ALIGNED4 + 0x100000
+    assert rq(L) == tb.TB_EHIP
+    assert L.tb_gemv_ternary(ctypes.byref(w), ALIGNED3, ALIGNED4, 1, y, None) == tb.TB_EHIP
+    assert L.tb_ffn_gateup_silu(ctypes.byref(w), ctypes.byref(w2), ALIGNED3, ALIGNED4, 1, y,
+                                None) == tb.TB_EHIP
+    assert L.tb_gemv_block_sums(ctypes.byref(w), ALIGNED3, 1, ALIGNED4, None) == tb.TB_EHIP
