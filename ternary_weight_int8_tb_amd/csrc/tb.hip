@@ -548,7 +548,7 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
         // (nbk is a multiple of kBpl: the blocks of one load are all in or all out)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            rc[d][q] = buffer_load16_nt(rcm, q * kBpl < nbk ? off + (uint32_t)q * 64u : kOutOfRange, so);
+            rc[d][q] = buffer_load16(rcm, q * kBpl < nbk ? off + (uint32_t)q * 64u : kOutOfRange, so);
         if (kTern) {
             rs[d].x = buffer_load_u32(rsm, soff, sso);
             rs[d].y = 0u;

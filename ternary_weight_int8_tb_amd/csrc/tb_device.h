@@ -87,6 +87,14 @@ __device__ __forceinline__ uint4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same without the non-temporal hint: for reads whose cache line is read again by a
+// neighbouring load (the matrix-core kernel reads each 128-byte line in two halves).
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, int soffset)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soffset, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint16_t buffer_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
