@@ -449,14 +449,17 @@ __host__ __device__ constexpr int mfma_threads(int fmt) { return fmt == TB_FMT_T
 //     the B operands are the matching transposed 16-byte activation groups (column j =
 //     activation row j), so the two MFMAs leave the block's exact integer sums in D: lane
 //     l holds rows 4 (l / 16) + r, r = 0..3, of activation row l % 16. The activation is
-//     staged as [step][chunk][code word][row] so that the 16 lanes of a B operand read
-//     consecutive 16-byte slots; the step-major layout of the other kernels has the rows
-//     256 bytes apart, and its 8-way bank conflicts made this kernel slower than the VALU
-//     one.
-//   * The block term (s * dq) * isum, the step tree over the step's 8 blocks, and the step
+//     staged as [step][chunk][code word][row] (sign: [step][chunk][word][half][row]) so
+//     that the 16 lanes of a B operand read consecutive 16-byte slots; the step-major
+//     layout of the other kernels has the rows 256 bytes apart, and its 8-way bank
+//     conflicts made this kernel slower than the VALU one.
+//   * The block term (s * dq) * isum, the step tree over the step's blocks, and the step
 //     sum in step order from +0 are those of the other kernels (row_tree reads lane L - off,
 //     so lane 0 of a row ends with ((t0 + t7) + (t6 + t5)) + ((t4 + t3) + (t2 + t1)) over
-//     the block terms t), so every row is bit-identical to the row computed alone.
+//     the block terms t, and the same pattern over 16 blocks for sign), so every row is
+//     bit-identical to the row computed alone.
+//   * The weight loads carry no non-temporal hint: the two 64-byte halves of a row's line
+//     come from neighbouring loads, and with the hint the second half was fetched again.
 //   * A block's scales reach the fold lanes with ds_bpermute from the lanes that loaded
 //     them (the blocks of row i that the lane's code load covers; nb must be a multiple
 //     of 2 (ternary) or 4 (sign)).
