@@ -59,23 +59,41 @@ constexpr int kRingThreads = 64 * kRingWaves;
 constexpr int kRingDepthTwo = TB_RING_DEPTH_TWO;   // items in flight per wave, gate + up
 constexpr int kRingDepthOne = TB_RING_DEPTH_ONE;   // one matrix
 #ifndef TB_MFMA_DEPTH
-#define TB_MFMA_DEPTH 2
+#define TB_MFMA_DEPTH 1
 #endif
-#ifndef TB_MFMA_MIN_ROWS
-#define TB_MFMA_MIN_ROWS 6
+#ifndef TB_MFMA_DEPTH_SIGN_GATEUP
+#define TB_MFMA_DEPTH_SIGN_GATEUP 2
 #endif
-constexpr int kMfmaDepth = TB_MFMA_DEPTH;         // items in flight per wave (MFMA kernel)
-// M from which gate/up runs on the matrix cores. The MFMA kernel takes about the same time
-// for every M (21 µs for gate/up at the FFN shape, M = 4 or 8), the dot-product kernel
-// grows with M (18 µs at M = 4, 26 µs at M = 8).
-constexpr int kMfmaMinRows = TB_MFMA_MIN_ROWS;
-// The same for one matrix (tb_gemv_ternary, the down GEMV): at the FFN's down shape its 20
-// rows per CU fill 20 of 32 MFMA rows; measured 20.7 µs against 22.4 at M = 8, 21.0
-// against 19.4 at M = 6.
-#ifndef TB_MFMA_MIN_ROWS_ONE
-#define TB_MFMA_MIN_ROWS_ONE 8
+// items in flight per wave in the MFMA kernel: one, except for sign gate/up (measured at
+// M = 8: ternary gate/up 17.4 µs at depth 1 against 19.7 at depth 2, one matrix 18.9
+// against 20.2; sign gate/up 19.9 at depth 2 against 20.7 at depth 1)
+constexpr int mfma_depth(int fmt, bool gateup)
+{
+    return fmt == TB_FMT_SIGN1 && gateup ? TB_MFMA_DEPTH_SIGN_GATEUP : TB_MFMA_DEPTH;
+}
+// M from which a GEMV runs on the matrix cores, per weight format, for gate/up and for one
+// matrix (tb_gemv_ternary, the down GEMV). The MFMA kernel takes about the same time for
+// every M, the dot-product kernel grows with M; the crossings measured at the FFN shapes
+// (hidden 5120, inter 17408): ternary gate/up 17.2 µs against 18.0 at M = 4, ternary down
+// (with the rotation of h) 17.8 against 18.6 at M = 6, sign down 18.6 against 19.3 at M = 7;
+// sign gate/up moves over at M = 6.
+#ifndef TB_MFMA_MIN_ROWS_TERN
+#define TB_MFMA_MIN_ROWS_TERN 4
 #endif
-constexpr int kMfmaMinRowsOne = TB_MFMA_MIN_ROWS_ONE;
+#ifndef TB_MFMA_MIN_ROWS_TERN_ONE
+#define TB_MFMA_MIN_ROWS_TERN_ONE 6
+#endif
+#ifndef TB_MFMA_MIN_ROWS_SIGN
+#define TB_MFMA_MIN_ROWS_SIGN 6
+#endif
+#ifndef TB_MFMA_MIN_ROWS_SIGN_ONE
+#define TB_MFMA_MIN_ROWS_SIGN_ONE 7
+#endif
+constexpr int mfma_min_rows(bool ternary, bool gateup)
+{
+    return ternary ? (gateup ? TB_MFMA_MIN_ROWS_TERN : TB_MFMA_MIN_ROWS_TERN_ONE)
+                   : (gateup ? TB_MFMA_MIN_ROWS_SIGN : TB_MFMA_MIN_ROWS_SIGN_ONE);
+}
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 enum Mode { kModeY = 0, kModeGateUp = 1, kModeIsum = 2 };
@@ -477,7 +495,7 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
     constexpr int kMatShift = kTwo ? 1 : 0;   // gate/up: item = ((tile, step), matrix)
     constexpr int kBps = kTern ? 8 : 16;      // blocks per step (256 code bytes per row)
     constexpr int kBpl = kBps / 4;            // blocks per 16-byte load of the 4 lanes of a row
-    constexpr int kDepth = kMfmaDepth;
+    constexpr int kDepth = mfma_depth(FMT, MODE == kModeGateUp);
     constexpr int kThreads = mfma_threads(FMT), kWaves = kThreads / 64;
 
     const int k = a.k, n = a.n, nb = k / kBlock;
@@ -830,14 +848,17 @@ template <int FMT, int MODE>
 GemvFn gemv_mfma_pick_m(int m)
 {
     switch (m) {
+    case 4: return gemv_mfma_kernel<4, FMT, MODE>;
+    case 5: return gemv_mfma_kernel<5, FMT, MODE>;
     case 6: return gemv_mfma_kernel<6, FMT, MODE>;
     case 7: return gemv_mfma_kernel<7, FMT, MODE>;
     case 8: return gemv_mfma_kernel<8, FMT, MODE>;
     default: return nullptr;
     }
 }
-static_assert(kMfmaMinRows >= 6 && kMfmaMinRowsOne >= 6,
-              "gemv_mfma_kernel is instantiated for M = 6 .. 8");
+static_assert(mfma_min_rows(true, true) >= 4 && mfma_min_rows(true, false) >= 4 &&
+                  mfma_min_rows(false, true) >= 4 && mfma_min_rows(false, false) >= 4,
+              "gemv_mfma_kernel is instantiated for M = 4 .. 8");
 
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
@@ -961,8 +982,8 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     // batched rows: the matrix-core kernel, when its LDS plan fits (a lane's scale load
     // holds whole block pairs (ternary) or quads (sign) of one row)
     const bool tern = w0->fmt == TB_FMT_TERNARY2;
-    if (nb % (tern ? 2 : 4) == 0 &&
-        ((mode == kModeGateUp && m >= kMfmaMinRows) || (mode == kModeY && m >= kMfmaMinRowsOne))) {
+    if (nb % (tern ? 2 : 4) == 0 && mode != kModeIsum &&
+        m >= mfma_min_rows(tern, mode == kModeGateUp)) {
         const size_t rows_cu = (size_t)((tiles + ring_grid - 1) / ring_grid) * kRowsPerWave;
         const size_t bps = tern ? 8 : 16;
         const size_t mfma_lds = (size_t)steps * step_bytes + (size_t)m * (nb + bps) * 4 * (tern ? 1 : 2) +

@@ -131,10 +131,11 @@ def test_sliced_and_streaming_kernels_fold_alike(o, fmt):
                                      (TERN, 1152, 5120), (SIGN, 3, 512), (SIGN, 100, 1536),
                                      (SIGN, 2180, 1536), (SIGN, 1152, 5120)])
 def test_matrix_core_and_dot_kernels_fold_alike(o, fmt, n, k):
-    # Gate/up from M = 6 on, and a single GEMV at M = 8, run on the matrix cores (16-row
-    # tiles, rows past a CU's range masked; the k = 1280 ternary and k = 1536 sign rows end
-    # in a ragged step); a row alone runs on the dot-product kernel. Both fold every row in
-    # the same order, so the batched rows must equal the rows alone bit for bit.
+    # Gate/up from M = 4 (ternary) or 6 (sign) on, and a single GEMV from M = 6 (ternary)
+    # or 7 (sign) on, run on the matrix cores (16-row tiles, rows past a CU's range masked;
+    # the k = 1280 ternary and k = 1536 sign rows end in a ragged step); a row alone runs on
+    # the dot-product kernel. Both fold every row in the same order, so the batched rows
+    # must equal the rows alone bit for bit.
     say(f"matrix-core vs dot-product fmt={fmt} n={n} k={k}")
     wg = synth.matrix(fmt, n, k, 13, 0, synth.T_GATE)
     wu = synth.matrix(fmt, n, k, 13, 0, synth.T_UP)
@@ -148,19 +149,21 @@ def test_matrix_core_and_dot_kernels_fold_alike(o, fmt, n, k):
     x = synth.normal_rows(8, k, 13, 0)
     q, dq = o.rotate_quant(x)
     alone = [gateup(q[r:r + 1], dq[r:r + 1])[0].tobytes() for r in range(8)]
-    for m in (6, 7, 8):
+    for m in (4, 5, 6, 7, 8):
         h = gateup(q[:m], dq[:m])
         for r in range(m):
             assert h[r].tobytes() == alone[r], f"M={m} row {r}"
     r = o.gateup_silu(wg, wu, q, dq)
     tol = bounds.h_tolerance(r["g"], r["u"], r["sg"], r["su"])
     assert np.all(np.abs(h.astype(np.float64) - r["h"]) <= tol)
-    # one matrix (tb_gemv_ternary, the down GEMV's kernel) runs on the matrix cores at M = 8
-    y8 = gu.gemv(dg, q, dq)
-    for row in range(8):
-        assert gu.gemv(dg, q[row:row + 1], dq[row:row + 1])[0].tobytes() == y8[row].tobytes(), row
+    # one matrix (tb_gemv_ternary, the down GEMV's kernel)
+    y_alone = [gu.gemv(dg, q[row:row + 1], dq[row:row + 1])[0].tobytes() for row in range(8)]
+    for m in (6, 7, 8):
+        y = gu.gemv(dg, q[:m], dq[:m])
+        for row in range(m):
+            assert y[row].tobytes() == y_alone[row], f"M={m} row {row}"
     yo, sabs = o.gemv(wg, q, dq)
-    assert bounds.gemv_ok(y8, yo, sabs)[0]
+    assert bounds.gemv_ok(y, yo, sabs)[0]
 
 
 def test_code3_and_zero_cases(o):
