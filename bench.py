@@ -187,6 +187,57 @@ def gateup_event_timing(torch, s: Stream64, reps: int):
     return total / (reps * n)
 
 
+def call_breakdown(torch, s: Stream64, layer_s: float, reps: int):
+    """Per-call device time of the separate-call stream, without a tracer.
+
+    Each call type is captured 64 times back to back (one per layer's weights) in a HIP
+    graph and timed with HIP events around `reps` replays, so a figure is the kernel's
+    duration plus the dependency between two launches on one stream. The stream's layer
+    time minus the sum of its three calls is what changes when the calls alternate
+    (caches, launch shapes). Returns microseconds per call and kernel-only GB/s."""
+    tb, n = s.tb, len(s.layers)
+    tb.tb_rotate_quant_i8(s.x[0], s.q, s.dq)
+    tb.tb_ffn_gateup_silu(*s.layers[0][:2], s.q, s.dq, s.h)
+    tb.tb_rotate_quant_i8(s.h, s.qh, s.dqh)
+    torch.cuda.synchronize()
+    calls = {
+        "rotate_quant_x": lambda l, w: tb.tb_rotate_quant_i8(s.x[l], s.q, s.dq),
+        "gateup_silu": lambda l, w: tb.tb_ffn_gateup_silu(w[0], w[1], s.q, s.dq, s.h),
+        "rotate_quant_h": lambda l, w: tb.tb_rotate_quant_i8(s.h, s.qh, s.dqh),
+        "down_gemv": lambda l, w: tb.tb_gemv_ternary(w[2], s.qh, s.dqh, s.y[l]),
+        "ffn_down": lambda l, w: tb.tb_ffn_down(w[2], s.h, s.qh, s.dqh, s.y[l]),
+    }
+    out = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, call in calls.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l, w in enumerate(s.layers):
+                call(l, w)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e-3 / (reps * n)
+        del g
+    w = s.layers[0]
+    gu_bytes = w[0].nbytes + w[1].nbytes
+    res = {k + "_us": round(v * 1e6, 3) for k, v in out.items()}
+    summed = out["rotate_quant_x"] + out["gateup_silu"] + out["ffn_down"]
+    res.update({
+        "layer_us": round(layer_s * 1e6, 3),
+        "sum_of_calls_us": round(summed * 1e6, 3),
+        "layer_minus_sum_us": round((layer_s - summed) * 1e6, 3),
+        "gateup_kernel_only_gbs": round(gu_bytes / out["gateup_silu"] / 1e9, 1),
+        "down_gemv_kernel_only_gbs": round(w[2].nbytes / out["down_gemv"] / 1e9, 1),
+        "note": "HIP events around graph replays of 64 back-to-back calls of one kind; "
+                "kernel-only GB/s counts weight bytes"})
+    return res
+
+
 def fused_event_timing(torch, f: Fused64, reps: int):
     """Mean duration (s) of one fused launch (32 layers), from HIP events on its stream.
 
@@ -373,6 +424,9 @@ def main():
         k_key = "gemv_ring_kernel<1, 0, 1>"
     k_gbs = k_bytes / k_s / 1e9
     log(f"dominant kernel {k_name}: {k_s * 1e6:.2f} us/launch, {k_gbs:.1f} GB/s")
+    breakdown = call_breakdown(torch, s1, ts / args.layers, max(3, args.steps // 4))
+    log("M=1 calls (graph, us): " + ", ".join(f"{k[:-3]} {v}" for k, v in breakdown.items()
+                                               if k.endswith("_us")))
     clocks = gpu_clocks(torch, s1.step)
     log("clocks (under the M=1 stream): " + (" | ".join(clocks) if clocks else "amd-smi unavailable"))
     del f1, s1
@@ -466,6 +520,7 @@ def main():
                      "kernel": k_name, "bytes_per_launch": k_bytes,
                      "us_per_launch": round(k_s * 1e6, 3)},
         "cpu_baseline": cpu,
+        "m1_call_breakdown": breakdown,
         "gpu_clocks_amd_smi": clocks,
     }
     print(json.dumps(out), flush=True)

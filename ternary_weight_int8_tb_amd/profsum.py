@@ -72,6 +72,62 @@ def read_stats(d: str):
     return rows
 
 
+SIGN_MATRIX_BYTES = INTER * HIDDEN // 8 + INTER * NB_H * 2
+# the four kernels of one layer of the separate-call stream: rotquant(x), gate/up,
+# rotquant(h), down GEMV; weight bytes of the two GEMV launches
+STREAMS = {
+    "ternary M=1": ("gemv_ring_kernel<1, 0, 1>", "gemv_ring_kernel<1, 0, 0>", MATRIX_BYTES),
+    "ternary M=8": ("gemv_mfma_kernel<8, 0, 1>", "gemv_mfma_kernel<8, 0, 0>", MATRIX_BYTES),
+    "sign M=1": ("gemv_ring_kernel<1, 1, 1>", "gemv_ring_kernel<1, 1, 0>", SIGN_MATRIX_BYTES),
+    "sign M=8": ("gemv_mfma_kernel<8, 1, 1>", "gemv_mfma_kernel<8, 1, 0>", SIGN_MATRIX_BYTES),
+}
+
+
+def median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if v else float("nan")
+
+
+def stream_passes(d: str):
+    """Graph passes of each 64-layer stream in a kernel trace.
+
+    A pass is 256 consecutive dispatches in the layer order above. Eager passes (host
+    launch gaps between kernels) are dropped: a graph pass is one whose median gap between
+    consecutive dispatches is at most zero. Returns, per stream, the number of passes
+    and per position the median duration and the median gap to the next dispatch (us),
+    plus the median pass span and busy time per layer."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return {}
+    with open(files[0]) as fh:
+        seq = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short_name(r["Kernel_Name"]))
+                      for r in csv.DictReader(fh)))
+    names = [n for _, _, n in seq]
+    out = {}
+    for label, (gu, dn, _) in STREAMS.items():
+        pat = ["rotquant_kernel", gu, "rotquant_kernel", dn] * LAYERS
+        passes, i = [], 0
+        while i + len(pat) <= len(seq):
+            if names[i:i + len(pat)] == pat:
+                p = seq[i:i + len(pat)]
+                if median([p[j + 1][0] - p[j][1] for j in range(len(p) - 1)]) <= 0:
+                    passes.append(p)
+                i += len(pat)
+            else:
+                i += 1
+        if not passes:
+            continue
+        pos = []
+        for k in range(4):
+            dur = [(p[j][1] - p[j][0]) / 1e3 for p in passes for j in range(k, len(pat), 4)]
+            gap = [(p[j + 1][0] - p[j][1]) / 1e3 for p in passes for j in range(k, len(pat) - 1, 4)]
+            pos.append((pat[k], median(dur), median(gap), sum(gap) / len(gap)))
+        span = median([(p[-1][1] - p[0][0]) / 1e3 / LAYERS for p in passes])
+        busy = median([sum(e - b for b, e, _ in p) / 1e3 / LAYERS for p in passes])
+        out[label] = {"passes": len(passes), "positions": pos, "span_us": span, "busy_us": busy}
+    return out
+
+
 def read_counter(d: str, counter: str):
     """Per kernel (short name): list of the counter's value per dispatch (KiB)."""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -120,8 +176,8 @@ def main():
                      f"{r['max_us']:.2f} | {r['pct']:.1f} |")
     lines += ["", "Template arguments: gemv_ring_kernel<M, FMT, MODE>, FMT 0 = ternary, 1 = sign; "
               "MODE 0 = single GEMV (down), 1 = gate/up + SiLU, 2 = block-sum export. "
-              "gemv_mfma_kernel<M, FMT, MODE> runs on the matrix cores (gate/up for M >= 6, "
-              "a single GEMV at M = 8). "
+              "gemv_mfma_kernel<M, FMT, MODE> runs on the matrix cores (ternary: gate/up for "
+              "M >= 4, a single GEMV for M >= 6; sign: gate/up for M >= 6, a single GEMV for M >= 7). "
               "ffn_layers_kernel<M, FMT> is one tb_ffn_layers launch of up to 32 whole layers. "
               "stream_read_kernel is the 4 GiB read probe."]
     if bench:
@@ -130,6 +186,31 @@ def main():
         keep["entry_point"] = bench.get("config", {}).get("entry_point")
         lines += ["", "Bench line of a run on the same box (headline fields and roofline):", "", "```",
                   json.dumps(keep), json.dumps(bench.get("roofline")), "```"]
+    passes = stream_passes(a.stats)
+    if passes:
+        lines += ["", "Graph passes of the 64-layer separate-call stream in the same trace (per layer: "
+                  "rotquant(x), gate/up, rotquant(h), down GEMV). Durations and gaps are medians over "
+                  "every layer of every graph pass; a negative gap means the tracer stamped the next "
+                  "start before the previous end. Kernel-only GB/s counts weight bytes over the "
+                  "traced duration. The tracer's completion signal per dispatch lengthens passes, "
+                  "at M=1 most of all, so span per layer here exceeds the untraced figure below.",
+                  "", "| stream | passes | kernel | median us | kernel-only GB/s | median gap after us "
+                  "| mean gap after us |", "|---|---|---|---|---|---|---|"]
+        for label, r in passes.items():
+            mbytes = STREAMS[label][2]
+            for k, (name, dur, gap, mgap) in enumerate(r["positions"]):
+                wb = {1: 2 * mbytes, 3: mbytes}.get(k)
+                gbs = f"{wb / dur / 1e3:.0f}" if wb else "-"
+                lines.append(f"| {label} | {r['passes']} | `{name}` | {dur:.2f} | {gbs} | {gap:.2f} | "
+                             f"{mgap:.2f} |")
+        lines += ["", "| stream | traced span per layer us | traced kernel busy per layer us |",
+                  "|---|---|---|"]
+        for label, r in passes.items():
+            lines.append(f"| {label} | {r['span_us']:.2f} | {r['busy_us']:.2f} |")
+    if bench and bench.get("m1_call_breakdown"):
+        lines += ["", "Untraced per-call device time at M=1 from the same bench run (HIP events around "
+                  "graph replays of 64 back-to-back calls of one kind):", "", "```",
+                  json.dumps(bench["m1_call_breakdown"]), "```"]
     os.makedirs(a.out, exist_ok=True)
     with open(os.path.join(a.out, "ffn64_stream_kernel_stats.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
