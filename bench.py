@@ -284,22 +284,22 @@ def measured_traffic(kernel_key: str):
     return int(doc["kernels"][kernel_key]["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(layers_host, xs, seconds: float):
-    """The scalar oracle, single-threaded, on the first layers of the same stream."""
+def cpu_baseline(layers_host, xs, seconds: float, m: int = 1):
+    """The scalar oracle, single-threaded, on the first layers of the same stream at m rows."""
     import oracle
     o = oracle.default()
     t0 = time.perf_counter()
     done, nbytes = 0, 0
     while True:
         l = done % len(layers_host)
-        o.ffn(layers_host[l], xs[l][:1])
+        o.ffn(layers_host[l], xs[l][:m])
         done += 1
         nbytes += layers_host[l].nbytes
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} FFN layers of the same 64-layer stream at M=1 "
+            "sample": f"{done} FFN layers of the same 64-layer stream at M={m} "
                       f"({nbytes} weight bytes, {dt:.1f} s, 1 thread)"}
 
 
@@ -483,7 +483,10 @@ def main():
     gb1 = step_bytes / t1 / 1e9
 
     cpu = cpu_baseline(layers[:4], xs, args.cpu_seconds)
-    log(f"cpu oracle: {cpu['value']} GB/s ({cpu['sample']})")
+    cpu8 = cpu_baseline(layers[:4], xs, args.cpu_seconds / 2, m=8)
+    cpu["m8"] = {"value": cpu8["value"], "unit": cpu8["unit"], "sample": cpu8["sample"]}
+    log(f"cpu oracle: {cpu['value']} GB/s ({cpu['sample']}); M=8 {cpu8['value']} GB/s "
+        f"({cpu8['sample']})")
 
     out = {
         "metric": METRIC,
