@@ -92,7 +92,7 @@ SHAPES = [(256, 512), (1, 128), (63, 256), (65, 640), (257, 2176), (2176, 640), 
 
 @pytest.mark.parametrize("fmt", [TERN, SIGN])
 @pytest.mark.parametrize("n,k", SHAPES)
-@pytest.mark.parametrize("m", [1, 2, 5, 8])
+@pytest.mark.parametrize("m", range(1, 9))   # the dot-product and matrix-core routes
 def test_block_sums_and_gemv(o, fmt, n, k, m):
     say(f"gemv fmt={fmt} n={n} k={k} m={m}")
     w = synth.matrix(fmt, n, k, 7 + n + k, 0, synth.T_GATE)
