@@ -82,11 +82,12 @@ constexpr int mfma_depth(int fmt, bool gateup)
 // M from which a GEMV runs on the matrix cores, per weight format, for gate/up and for one
 // matrix (tb_gemv_ternary, the down GEMV). The MFMA kernel takes about the same time for
 // every M, the dot-product kernel grows with M; the crossings measured at the FFN shapes
-// (hidden 5120, inter 17408): ternary gate/up 17.2 µs against 18.0 at M = 4, ternary down
-// (with the rotation of h) 17.8 against 18.6 at M = 6, sign down 18.6 against 19.3 at M = 7;
-// sign gate/up moves over at M = 6.
+// (hidden 5120, inter 17408): ternary gate/up 17.3 µs against about 18 at M = 5 (at M = 4
+// the dot-product kernel is 0.5-1 µs faster), ternary down (with the rotation of h) 17.8
+// against 18.6 at M = 6, sign down 18.6 against 19.3 at M = 7; sign gate/up moves over at
+// M = 6 (at M = 6 the dot-product kernel is 0.8-1.5 µs slower).
 #ifndef TB_MFMA_MIN_ROWS_TERN
-#define TB_MFMA_MIN_ROWS_TERN 4
+#define TB_MFMA_MIN_ROWS_TERN 5
 #endif
 #ifndef TB_MFMA_MIN_ROWS_TERN_ONE
 #define TB_MFMA_MIN_ROWS_TERN_ONE 6
