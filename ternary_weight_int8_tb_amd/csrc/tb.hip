@@ -456,12 +456,18 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     }
 }
 
-// Threads per workgroup of gemv_mfma_kernel: 16 waves for ternary; 8 for sign, whose
-// 16-block steps need more than the 128 registers a wave has at 16 waves per CU.
-__host__ __device__ constexpr int mfma_threads(int fmt) { return fmt == TB_FMT_TERNARY2 ? 1024 : 512; }
+// Threads per workgroup of gemv_mfma_kernel: 16 waves for ternary. Sign's 16-block steps
+// need more than the 128 registers a wave has at 16 waves per CU: its single GEMV (160
+// registers) runs 12 waves, its gate/up (two matrices in flight) 8, since at 12 it spills
+// to scratch (sign down at M=8: 17.7-17.8 µs at 12 waves against 18.9-19.1 at 8; gate/up
+// 22.6-23.3 against 20.2-20.7).
+__host__ __device__ constexpr int mfma_threads(int fmt, bool gateup)
+{
+    return fmt == TB_FMT_TERNARY2 ? 1024 : (gateup ? 512 : 768);
+}
 
 // ------------------------------------------------------------------------------------
-// Batched streaming GEMV on the matrix cores (ternary and sign weights, M >= 6 rows).
+// Batched streaming GEMV on the matrix cores (ternary and sign weights, M >= 5 to 7 rows).
 // With M rows the dot products cost M VALU instructions per 4 weights and lane; here
 // v_mfma_i32_16x16x64_i8 takes them, and the VALU keeps the decode and the fold.
 //   * Workgroup c owns the rows of the same 4-row tiles [tA, tB) as in gemv_ring_kernel
@@ -490,11 +496,11 @@ __host__ __device__ constexpr int mfma_threads(int fmt) { return fmt == TB_FMT_T
 //   * A block's scales reach the fold lanes with ds_bpermute from the lanes that loaded
 //     them (the blocks of row i that the lane's code load covers; nb must be a multiple
 //     of 2 (ternary) or 4 (sign)).
-//   * Sign runs 8 waves per CU: its 16-block steps need more than the 128 registers a
-//     wave has at 16.
+//   * Sign runs 12 waves per CU for one matrix and 8 for gate/up: its 16-block steps need
+//     more than the 128 registers a wave has at 16.
 // ------------------------------------------------------------------------------------
 template <int M, int FMT, int MODE>
-__global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a)
+__global__ __launch_bounds__(mfma_threads(FMT, MODE == kModeGateUp)) void gemv_mfma_kernel(GemvArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     using L = StepLayout<M, FMT>;
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
     constexpr int kBps = kTern ? 8 : 16;      // blocks per step (256 code bytes per row)
     constexpr int kBpl = kBps / 4;            // blocks per 16-byte load of the 4 lanes of a row
     constexpr int kDepth = mfma_depth(FMT, MODE == kModeGateUp);
-    constexpr int kThreads = mfma_threads(FMT), kWaves = kThreads / 64;
+    constexpr int kThreads = mfma_threads(FMT, MODE == kModeGateUp), kWaves = kThreads / 64;
 
     const int k = a.k, n = a.n, nb = k / kBlock;
     const int C = k / Fmt<FMT>::kWeightsPerChunk, I = (C + kChunkLanes - 1) / kChunkLanes;
@@ -1006,7 +1012,8 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
                 return TB_EINVAL;
             if ((rc = set_lds(fn, mfma_lds)))
                 return rc;
-            hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(mfma_threads(w0->fmt)), mfma_lds, stream, a);
+            hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(mfma_threads(w0->fmt, mode == kModeGateUp)), mfma_lds,
+                               stream, a);
             return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
         }
     }
