@@ -69,23 +69,17 @@ constexpr int kRingDepthOne = TB_RING_DEPTH_ONE;   // one matrix
 #ifndef TB_MFMA_DEPTH
 #define TB_MFMA_DEPTH 1
 #endif
-#ifndef TB_MFMA_DEPTH_SIGN_GATEUP
-#define TB_MFMA_DEPTH_SIGN_GATEUP 2
-#endif
-// items in flight per wave in the MFMA kernel: one, except for sign gate/up (measured at
-// M = 8: ternary gate/up 17.4 µs at depth 1 against 19.7 at depth 2, one matrix 18.9
-// against 20.2; sign gate/up 19.9 at depth 2 against 20.7 at depth 1)
-constexpr int mfma_depth(int fmt, bool gateup)
-{
-    return fmt == TB_FMT_SIGN1 && gateup ? TB_MFMA_DEPTH_SIGN_GATEUP : TB_MFMA_DEPTH;
-}
+// items in flight per wave in the MFMA kernel (measured at M = 8: ternary gate/up 17.4 µs
+// at depth 1 against 19.7 at depth 2, one matrix 18.9 against 20.2; sign gate/up, which
+// fits 12 waves only at depth 1, 17.3-17.8 there against 19.8-20.8 at depth 2 on 8 waves)
+constexpr int kMfmaDepth = TB_MFMA_DEPTH;
 // M from which a GEMV runs on the matrix cores, per weight format, for gate/up and for one
 // matrix (tb_gemv_ternary, the down GEMV). The MFMA kernel takes about the same time for
 // every M, the dot-product kernel grows with M; the crossings measured at the FFN shapes
 // (hidden 5120, inter 17408): ternary gate/up 17.3 µs against about 18 at M = 5 (at M = 4
 // the dot-product kernel is 0.5-1 µs faster), ternary down (with the rotation of h) 17.8
-// against 18.6 at M = 6, sign down 18.6 against 19.3 at M = 7; sign gate/up moves over at
-// M = 6 (at M = 6 the dot-product kernel is 0.8-1.5 µs slower).
+// against 18.6 at M = 6, sign down 18.6 against 19.3 at M = 7, sign gate/up 17.1-17.4
+// against 18.2-19.7 at M = 5 (a tie at M = 4).
 #ifndef TB_MFMA_MIN_ROWS_TERN
 #define TB_MFMA_MIN_ROWS_TERN 5
 #endif
@@ -93,7 +87,7 @@ constexpr int mfma_depth(int fmt, bool gateup)
 #define TB_MFMA_MIN_ROWS_TERN_ONE 6
 #endif
 #ifndef TB_MFMA_MIN_ROWS_SIGN
-#define TB_MFMA_MIN_ROWS_SIGN 6
+#define TB_MFMA_MIN_ROWS_SIGN 5
 #endif
 #ifndef TB_MFMA_MIN_ROWS_SIGN_ONE
 #define TB_MFMA_MIN_ROWS_SIGN_ONE 7
@@ -456,15 +450,10 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     }
 }
 
-// Threads per workgroup of gemv_mfma_kernel: 16 waves for ternary. Sign's 16-block steps
-// need more than the 128 registers a wave has at 16 waves per CU: its single GEMV (160
-// registers) runs 12 waves, its gate/up (two matrices in flight) 8, since at 12 it spills
-// to scratch (sign down at M=8: 17.7-17.8 µs at 12 waves against 18.9-19.1 at 8; gate/up
-// 22.6-23.3 against 20.2-20.7).
-__host__ __device__ constexpr int mfma_threads(int fmt, bool gateup)
-{
-    return fmt == TB_FMT_TERNARY2 ? 1024 : (gateup ? 512 : 768);
-}
+// Threads per workgroup of gemv_mfma_kernel: 16 waves for ternary; 12 for sign, whose
+// 16-block steps need 156-160 registers, more than the 128 a wave has at 16 waves per CU
+// (sign down at M=8: 17.7-17.8 µs at 12 waves against 18.9-19.1 at 8).
+__host__ __device__ constexpr int mfma_threads(int fmt) { return fmt == TB_FMT_TERNARY2 ? 1024 : 768; }
 
 // ------------------------------------------------------------------------------------
 // Batched streaming GEMV on the matrix cores (ternary and sign weights, M >= 5 to 7 rows).
@@ -496,11 +485,11 @@ __host__ __device__ constexpr int mfma_threads(int fmt, bool gateup)
 //   * A block's scales reach the fold lanes with ds_bpermute from the lanes that loaded
 //     them (the blocks of row i that the lane's code load covers; nb must be a multiple
 //     of 2 (ternary) or 4 (sign)).
-//   * Sign runs 12 waves per CU for one matrix and 8 for gate/up: its 16-block steps need
-//     more than the 128 registers a wave has at 16.
+//   * Sign runs 12 waves per CU: its 16-block steps need more than the 128 registers a
+//     wave has at 16.
 // ------------------------------------------------------------------------------------
 template <int M, int FMT, int MODE>
-__global__ __launch_bounds__(mfma_threads(FMT, MODE == kModeGateUp)) void gemv_mfma_kernel(GemvArgs a)
+__global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     using L = StepLayout<M, FMT>;
@@ -510,8 +499,8 @@ __global__ __launch_bounds__(mfma_threads(FMT, MODE == kModeGateUp)) void gemv_m
     constexpr int kMatShift = kTwo ? 1 : 0;   // gate/up: item = ((tile, step), matrix)
     constexpr int kBps = kTern ? 8 : 16;      // blocks per step (256 code bytes per row)
     constexpr int kBpl = kBps / 4;            // blocks per 16-byte load of the 4 lanes of a row
-    constexpr int kDepth = mfma_depth(FMT, MODE == kModeGateUp);
-    constexpr int kThreads = mfma_threads(FMT, MODE == kModeGateUp), kWaves = kThreads / 64;
+    constexpr int kDepth = kMfmaDepth;
+    constexpr int kThreads = mfma_threads(FMT), kWaves = kThreads / 64;
 
     const int k = a.k, n = a.n, nb = k / kBlock;
     const int C = k / Fmt<FMT>::kWeightsPerChunk, I = (C + kChunkLanes - 1) / kChunkLanes;
@@ -1012,8 +1001,7 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
                 return TB_EINVAL;
             if ((rc = set_lds(fn, mfma_lds)))
                 return rc;
-            hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(mfma_threads(w0->fmt, mode == kModeGateUp)), mfma_lds,
-                               stream, a);
+            hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(mfma_threads(w0->fmt)), mfma_lds, stream, a);
             return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
         }
     }

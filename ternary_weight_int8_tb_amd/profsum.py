@@ -177,7 +177,7 @@ def main():
     lines += ["", "Template arguments: gemv_ring_kernel<M, FMT, MODE>, FMT 0 = ternary, 1 = sign; "
               "MODE 0 = single GEMV (down), 1 = gate/up + SiLU, 2 = block-sum export. "
               "gemv_mfma_kernel<M, FMT, MODE> runs on the matrix cores (ternary: gate/up for "
-              "M >= 5, a single GEMV for M >= 6; sign: gate/up for M >= 6, a single GEMV for M >= 7). "
+              "M >= 5, a single GEMV for M >= 6; sign: gate/up for M >= 5, a single GEMV for M >= 7). "
               "ffn_layers_kernel<M, FMT> is one tb_ffn_layers launch of up to 32 whole layers. "
               "stream_read_kernel is the 4 GiB read probe."]
     if bench:

@@ -131,7 +131,7 @@ def test_sliced_and_streaming_kernels_fold_alike(o, fmt):
                                      (TERN, 1152, 5120), (SIGN, 3, 512), (SIGN, 100, 1536),
                                      (SIGN, 2180, 1536), (SIGN, 1152, 5120)])
 def test_matrix_core_and_dot_kernels_fold_alike(o, fmt, n, k):
-    # Gate/up from M = 5 (ternary) or 6 (sign) on, and a single GEMV from M = 6 (ternary)
+    # Gate/up from M = 5 on, and a single GEMV from M = 6 (ternary)
     # or 7 (sign) on, run on the matrix cores (16-row tiles, rows past a CU's range masked;
     # the k = 1280 ternary and k = 1536 sign rows end in a ragged step); a row alone runs on
     # the dot-product kernel. Both fold every row in the same order, so the batched rows
