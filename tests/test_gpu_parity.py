@@ -200,7 +200,9 @@ def test_gateup_silu(o, fmt, n, k, m):
 
 # ----------------------------------------------------------------- a6, a7: down stage
 @pytest.mark.parametrize("fmt", [TERN, SIGN])
-@pytest.mark.parametrize("n,k,m", [(65, 2176, 2), (5120, 17408, 1), (5120, 17408, 8)])
+# full down shape at M = 6 and 7: where the down GEMV moves to the matrix cores
+@pytest.mark.parametrize("n,k,m", [(65, 2176, 2), (5120, 17408, 1), (5120, 17408, 6),
+                                   (5120, 17408, 7), (5120, 17408, 8)])
 def test_down_stage(o, fmt, n, k, m):
     say(f"down fmt={fmt} n={n} k={k} m={m}")
     wd = synth.matrix(fmt, n, k, 12, 0, synth.T_DOWN)
