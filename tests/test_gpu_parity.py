@@ -183,7 +183,9 @@ def test_code3_and_zero_cases(o):
 
 # ----------------------------------------------------------------- a5: gate/up + SiLU
 @pytest.mark.parametrize("fmt", [TERN, SIGN])
-@pytest.mark.parametrize("n,k,m", [(384, 256, 1), (2176, 640, 3), (1152, 5120, 8)])
+# the full gate/up shape at M = 5, where gate/up moves to the matrix cores
+@pytest.mark.parametrize("n,k,m", [(384, 256, 1), (2176, 640, 3), (1152, 5120, 8),
+                                   (17408, 5120, 5)])
 def test_gateup_silu(o, fmt, n, k, m):
     say(f"gateup fmt={fmt} n={n} k={k} m={m}")
     layer = synth.ffn_layer(11, 0, fmt, hidden=k, inter=n)
