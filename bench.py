@@ -17,8 +17,15 @@ calls per layer (tb_rotate_quant_i8, tb_ffn_gateup_silu, tb_ffn_down) replayed
 from a HIP graph (and eagerly). The value is the faster of the two; the JSON
 names it. Also printed: the same at M=8; the 1-bit sign stream; the roofline
 of the headline path's dominant kernel, timed with HIP events on the stream it
-runs on; a 4 GiB streaming-read probe; and the scalar CPU oracle timed on a
-bounded sample on this host.
+runs on; a 4 GiB streaming-read probe; and the scalar CPU oracle timed on this
+host's cores.
+
+The timed outputs are checked: after timing, the y of every layer from the
+timed graph replay must equal, byte for byte, that of the same calls run
+eagerly and that of the fused launch; and the CPU-baseline leg (the oracle run
+over all 64 layers on every host core) checks every layer's y against the
+oracle within the chained-layer bound. Any mismatch prints the JSON line with
+parity_checked false and exits with status 3.
 """
 
 from __future__ import annotations
@@ -53,55 +60,75 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--skip-sign", action="store_true")
     p.add_argument("--skip-m8", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="target CPU time of the single-thread oracle sample")
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="host threads of the all-cores oracle pass (0: the usable cores, "
+                        "at most 16)")
+    p.add_argument("--skip-oracle-m8", action="store_true",
+                   help="no all-cores oracle pass (and oracle parity check) at M=8")
     p.add_argument("--profile-only", action="store_true",
-                   help="one eager M=1 pass and exit (for rocprofv3 counter runs)")
+                   help="one eager pass of each path and exit (for rocprofv3 counter runs)")
+    p.add_argument("--profile-m", type=int, default=1,
+                   help="rows of the --profile-only pass (1..8)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a device copy of this many MiB (counter calibration)")
     return p.parse_args()
 
 
 class Stream64:
-    """Device weights and buffers of the layer stream at m rows."""
+    """Device weights and buffers of the layer stream at m rows.
+
+    Every layer writes its own q, dq, h, rotquant(h) and y (the same kernels and bytes as
+    with shared buffers), so all of a timed step's intermediates can be checked after it."""
 
     def __init__(self, tb, layers_dev, xs, m, torch):
         self.tb, self.layers, self.m = tb, layers_dev, m
         dev = "cuda"
         k = layers_dev[0][0].k
         n = layers_dev[0][0].n
+        L = len(layers_dev)
         self.x = [torch.from_numpy(x[:m].copy()).to(dev) for x in xs]
-        self.q = torch.empty(m, k, dtype=torch.int8, device=dev)
-        self.dq = torch.empty(m, k // 128, dtype=torch.float32, device=dev)
-        self.h = torch.empty(m, n, dtype=torch.float32, device=dev)
-        self.qh = torch.empty(m, n, dtype=torch.int8, device=dev)
-        self.dqh = torch.empty(m, n // 128, dtype=torch.float32, device=dev)
-        self.y = torch.empty(len(layers_dev), m, k, dtype=torch.float32, device=dev)
+        self.q = torch.empty(L, m, k, dtype=torch.int8, device=dev)
+        self.dq = torch.empty(L, m, k // 128, dtype=torch.float32, device=dev)
+        self.h = torch.empty(L, m, n, dtype=torch.float32, device=dev)
+        self.qh = torch.empty(L, m, n, dtype=torch.int8, device=dev)
+        self.dqh = torch.empty(L, m, n // 128, dtype=torch.float32, device=dev)
+        self.y = torch.empty(L, m, k, dtype=torch.float32, device=dev)
 
     def step(self):
         tb = self.tb
         for l, (wg, wu, wd) in enumerate(self.layers):
-            tb.tb_rotate_quant_i8(self.x[l], self.q, self.dq)
-            tb.tb_ffn_gateup_silu(wg, wu, self.q, self.dq, self.h)
-            tb.tb_ffn_down(wd, self.h, self.qh, self.dqh, self.y[l])
+            tb.tb_rotate_quant_i8(self.x[l], self.q[l], self.dq[l])
+            tb.tb_ffn_gateup_silu(wg, wu, self.q[l], self.dq[l], self.h[l])
+            tb.tb_ffn_down(wd, self.h[l], self.qh[l], self.dqh[l], self.y[l])
+
+    def outputs(self):
+        """Every intermediate and output of the last step, on the host."""
+        return {name: getattr(self, name).cpu().numpy().copy()
+                for name in ("q", "dq", "h", "qh", "dqh", "y")}
 
 
 class Fused64:
-    """The same stream through tb_ffn_layers: one call per step (one launch per 32 layers)."""
+    """The same stream through tb_ffn_layers: one call per step (one launch per 32 layers).
 
-    def __init__(self, tb, layers_dev, xs, m, torch):
-        self.tb, self.m = tb, m
+    chain=True runs the layers chained (layer l+1 takes layer l's y), the real decode
+    dependency; chain=False gives every layer its own input, like Stream64."""
+
+    def __init__(self, tb, layers_dev, xs, m, torch, chain=False):
+        self.tb, self.m, self.chain = tb, m, chain
         dev = "cuda"
         k = layers_dev[0][0].k
         n = layers_dev[0][0].n
         self.arr = tb.FfnLayers(layers_dev)
-        self.x = torch.from_numpy(np.stack([x[:m] for x in xs])).to(dev)
+        x = xs[0][:m] if chain else np.stack([x[:m] for x in xs])
+        self.x = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
         self.y = torch.empty(len(layers_dev), m, k, dtype=torch.float32, device=dev)
         self.ws = torch.empty(tb.tb_ffn_workspace_bytes(m, k, n), dtype=torch.uint8, device=dev)
         tb.tb_ffn_workspace_init(self.ws)
 
     def step(self):
-        self.tb.tb_ffn_layers(self.arr, self.x, self.ws, self.y)
+        self.tb.tb_ffn_layers(self.arr, self.x, self.ws, self.y, chain=self.chain)
 
     def check(self):
         err = self.tb.tb_ffn_workspace_error(self.ws)
@@ -135,6 +162,7 @@ def time_stream(torch, s, steps: int, warmup: int, use_graph: bool):
     torch.cuda.synchronize()
     total = (time.perf_counter() - t0) / steps
     per = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(steps)]
+    s.graph = graph   # kept for replays after the timed region (clock reading)
     return total, per
 
 
@@ -172,7 +200,7 @@ def gateup_event_timing(torch, s: Stream64, reps: int):
     over every layer's weights (each launch streams its 47 MB from HBM), on the current
     stream, which is the stream the library launches on."""
     tb = s.tb
-    tb.tb_rotate_quant_i8(s.x[0], s.q, s.dq)
+    tb.tb_rotate_quant_i8(s.x[0], s.q[0], s.dq[0])
     torch.cuda.synchronize()
     n = len(s.layers)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -180,7 +208,7 @@ def gateup_event_timing(torch, s: Stream64, reps: int):
     for _ in range(reps):
         e0.record()
         for wg, wu, _wd in s.layers:
-            tb.tb_ffn_gateup_silu(wg, wu, s.q, s.dq, s.h)
+            tb.tb_ffn_gateup_silu(wg, wu, s.q[0], s.dq[0], s.h[0])
         e1.record()
         torch.cuda.synchronize()
         total += e0.elapsed_time(e1) * 1e-3
@@ -196,16 +224,16 @@ def call_breakdown(torch, s: Stream64, layer_s: float, reps: int):
     time minus the sum of its three calls is what changes when the calls alternate
     (caches, launch shapes). Returns microseconds per call and kernel-only GB/s."""
     tb, n = s.tb, len(s.layers)
-    tb.tb_rotate_quant_i8(s.x[0], s.q, s.dq)
-    tb.tb_ffn_gateup_silu(*s.layers[0][:2], s.q, s.dq, s.h)
-    tb.tb_rotate_quant_i8(s.h, s.qh, s.dqh)
+    tb.tb_rotate_quant_i8(s.x[0], s.q[0], s.dq[0])
+    tb.tb_ffn_gateup_silu(*s.layers[0][:2], s.q[0], s.dq[0], s.h[0])
+    tb.tb_rotate_quant_i8(s.h[0], s.qh[0], s.dqh[0])
     torch.cuda.synchronize()
     calls = {
-        "rotate_quant_x": lambda l, w: tb.tb_rotate_quant_i8(s.x[l], s.q, s.dq),
-        "gateup_silu": lambda l, w: tb.tb_ffn_gateup_silu(w[0], w[1], s.q, s.dq, s.h),
-        "rotate_quant_h": lambda l, w: tb.tb_rotate_quant_i8(s.h, s.qh, s.dqh),
-        "down_gemv": lambda l, w: tb.tb_gemv_ternary(w[2], s.qh, s.dqh, s.y[l]),
-        "ffn_down": lambda l, w: tb.tb_ffn_down(w[2], s.h, s.qh, s.dqh, s.y[l]),
+        "rotate_quant_x": lambda l, w: tb.tb_rotate_quant_i8(s.x[l], s.q[l], s.dq[l]),
+        "gateup_silu": lambda l, w: tb.tb_ffn_gateup_silu(w[0], w[1], s.q[0], s.dq[0], s.h[l]),
+        "rotate_quant_h": lambda l, w: tb.tb_rotate_quant_i8(s.h[0], s.qh[l], s.dqh[l]),
+        "down_gemv": lambda l, w: tb.tb_gemv_ternary(w[2], s.qh[0], s.dqh[0], s.y[l]),
+        "ffn_down": lambda l, w: tb.tb_ffn_down(w[2], s.h[0], s.qh[l], s.dqh[l], s.y[l]),
     }
     out = {}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -284,8 +312,28 @@ def measured_traffic(kernel_key: str):
     return int(doc["kernels"][kernel_key]["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(layers_host, xs, seconds: float, m: int = 1):
-    """The scalar oracle, single-threaded, on the first layers of the same stream at m rows."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads(requested: int) -> int:
+    if requested > 0:
+        return requested
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_single_thread(layers_host, xs, seconds: float, m: int = 1):
+    """The scalar oracle, one thread, on the first layers of the same stream at m rows."""
     import oracle
     o = oracle.default()
     t0 = time.perf_counter()
@@ -298,15 +346,67 @@ def cpu_baseline(layers_host, xs, seconds: float, m: int = 1):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} FFN layers of the same 64-layer stream at M={m} "
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "sample": f"{done} FFN layers of the 64-layer stream at M={m} "
                       f"({nbytes} weight bytes, {dt:.1f} s, 1 thread)"}
 
 
-def gpu_clocks(torch, work=None):
-    """The GPU's clock lines from `amd-smi metric --clock`, run as a child process after the
-    timed region; while it runs, `work` (the M=1 stream step) is replayed so the reading is
-    taken under load. None when the tool is missing or refuses."""
+def cpu_all_cores(layers_host, xs, m: int, threads: int):
+    """The oracle over every layer of the stream at m rows, one layer per task on `threads`
+    host threads (its C calls release the GIL). Returns (results per layer, seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    o = oracle.default()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(lambda l: o.ffn(layers_host[l], xs[l][:m]), range(len(layers_host))))
+    return res, time.perf_counter() - t0
+
+
+def oracle_parity(layers_host, res, got, threads: int):
+    """Every layer of a timed step against the oracle, stagewise (the bars of the tests):
+      q, dq                  bit-exact against the oracle's rotquant(x);
+      h                      within the h bound propagated from the 1e-4 fold bar;
+      rotquant(h), its dq    bit-exact against the oracle's rotquant of the GPU's own h;
+      y                      within 1e-4 * sum|terms| of the oracle's down GEMV on that q_h.
+    res: the oracle's ffn() of every layer (from the timed all-cores pass); got: the timed
+    step's outputs [L][m][...] (Stream64.outputs()). Returns (all pass, worst h error over
+    its bound, worst y error over its bound, failures as text)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    from tests import bounds
+    o = oracle.default()
+
+    def one(l):
+        r, bad = res[l], []
+        if not np.array_equal(got["q"][l], r["q"]):
+            bad.append("q")
+        if got["dq"][l].view(np.uint32).tobytes() != r["dq"].view(np.uint32).tobytes():
+            bad.append("dq")
+        tol_h = bounds.h_tolerance(r["g"], r["u"], r["sg"], r["su"])
+        wh = float(np.max(np.abs(got["h"][l].astype(np.float64) - r["h"]) / tol_h))
+        if not wh <= 1.0:
+            bad.append("h")
+        d = o.ffn_down(layers_host[l].down, got["h"][l])
+        if not np.array_equal(got["qh"][l], d["qh"]):
+            bad.append("qh")
+        if got["dqh"][l].view(np.uint32).tobytes() != d["dqh"].view(np.uint32).tobytes():
+            bad.append("dqh")
+        ok_y, wy = bounds.gemv_ok(got["y"][l], d["y"], d["sabs"])
+        if not ok_y:
+            bad.append("y")
+        return bad, wh, wy
+
+    with ThreadPoolExecutor(threads) as ex:
+        out = list(ex.map(one, range(len(res))))
+    fails = [f"layer {l}: {','.join(b)}" for l, (b, _, _) in enumerate(out) if b]
+    return (not fails, max(w for _, w, _ in out), max(w for _, _, w in out), fails[:8])
+
+
+def gpu_clocks(torch, replay):
+    """The GPU's clock lines from `amd-smi metric --clock`, read while `replay` (one graph
+    replay of the M=1 stream, about 1.5 ms) is queued back to back, 200 at a time, so
+    the GPU is busy the whole time the tool runs. None when the tool is missing."""
     import re
     import subprocess
     try:
@@ -315,13 +415,12 @@ def gpu_clocks(torch, work=None):
     except OSError:
         return None
     t0 = time.perf_counter()
+    bursts = 0
     while proc.poll() is None and time.perf_counter() - t0 < 30:
-        if work is not None:
-            for _ in range(4):
-                work()
-            torch.cuda.synchronize()
-        else:
-            time.sleep(0.05)
+        for _ in range(200):
+            replay()
+        torch.cuda.synchronize()
+        bursts += 1
     try:
         out, _ = proc.communicate(timeout=5)
     except subprocess.SubprocessError:
@@ -330,7 +429,8 @@ def gpu_clocks(torch, work=None):
     if proc.returncode != 0:
         return None
     lines = [" ".join(x.split()) for x in out.splitlines() if re.search(r"GFX_\d|CLK:|MEM", x)]
-    return lines[:16] or None
+    return {"lines": lines[:16], "replays_while_reading": bursts * 200,
+            "seconds": round(time.perf_counter() - t0, 2)}
 
 
 def copy_probe(torch, mib: int):
@@ -341,6 +441,20 @@ def copy_probe(torch, mib: int):
         b.copy_(a)
     torch.cuda.synchronize()
     log(f"copy probe: {mib} MiB read + {mib} MiB written per copy, 3 copies")
+
+
+def timed_outputs(torch, s):
+    """The y of every layer as left by the last timed step, on the host."""
+    torch.cuda.synchronize()
+    return s.y.cpu().numpy().copy()
+
+
+def eager_reference(torch, s):
+    """The same calls run once more eagerly (no graph) into poisoned outputs."""
+    s.y.fill_(float("nan"))
+    s.step()
+    torch.cuda.synchronize()
+    return s.y.cpu().numpy().copy()
 
 
 def main():
@@ -374,15 +488,17 @@ def main():
     dev_layers = upload(layers)
     torch.cuda.synchronize()
 
+    if args.profile_only:
+        fp = Fused64(tb, dev_layers, xs, args.profile_m, torch)
+        sp = Stream64(tb, dev_layers, xs, args.profile_m, torch)
+        fp.step()
+        sp.step()
+        torch.cuda.synchronize()
+        fp.check()
+        log(f"profile pass done at M={args.profile_m} (one fused step, one pass of separate calls)")
+        return
     f1 = Fused64(tb, dev_layers, xs, 1, torch)
     s1 = Stream64(tb, dev_layers, xs, 1, torch)
-    if args.profile_only:
-        f1.step()
-        s1.step()
-        torch.cuda.synchronize()
-        f1.check()
-        log("profile pass done (one fused step, one pass of separate calls)")
-        return
 
     def summary(total, per):
         per = sorted(per)
@@ -395,17 +511,32 @@ def main():
 
     use_graph = not args.no_graph
     paths = {}
+    parity = {}
     tf, pf = time_stream(torch, f1, args.steps, args.warmup, False)
     f1.check()
+    y_fused1 = timed_outputs(torch, f1)
     paths["fused"] = summary(tf, pf)
     log(f"fused M=1: {tf / args.layers * 1e6:.2f} us/layer, {step_bytes / tf / 1e9:.1f} GB/s")
+    fc = Fused64(tb, dev_layers, xs, 1, torch, chain=True)
+    tfc, pfc = time_stream(torch, fc, args.steps, args.warmup, False)
+    fc.check()
+    paths["fused_chained"] = summary(tfc, pfc)
+    log(f"fused M=1 chained (layer l+1 takes layer l's y): {tfc / args.layers * 1e6:.2f} us/layer")
+    del fc
     ts, ps = time_stream(torch, s1, args.steps, args.warmup, use_graph)
+    torch.cuda.synchronize()
+    got1 = s1.outputs()
+    y_sep1 = got1["y"]
     paths["separate"] = summary(ts, ps)
     log(f"separate calls M=1 ({'graph' if use_graph else 'eager'}): {ts / args.layers * 1e6:.2f} "
         f"us/layer, {step_bytes / ts / 1e9:.1f} GB/s")
+    graph1 = s1.graph
     te, pe = time_stream(torch, s1, max(3, args.steps // 4), 1, False)
     paths["separate_eager"] = summary(te, pe)
     log(f"separate calls M=1 (eager): {te / args.layers * 1e6:.2f} us/layer")
+    y_eager1 = eager_reference(torch, s1)
+    parity["m1_timed_graph_equals_eager"] = bool(y_sep1.tobytes() == y_eager1.tobytes())
+    parity["m1_fused_equals_separate"] = bool(y_fused1.tobytes() == y_eager1.tobytes())
     head = "fused" if tf <= ts else "separate"
     t1 = tf if head == "fused" else ts
 
@@ -427,21 +558,30 @@ def main():
     breakdown = call_breakdown(torch, s1, ts / args.layers, max(3, args.steps // 4))
     log("M=1 calls (graph, us): " + ", ".join(f"{k[:-3]} {v}" for k, v in breakdown.items()
                                                if k.endswith("_us")))
-    clocks = gpu_clocks(torch, s1.step)
-    log("clocks (under the M=1 stream): " + (" | ".join(clocks) if clocks else "amd-smi unavailable"))
-    del f1, s1
+    clocks = gpu_clocks(torch, graph1.replay) if graph1 is not None else None
+    log("clocks (while the M=1 graph replays): "
+        + (" | ".join(clocks["lines"]) if clocks else "amd-smi unavailable"))
+    del f1, s1, graph1
 
     res_m8 = None
+    y_sep8 = None
     if not args.skip_m8:
         m8 = {}
         f8 = Fused64(tb, dev_layers, xs, 8, torch)
         t8, p8 = time_stream(torch, f8, args.steps, args.warmup, False)
         f8.check()
+        y_fused8 = timed_outputs(torch, f8)
         m8["fused"] = summary(t8, p8)
         del f8
         s8 = Stream64(tb, dev_layers, xs, 8, torch)
         t8s, p8s = time_stream(torch, s8, args.steps, args.warmup, use_graph)
+        torch.cuda.synchronize()
+        got8 = s8.outputs()
+        y_sep8 = got8["y"]
         m8["separate"] = summary(t8s, p8s)
+        y_eager8 = eager_reference(torch, s8)
+        parity["m8_timed_graph_equals_eager"] = bool(y_sep8.tobytes() == y_eager8.tobytes())
+        parity["m8_fused_equals_separate"] = bool(y_fused8.tobytes() == y_eager8.tobytes())
         del s8
         best = "fused" if t8 <= t8s else "separate"
         res_m8 = dict(m8[best], entry_point=best, paths=m8)
@@ -461,10 +601,15 @@ def main():
             fs = Fused64(tb, sdev, xs, m, torch)
             tfs, _ = time_stream(torch, fs, args.steps, args.warmup, False)
             fs.check()
+            yf = timed_outputs(torch, fs)
             row["fused_us_per_layer"] = round(tfs / args.layers * 1e6, 3)
             del fs
             ss = Stream64(tb, sdev, xs, m, torch)
             tss, _ = time_stream(torch, ss, args.steps, args.warmup, use_graph)
+            ys = timed_outputs(torch, ss)
+            ye = eager_reference(torch, ss)
+            parity[f"sign_m{m}_timed_graph_equals_eager"] = bool(ys.tobytes() == ye.tobytes())
+            parity[f"sign_m{m}_fused_equals_separate"] = bool(yf.tobytes() == ye.tobytes())
             row["separate_us_per_layer"] = round(tss / args.layers * 1e6, 3)
             del ss
             tb_ = min(tfs, tss)
@@ -482,11 +627,42 @@ def main():
     log(f"read probe (4 GiB): {probe:.1f} GB/s")
     gb1 = step_bytes / t1 / 1e9
 
-    cpu = cpu_baseline(layers[:4], xs, args.cpu_seconds)
-    cpu8 = cpu_baseline(layers[:4], xs, args.cpu_seconds / 2, m=8)
-    cpu["m8"] = {"value": cpu8["value"], "unit": cpu8["unit"], "sample": cpu8["sample"]}
-    log(f"cpu oracle: {cpu['value']} GB/s ({cpu['sample']}); M=8 {cpu8['value']} GB/s "
-        f"({cpu8['sample']})")
+    # ---- CPU baseline leg: the oracle on this host, which also checks the timed outputs
+    threads = host_threads(args.cpu_threads)
+    single = cpu_single_thread(layers[:4], xs, args.cpu_seconds)
+    res1, dt1 = cpu_all_cores(layers, xs, 1, threads)
+    ok1, wh1, wy1, f1s = oracle_parity(layers, res1, got1, threads)
+    parity["m1_oracle_all_layers"] = ok1
+    parity["m1_oracle_worst_h_over_bound"] = round(wh1, 4)
+    parity["m1_oracle_worst_y_over_bound"] = round(wy1, 4)
+    if f1s:
+        parity["m1_oracle_failures"] = f1s
+    del res1, got1
+    cpu = {"value": round(step_bytes / dt1 / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"all {args.layers} layers of the stream at M=1, one layer per task on "
+                     f"{threads} threads ({dt1:.1f} s; CPU: {cpu_model()}, "
+                     f"{os.cpu_count()} logical CPUs)",
+           "single_thread": single}
+    log(f"cpu oracle: {cpu['value']} GB/s on {threads} threads ({dt1:.1f} s); single thread "
+        f"{single['value']} GB/s; M=1 parity vs oracle: {ok1} (worst h {wh1:.3g}, "
+        f"y {wy1:.3g} of bound)")
+    if y_sep8 is not None and not args.skip_oracle_m8:
+        res8, dt8 = cpu_all_cores(layers, xs, 8, threads)
+        ok8, wh8, wy8, f8s = oracle_parity(layers, res8, got8, threads)
+        parity["m8_oracle_all_layers"] = ok8
+        parity["m8_oracle_worst_h_over_bound"] = round(wh8, 4)
+        parity["m8_oracle_worst_y_over_bound"] = round(wy8, 4)
+        if f8s:
+            parity["m8_oracle_failures"] = f8s
+        del res8, got8
+        cpu["m8"] = {"value": round(step_bytes / dt8 / 1e9, 4), "unit": "GB/s",
+                     "cores": threads,
+                     "sample": f"all {args.layers} layers at M=8 on {threads} threads ({dt8:.1f} s)"}
+        log(f"cpu oracle M=8: {cpu['m8']['value']} GB/s; M=8 parity vs oracle: {ok8} "
+            f"(worst h {wh8:.3g}, y {wy8:.3g} of bound)")
+    parity_ok = all(v for k, v in parity.items() if isinstance(v, bool))
+    parity["all_ok"] = parity_ok
 
     out = {
         "metric": METRIC,
@@ -523,10 +699,14 @@ def main():
                      "kernel": k_name, "bytes_per_launch": k_bytes,
                      "us_per_launch": round(k_s * 1e6, 3)},
         "cpu_baseline": cpu,
+        "parity_checked": parity,
         "m1_call_breakdown": breakdown,
         "gpu_clocks_amd_smi": clocks,
     }
     print(json.dumps(out), flush=True)
+    if not parity_ok:
+        log("bench.py: a timed output failed its check: " + json.dumps(parity))
+        sys.exit(3)
 
 
 if __name__ == "__main__":

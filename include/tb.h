@@ -21,6 +21,11 @@
  *            the tb_matrix pointers are HOST memory; they are read during the
  *            call only. The library allocates no device memory and keeps no
  *            pointer after it returns.
+ *   State    The only state is a process-wide table, filled on a device's
+ *            first call and guarded by a mutex, of that device's LDS limit and
+ *            compute-unit count, and the kernels whose LDS limit has been
+ *            raised. It never changes a result. Calls from several host
+ *            threads are safe.
  *   Rows     m is the number of activation rows, 1 <= m <= 8. Rows are
  *            independent. Row r's outputs are bit-identical for every m and
  *            for every position r in the batch.
@@ -84,8 +89,8 @@ typedef struct tb_matrix {
     int32_t fmt; /* enum tb_format */
 } tb_matrix;
 
-/* Rotate and quantise activation rows: the "Hadamard rotation emits the int8
- * copy" step (PR #1154, commit message).
+/* Rotate and quantise activation rows: the step that turns the activation into
+ * its rotated int8 copy (PR #1154, commit message).
  * For every row r and 128-block b, with v = x[r][128b .. 128b+127]:
  *   u = H v       unnormalised Walsh-Hadamard transform, H[i][j] =
  *                 (-1)^popcount(i&j). Butterfly stages of span 1, 2, ..., 64
@@ -99,8 +104,9 @@ typedef struct tb_matrix {
  *   dq float [m][k/128] output */
 int tb_rotate_quant_i8(const float *x, int m, int k, int8_t *q, float *dq, void *stream);
 
-/* Ternary (or sign) GEMV: the "dp4a GEMV" with "per-block fold" and
- * "shuffle tree" (PR #1154, commit message).
+/* Ternary (or sign) GEMV: integer dot products per 128-weight block, each
+ * block's scales folded into its integer sum, and a fixed lane tree per row
+ * (PR #1154, commit message).
  *   isum[r][j][b] = sum_i t(j, 128b+i) * q[r][128b+i]          (int32, exact)
  *   y[r][j]       = sum_b scale[j][b] * dq[r][b] * isum[r][j][b]  (fp32 fold)
  *   w  matrix with w->k inputs, w->n outputs, fmt TERNARY2 or SIGN1
@@ -110,9 +116,9 @@ int tb_rotate_quant_i8(const float *x, int m, int k, int8_t *q, float *dq, void 
 int tb_gemv_ternary(const tb_matrix *w, const int8_t *q, const float *dq, int m, float *y,
                     void *stream);
 
-/* Gate and up GEMVs from one shared int8 copy, then the SiLU gate ("the
- * Hadamard rotation emits that int8 copy for gate and up to share", PR #1154,
- * commit message):
+/* Gate and up GEMVs from one shared int8 copy, then the SiLU gate. The two
+ * projections read the same rotated int8 activation, made once per step
+ * (PR #1154, commit message):
  *   g = gemv(wg, q, dq), u = gemv(wu, q, dq), h[r][j] = silu(g) * u with
  *   silu(z) = z / (1 + exp(-z)).
  *   wg, wu  same n, k and fmt
@@ -131,9 +137,18 @@ int tb_ffn_gateup_silu(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q
 int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,
                 float *y, void *stream);
 
-/* Test export: the per-block integer sums of tb_gemv_ternary, from the same
- * decode and dot-product code, before the scale fold.
- *   isum int32 [m][w->n][w->k/128] output */
+/* Test export: the per-block integer sums, before the scale fold, computed by
+ * the integer core that production runs:
+ *   m <= 4, or k/128 not a multiple of 2 (ternary) or 4 (sign): the dot-product
+ *     core (v_dot4), which tb_gemv_ternary and tb_ffn_gateup_silu run for those m;
+ *   m >= 5 otherwise: the matrix-core core (v_mfma_i32_16x16x64_i8), which
+ *     tb_ffn_gateup_silu runs from m = 5 on and tb_gemv_ternary (so tb_ffn_down)
+ *     from m = 6 (ternary) or m = 7 (sign) on.
+ * For a single GEMV at m = 5 (ternary) or m = 5, 6 (sign) production runs the
+ * dot-product core, which this export runs at m <= 4: the same code, templated
+ * on m.
+ *   isum int32 [m][w->n][w->k/128] output; m * n * (k/128) * 4 must be below
+ *   2 GiB (else TB_EUNSUPPORTED). */
 int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream);
 
 /* ---- Fused FFN layers ----------------------------------------------------

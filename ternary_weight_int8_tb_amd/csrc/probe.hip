@@ -3,8 +3,6 @@
 //   tbp_stream_read: reads a device buffer once with 16-byte non-temporal loads (the same
 //                    load the GEMV kernels use) and folds it into one word per workgroup,
 //                    to measure the achievable HBM read bandwidth.
-//   tbp_empty:       an empty single-workgroup kernel, to measure the fixed cost of a
-//                    dependent launch.
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -48,8 +46,6 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4 *__re
     }
 }
 
-__global__ void empty_kernel() {}
-
 }  // namespace
 
 extern "C" {
@@ -63,12 +59,6 @@ int tbp_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, voi
     hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(buf),
                        bytes / 16, sink);
-    return (int)hipGetLastError();
-}
-
-int tbp_empty(void *stream)
-{
-    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream));
     return (int)hipGetLastError();
 }
 

@@ -22,9 +22,12 @@
 //     v_dot4c_i32_i8 against the LDS-staged transposed activation, one DPP add to join the
 //     two half-block sums, an fp32 term per block, a fixed DPP tree per row and step, and
 //     the step partials summed in step order (tb_device.h).
-//   * With M <= 8 rows this is not a dense contraction: the roof is HBM. From M = 6 on,
-//     gate/up hands its integer dot products to v_mfma_i32_16x16x64_i8
-//     (gemv_mfma_kernel), where M dot products per 4 weights would bind the VALU.
+//   * With M <= 8 rows this is not a dense contraction: the roof is HBM. From M = 5 on
+//     gate/up (both formats), and from M = 6 (ternary) or 7 (sign) on the single GEMV,
+//     hand their integer dot products to v_mfma_i32_16x16x64_i8 (gemv_mfma_kernel), where
+//     M dot products per 4 weights would bind the VALU. The block-sum export follows the
+//     gate/up threshold, so it runs the matrix-core integer core at every M where
+//     production does.
 //   * No floating-point atomics.
 #include <hip/hip_runtime.h>
 
@@ -257,7 +260,9 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     constexpr int kWpc = Fmt<FMT>::kWeightsPerChunk;
     constexpr int kCpb = Fmt<FMT>::kChunksPerBlock;
     constexpr int kBlocksPerStep = kChunkLanes / kCpb;   // 8 ternary, 16 sign
-    constexpr int kDepth = kTwo ? kRingDepthTwo : kRingDepthOne;
+    // (the block-sum export runs one item deep: it keeps the sign export's registers below
+    // the 128 a wave has, where two items spilled from M = 4 on)
+    constexpr int kDepth = MODE == kModeIsum ? 1 : kTwo ? kRingDepthTwo : kRingDepthOne;
 
     const int k = a.k, n = a.n, nb = k / kBlock;
     const int C = k / kWpc;                 // chunks per row
@@ -501,6 +506,7 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
     constexpr int kBpl = kBps / 4;            // blocks per 16-byte load of the 4 lanes of a row
     constexpr int kDepth = kMfmaDepth;
     constexpr int kThreads = mfma_threads(FMT), kWaves = kThreads / 64;
+    constexpr bool kIsum = MODE == kModeIsum;
 
     const int k = a.k, n = a.n, nb = k / kBlock;
     const int C = k / Fmt<FMT>::kWeightsPerChunk, I = (C + kChunkLanes - 1) / kChunkLanes;
@@ -518,6 +524,8 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
     int *ctr_s = qsum_s + (kTern ? 0 : (nb + kBps) * M);
     float *part_s = reinterpret_cast<float *>(ctr_s + 4);   // [row - R0][step][m][part]
 
+    const __amdgpu_buffer_rsrc_t rout =
+        buffer_rsrc(a.isum, kIsum ? (uint32_t)((size_t)M * n * nb * 4) : 0u);
     if (tid == 0)
         *ctr_s = kWaves;   // wave w starts with item w
     if (!kTern)
@@ -559,7 +567,7 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
             nbk = min(kBps, nb - gstep * kBps);   // blocks of this step inside the row
             if (row0 + li < R1) {
                 off = lane_off;
-                soff = gstep * kBps + lg * kBpl < nb ? lane_soff : kOutOfRange;
+                soff = (!kIsum && gstep * kBps + lg * kBpl < nb) ? lane_soff : kOutOfRange;
             }
             int v = 0;
             if (lane == 0)
@@ -653,6 +661,21 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
             const int qs = kTern ? 0 : qsum_s[blk * M + mB];
+            if constexpr (kIsum) {
+                // the block-sum export: D's exact sums, before any scale, for the live
+                // activation rows (lanes li < M) of rows inside this workgroup's range
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = R0 + tile * 16 + 4 * lg + r;
+                    const bool wr = li < M && row < R1 && blk < nb;
+                    const int v = kTern ? acc[r] : 2 * acc[r] - qs;
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        (uint32_t)v, rout, wr ? (uint32_t)(((li * n + row) * nb + blk) * 4) : kOutOfRange, 0, 0);
+                }
+                if (!kTern)
+                    __builtin_amdgcn_sched_barrier(0);
+                continue;
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 // the scale of row 4 lg + r and block kb, from the lane that loaded it
@@ -682,7 +705,7 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
             if (!kTern)
                 __builtin_amdgcn_sched_barrier(0);
         }
-        if (li < M) {
+        if (!kIsum && li < M) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int lrow = tile * 16 + 4 * lg + r;   // row - R0
@@ -706,6 +729,8 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
             break;
     }
 
+    if (kIsum)
+        return;
     // ---- every row: its step partials in step order, from +0
     __syncthreads();
     for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
@@ -871,6 +896,15 @@ struct DeviceInfo {
 };
 std::mutex g_mu;
 DeviceInfo g_dev[kMaxDevices];
+// Kernels whose dynamic LDS limit has been raised, per device, with the limit set: the
+// attribute is set once per kernel and size instead of on every launch.
+constexpr int kMaxRaised = 512;
+struct Raised {
+    const void *fn;
+    int lds;
+};
+Raised g_raised[kMaxDevices][kMaxRaised];
+int g_nraised[kMaxDevices];
 
 int device_info(DeviceInfo *out)
 {
@@ -942,15 +976,33 @@ size_t block_terms_bytes(int fmt, int m, int nb)
     return (size_t)m * nb * 4 * (fmt == TB_FMT_TERNARY2 ? 1 : 2);
 }
 
-int set_lds(GemvFn fn, size_t lds)
+// Raise fn's dynamic LDS limit to at least lds bytes on the current device (once).
+int raise_lds(const void *fn, size_t lds)
 {
     if (lds <= 65536)
         return TB_OK;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess
-               ? TB_OK
-               : TB_EHIP;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return TB_EHIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    Raised *tab = g_raised[dev];
+    int &cnt = g_nraised[dev];
+    for (int i = 0; i < cnt; ++i)
+        if (tab[i].fn == fn && tab[i].lds >= (int)lds)
+            return TB_OK;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return TB_EHIP;
+    for (int i = 0; i < cnt; ++i)
+        if (tab[i].fn == fn) {
+            tab[i].lds = (int)lds;
+            return TB_OK;
+        }
+    if (cnt < kMaxRaised)
+        tab[cnt++] = Raised{fn, (int)lds};
+    return TB_OK;
 }
+
+int set_lds(GemvFn fn, size_t lds) { return raise_lds(reinterpret_cast<const void *>(fn), lds); }
 
 int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t *q,
                 const float *dq, int m, float *out, int32_t *isum, hipStream_t stream)
@@ -986,17 +1038,21 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     // batched rows: the matrix-core kernel, when its LDS plan fits (a lane's scale load
     // holds whole block pairs (ternary) or quads (sign) of one row)
     const bool tern = w0->fmt == TB_FMT_TERNARY2;
-    if (nb % (tern ? 2 : 4) == 0 && mode != kModeIsum &&
-        m >= mfma_min_rows(tern, mode == kModeGateUp)) {
+    // The block-sum export takes the matrix-core route from the gate/up threshold on (the
+    // smallest M at which production runs the matrix-core integer core, which is the same
+    // code in gate/up and one-matrix mode).
+    if (nb % (tern ? 2 : 4) == 0 && m >= mfma_min_rows(tern, mode != kModeY)) {
         const size_t rows_cu = (size_t)((tiles + ring_grid - 1) / ring_grid) * kRowsPerWave;
         const size_t bps = tern ? 8 : 16;
         const size_t mfma_lds = (size_t)steps * step_bytes + (size_t)m * (nb + bps) * 4 * (tern ? 1 : 2) +
                                 16 + rows_cu * steps * m * (mode == kModeGateUp ? 2 : 1) * 4;
         if (mfma_lds <= (size_t)info.lds_limit) {
             GemvFn fn = tern ? (mode == kModeGateUp ? gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
-                                                    : gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeY>(m))
+                                : mode == kModeY  ? gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeY>(m)
+                                                  : gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeIsum>(m))
                              : (mode == kModeGateUp ? gemv_mfma_pick_m<TB_FMT_SIGN1, kModeGateUp>(m)
-                                                    : gemv_mfma_pick_m<TB_FMT_SIGN1, kModeY>(m));
+                                : mode == kModeY  ? gemv_mfma_pick_m<TB_FMT_SIGN1, kModeY>(m)
+                                                  : gemv_mfma_pick_m<TB_FMT_SIGN1, kModeIsum>(m));
             if (!fn)
                 return TB_EINVAL;
             if ((rc = set_lds(fn, mfma_lds)))
@@ -1227,6 +1283,9 @@ int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum
         return TB_EINVAL;
     if (!aligned16(q) || !aligned16(isum))
         return TB_EALIGN;
+    // the sums are written with 32-bit buffer offsets
+    if ((size_t)m * w->n * (w->k / kBlock) * 4 >= ((size_t)1 << 31))
+        return TB_EUNSUPPORTED;
     const Range ri = range_of(isum, (size_t)m * w->n * (w->k / kBlock) * 4);
     if (overlaps(ri, range_of(w->codes, codes_bytes(w))) ||
         overlaps(ri, range_of(w->scales, scales_bytes(w))) ||
@@ -1315,10 +1374,8 @@ int tb_ffn_layers(const tb_ffn_weights *layers, int num_layers, const float *x, 
     LayersFn fn = F == TB_FMT_TERNARY2 ? layers_pick_m<TB_FMT_TERNARY2>(m) : layers_pick_m<TB_FMT_SIGN1>(m);
     if (!fn)
         return TB_EINVAL;
-    if (plan.total > 65536 &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            plan.total) != hipSuccess)
-        return TB_EHIP;
+    if ((rc = raise_lds(reinterpret_cast<const void *>(fn), (size_t)plan.total)))
+        return rc;
 
     uint8_t *wsb = static_cast<uint8_t *>(ws);
     tbl::LArgs a;

@@ -5,11 +5,10 @@
 // row is fixed by its shape alone: in step i lane cl holds chunk 16 i + cl; the step's
 // partial is the fixed 16-lane row tree of the lanes' terms (scale * dq) * isum; the row's
 // output is the sum of its step partials in step order, starting from +0. Neither the
-// row count M, nor the kernel, nor which wave ran which step changes it. The pages state
-// the property this gives for the batched kernel ("perf(bonsai): decode and small packed
-// batches read the FFN from a ternary copy through a dp4a GEMV", sparkinfer PR #1154,
-// commit message): each row's lane walk, per-block fold and shuffle tree are unchanged,
-// so a batched row is bit-identical to its single-row run.
+// row count M, nor the kernel, nor which wave ran which step changes it. That is what
+// makes a batched row bit-identical to the same row run alone, the property the pages
+// claim for their batched kernel ("perf(bonsai): decode and small packed batches read the
+// FFN from a ternary copy through a dp4a GEMV", sparkinfer PR #1154, commit message).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -604,8 +603,18 @@ __device__ __forceinline__ void chunk_sums_step(const uint4 &w0, const uint4 &w1
                     is1[m] = dot4(b1[3], av.w, is1[m]);
                 }
             }
-            if (M >= 4)
+            if (M >= 4) {
+                // Pin this plane's dot products before the barrier: they are pure
+                // operations, which the IR passes may otherwise sink below every plane (as
+                // they did in the block-sum export, keeping all 8 planes' reads live).
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    asm volatile("" : "+v"(is0[m]));
+                    if (TWO)
+                        asm volatile("" : "+v"(is1[m]));
+                }
                 __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 }

@@ -101,7 +101,10 @@ def chain_bounds(h_ref, tol_h, qh_or, dqh_or, isum_or, t_abs, scales, unit):
     d_dq = np.maximum(dq_hi - dqh_or, dqh_or - dq_lo)                   # [m][nb]
     extra = np.einsum("nb,rnb->rn", scales, np.abs(isum_or) * d_dq[:, None, :])
     wdev = np.maximum(q_hi - q_or, q_or - q_lo)                          # [m][k]
-    for r, kk in zip(*np.nonzero(wdev)):
-        b = kk // 128
-        extra[r] += scales[:, b] * dq_hi[r, b] * wdev[r, kk] * t_abs[:, kk]
+    # + sum over codes kk that may move: s[n][b] * dq_hi[r][b] * wdev[r][kk] * |t[n][kk]|,
+    # one block b = kk // 128 at a time as a product over its 128 codes
+    wb = wdev.reshape(m, nb, 128) * dq_hi[:, :, None]                   # [m][nb][128]
+    for b in np.nonzero(wb.any(axis=(0, 2)))[0]:
+        tb_ = t_abs[:, b * 128:(b + 1) * 128].astype(np.float64)         # [n][128]
+        extra += (tb_ @ wb[:, b, :].T).T * scales[:, b][None, :]
     return q_lo, q_hi, dq_lo, dq_hi, extra

@@ -108,6 +108,30 @@ def test_block_sums_and_gemv(o, fmt, n, k, m):
     assert ok
 
 
+@pytest.fixture(scope="module")
+def full_mats():
+    """The two FFN matrix shapes (gate/up 17408x5120, down 5120x17408) in both formats."""
+    return {(fmt, n, k): synth.matrix(fmt, n, k, 21, 0, synth.T_GATE)
+            for fmt in (TERN, SIGN) for (n, k) in ((synth.INTER, synth.HIDDEN),
+                                                   (synth.HIDDEN, synth.INTER))}
+
+
+@pytest.mark.parametrize("fmt", [TERN, SIGN])
+@pytest.mark.parametrize("n,k", [(synth.INTER, synth.HIDDEN), (synth.HIDDEN, synth.INTER)])
+@pytest.mark.parametrize("m", [5, 6, 7, 8])
+def test_block_sums_matrix_core_full_shape(o, full_mats, fmt, n, k, m):
+    # From M = 5 on the export runs the matrix-core integer core (v_mfma_i32_16x16x64_i8,
+    # lane swaps, the D layout) that gate/up and the down GEMV run in production; its sums
+    # must equal the oracle's bit for bit at the FFN shapes.
+    say(f"block sums (matrix cores) fmt={fmt} n={n} k={k} m={m}")
+    w = full_mats[(fmt, n, k)]
+    x = (synth.student_t_rows if fmt == SIGN else synth.normal_rows)(m, k, 22 + m, 0)
+    q, _ = o.rotate_quant(x)
+    got = gu.block_sums(tb.Matrix.upload(w), q)
+    want = o.block_sums(w, q)
+    assert np.array_equal(got, want), f"block sums differ at {np.argwhere(got != want)[:5]}"
+
+
 @pytest.mark.parametrize("fmt", [TERN, SIGN])
 def test_sliced_and_streaming_kernels_fold_alike(o, fmt):
     # k = 24576: at M=8 the activation does not fit in LDS, so the sliced kernel runs; the
