@@ -76,6 +76,17 @@ constexpr int kRingDepthOne = TB_RING_DEPTH_ONE;   // one matrix
 // at depth 1 against 19.7 at depth 2, one matrix 18.9 against 20.2; sign gate/up, which
 // fits 12 waves only at depth 1, 17.3-17.8 there against 19.8-20.8 at depth 2 on 8 waves)
 constexpr int kMfmaDepth = TB_MFMA_DEPTH;
+#ifndef TB_STAGE_FIRST
+#define TB_STAGE_FIRST 0
+#endif
+#ifndef TB_PACK_DEPTH
+#define TB_PACK_DEPTH 1
+#endif
+// items in flight per wave in gemv_mfma_pack_kernel
+constexpr int kPackDepth = TB_PACK_DEPTH;
+#ifndef TB_PACK_SIGN_WAVES
+#define TB_PACK_SIGN_WAVES 12
+#endif
 // M from which a GEMV runs on the matrix cores, per weight format, for gate/up and for one
 // matrix (tb_gemv_ternary, the down GEMV). The MFMA kernel takes about the same time for
 // every M, the dot-product kernel grows with M; the crossings measured at the FFN shapes
@@ -83,6 +94,10 @@ constexpr int kMfmaDepth = TB_MFMA_DEPTH;
 // the dot-product kernel is 0.5-1 µs faster), ternary down (with the rotation of h) 17.8
 // against 18.6 at M = 6, sign down 18.6 against 19.3 at M = 7, sign gate/up 17.1-17.4
 // against 18.2-19.7 at M = 5 (a tie at M = 4).
+// matrix-core GEMV with two blocks per MFMA for M <= 8 (gemv_mfma_pack_kernel)
+#ifndef TB_MFMA_PACK
+#define TB_MFMA_PACK 1
+#endif
 #ifndef TB_MFMA_MIN_ROWS_TERN
 #define TB_MFMA_MIN_ROWS_TERN 5
 #endif
@@ -220,7 +235,9 @@ __device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act
         const int i = tid + r * NTHREADS, b = i / M, m = i % M;
         dv[r] = (MODE != kModeIsum && i < nterm && b < nb) ? a.dq[m * nb + b] : 0.0f;
     }
+#if !TB_STAGE_FIRST
     prologue();
+#endif
 #pragma unroll
     for (int r = 0; r < kStageRound; ++r)
         if (tid + r * NTHREADS < units)
@@ -229,6 +246,9 @@ __device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act
     for (int r = 0; r < kTermRound; ++r)
         if (tid + r * NTHREADS < nterm)
             dq_s[tid + r * NTHREADS] = dv[r];
+#if TB_STAGE_FIRST
+    prologue();
+#endif
 }
 
 // ------------------------------------------------------------------------------------
@@ -459,6 +479,14 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
 // 16-block steps need 156-160 registers, more than the 128 a wave has at 16 waves per CU
 // (sign down at M=8: 17.7-17.8 µs at 12 waves against 18.9-19.1 at 8).
 __host__ __device__ constexpr int mfma_threads(int fmt) { return fmt == TB_FMT_TERNARY2 ? 1024 : 768; }
+// Threads per workgroup of gemv_mfma_pack_kernel.
+#ifndef TB_PACK_TERN_WAVES
+#define TB_PACK_TERN_WAVES 16
+#endif
+__host__ __device__ constexpr int pack_threads(int fmt)
+{
+    return fmt == TB_FMT_TERNARY2 ? 64 * TB_PACK_TERN_WAVES : 64 * TB_PACK_SIGN_WAVES;
+}
 
 // ------------------------------------------------------------------------------------
 // Batched streaming GEMV on the matrix cores (ternary and sign weights, M >= 5 to 7 rows).
@@ -747,6 +775,339 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
 }
 
 // ------------------------------------------------------------------------------------
+// Batched streaming GEMV on the matrix cores with two blocks per MFMA (2 <= M <= 8 rows).
+// The B operand of v_mfma_i32_16x16x64_i8 has 16 columns; with M <= 8 activation rows,
+// columns 0..7 carry the rows of one block of a pair and columns 8..15 those of the other.
+// The A operand's lane groups split the same way (groups 0, 1: k 0..31, the first block;
+// groups 2, 3: k 32..63, the second), and the B lanes of the other block read zeros, so
+// after four MFMAs D holds both blocks' exact integer sums for 16 weight rows and M
+// activation rows, with no unused column. The fold (block terms and step tree) then costs
+// half of what a 16-column D with M live columns would.
+//   * Ternary: lane (i, g) loads 16 code bytes of row i per load q, chunk 4 q + g: half g & 1
+//     of block 2 q + (g >> 1). That is the pair (2 q, 2 q + 1) split as above, so the code
+//     words go to the MFMAs as loaded, decoded by v_perm_b32. The step tree
+//     ((t0 + t7) + (t6 + t5)) + ((t4 + t3) + (t2 + t1)) takes the odd blocks' terms from the
+//     lane eight columns over (DPP row rotate by 8).
+//   * Sign: the pairs are (e, e - 1 mod 16) for even e, the first level of the sign step
+//     tree. Lane group g loads the whole block {4 q, 4 q + 2, 4 q - 1, 4 q + 1}[g] per load q;
+//     one v_permlane16_swap per dword pair (odd 16-lane rows of the first operand with even
+//     rows of the second) leaves every lane 64 weights of each of the load's two pairs:
+//     even groups dwords 2, 3 and odd groups dwords 0, 1 of their block.
+//   * Block scales: each lane loads the scale word(s) of the blocks its code load covers;
+//     a per-wave LDS scratch laid out [block][row] then gives each D lane its four rows'
+//     scales in one 8-byte read.
+// Rows, items, the ring and the step sum are those of gemv_mfma_kernel, and the fold order
+// is the one every kernel here uses, so a batched row is bit-identical to the row alone.
+// ------------------------------------------------------------------------------------
+// LDS carve-up of gemv_mfma_pack_kernel, shared with the host (16-byte aligned sections):
+// the activation (MFMA layout), block terms dq [b][m], code sums (sign), the item counter,
+// a zero region read as B by inactive lanes, per-wave scale scratch, then the step partials.
+constexpr int kPackZeroBytes = 1024;
+// per wave: the scales of one item, [block in step][row in tile] as uint16
+__host__ __device__ constexpr int pack_scratch_bytes(int fmt) { return (fmt == TB_FMT_TERNARY2 ? 8 : 16) * 16 * 2; }
+struct PackLds {
+    size_t dq, qsum, ctr, zero, scratch, part;
+};
+__host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+__host__ __device__ inline PackLds pack_lds(int M, int fmt, int k, int waves)
+{
+    const bool tern = fmt == TB_FMT_TERNARY2;
+    const int wpc = tern ? 64 : 128, bps = tern ? 8 : 16, nb = k / 128;
+    const int I = (k / wpc + 15) / 16;
+    PackLds p;
+    p.dq = (size_t)I * (tern ? 1024 : 2048) * M;
+    p.qsum = align16(p.dq + (size_t)(nb + bps) * M * 4);
+    p.ctr = align16(p.qsum + (tern ? 0 : (size_t)(nb + bps) * M * 4));
+    p.zero = align16(p.ctr + 16);
+    p.scratch = p.zero + kPackZeroBytes;
+    p.part = p.scratch + (size_t)waves * pack_scratch_bytes(fmt);
+    return p;
+}
+
+template <int M, int FMT, int MODE>
+__global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(GemvArgs a)
+{
+    static_assert(M >= 1 && M <= 8, "two blocks per MFMA: at most 8 activation rows");
+    extern __shared__ __align__(16) uint8_t lds[];
+    using L = StepLayout<M, FMT>;
+    constexpr bool kTern = FMT == TB_FMT_TERNARY2;
+    constexpr bool kTwo = MODE == kModeGateUp;
+    constexpr bool kIsum = MODE == kModeIsum;
+    constexpr int kParts = kTwo ? 2 : 1;
+    constexpr int kMatShift = kTwo ? 1 : 0;   // gate/up: item = ((tile, step), matrix)
+    constexpr int kBps = kTern ? 8 : 16;      // blocks per step (256 code bytes per row)
+    constexpr int kBpl = kBps / 4;            // blocks per scale load of one lane
+    constexpr int kDepth = kPackDepth;
+    constexpr int kThreads = pack_threads(FMT), kWaves = kThreads / 64;
+    constexpr int kScratch = pack_scratch_bytes(FMT);   // per wave: scales [block][row], uint16
+
+    const int k = a.k, n = a.n, nb = k / kBlock;
+    const int C = k / Fmt<FMT>::kWeightsPerChunk, I = (C + kChunkLanes - 1) / kChunkLanes;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = gridDim.x, c = blockIdx.x;
+    const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
+    const int R0 = part_lo(T, G, c) * kRowsPerWave;
+    const int R1 = min(part_lo(T, G, c + 1) * kRowsPerWave, n);
+    const int J = (((R1 - R0 + 15) / 16) * I) << kMatShift;   // this workgroup's items
+    const uint32_t row_bytes = (uint32_t)C * 16u;
+
+    const PackLds pl = pack_lds(M, FMT, k, kWaves);
+    uint8_t *act = lds;
+    float *dq_s = reinterpret_cast<float *>(lds + pl.dq);
+    int *qsum_s = reinterpret_cast<int *>(lds + pl.qsum);
+    int *ctr_s = reinterpret_cast<int *>(lds + pl.ctr);
+    const uint8_t *zero_s = lds + pl.zero;                                     // B of inactive lanes
+    uint16_t *sc_s = reinterpret_cast<uint16_t *>(lds + pl.scratch + wave * kScratch);
+    float *part_s = reinterpret_cast<float *>(lds + pl.part);   // [row - R0][step][m][part]
+
+    const __amdgpu_buffer_rsrc_t rout =
+        buffer_rsrc(a.isum, kIsum ? (uint32_t)((size_t)M * n * nb * 4) : 0u);
+    if (tid == 0)
+        *ctr_s = kWaves;   // wave w starts with item w
+    for (int i = tid; i < kPackZeroBytes / 4; i += kThreads)
+        reinterpret_cast<uint32_t *>(lds + pl.zero)[i] = 0u;
+    if (!kTern)
+        for (int i = tid; i < (nb + kBps) * M; i += kThreads)
+            qsum_s[i] = 0;
+    __syncthreads();
+
+    int gidx = 0, gtile = 0, gstep = 0;
+    auto advance_to = [&](int idx) {
+        gstep += idx - gidx;
+        gidx = idx;
+        while (gstep >= I) {
+            gstep -= I;
+            ++gtile;
+        }
+    };
+    // Code loads: ternary lane (i, g) reads bytes 64 q + 16 g .. + 15 of its row's step (load
+    // q = 0..3); sign lane (i, g) reads block bq(g) = {4 q, 4 q + 2, 4 q - 1 mod 16, 4 q + 1}[g].
+    // In sign load q, group 2 reads 16 bytes before the others' base, except in load 0, where
+    // its block 15 lies 240 bytes after it.
+    const int sgofs = lg == 0 ? 0 : lg == 1 ? 32 : lg == 2 ? -16 : 16;
+    const uint32_t lane_off = (uint32_t)li * row_bytes + (uint32_t)(kTern ? lg * 16 : sgofs + (lg == 2 ? 256 : 0));
+    auto code_block = [&](int q) -> int {   // sign: the block (in the step) of this lane's load q
+        return lg == 0 ? 4 * q : lg == 1 ? 4 * q + 2 : lg == 2 ? ((4 * q + 15) & 15) : 4 * q + 1;
+    };
+    // Scale loads: the word (ternary) or two words (sign) holding the scales of blocks
+    // kBpl g .. of row i.
+    const uint32_t lane_soff = ((uint32_t)li * (uint32_t)nb + (uint32_t)(lg * kBpl)) * 2u;
+    uint4 rc[kDepth][4];
+    u32x2 rs[kDepth];
+    int rit[kDepth];   // matrix << 30 | tile << 16 | step, or -1
+    int pending = tid >> 6;
+    auto issue = [&](int d) {
+        const int idx = __builtin_amdgcn_readfirstlane(pending);
+        uint32_t off = kOutOfRange, soff = kOutOfRange;
+        int so = 0, sso = 0, nbk = 0, mat = 0;
+        rit[d] = -1;
+        if (idx < J) {
+            advance_to(idx >> kMatShift);
+            mat = idx & (kTwo ? 1 : 0);
+            rit[d] = mat << 30 | gtile << 16 | gstep;
+            const int row0 = R0 + gtile * 16;
+            so = row0 * (int)row_bytes + gstep * 256;
+            sso = (row0 * nb + gstep * kBps) * 2;
+            nbk = min(kBps, nb - gstep * kBps);   // blocks of this step inside the row
+            if (row0 + li < R1) {
+                off = lane_off;
+                soff = (!kIsum && gstep * kBps + lg * kBpl < nb) ? lane_soff : kOutOfRange;
+            }
+            int v = 0;
+            if (lane == 0)
+                v = atomicAdd(ctr_s, 1);
+            pending = v;
+        }
+        const __amdgpu_buffer_rsrc_t rcm = buffer_rsrc(mat ? a.codes1 : a.codes0, a.codes_bytes);
+        const __amdgpu_buffer_rsrc_t rsm = buffer_rsrc(mat ? a.scales1 : a.scales0, a.scales_bytes);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t o;
+            if (kTern) {
+                // (nbk is even: both blocks of a load are in or out)
+                o = 2 * q < nbk ? off + (uint32_t)q * 64u : kOutOfRange;
+            } else {
+                // (nbk is a multiple of 4; load 0's group 2 reads block 15)
+                const uint32_t extra = (lg == 2 && q > 0) ? 256u : 0u;
+                o = code_block(q) < nbk ? off + (uint32_t)q * 64u - extra : kOutOfRange;
+                if (off == kOutOfRange)
+                    o = kOutOfRange;
+            }
+            rc[d][q] = buffer_load16(rcm, o, so);
+        }
+        if (kTern) {
+            rs[d].x = buffer_load_u32(rsm, soff, sso);
+            rs[d].y = 0u;
+        } else {
+            rs[d] = __builtin_amdgcn_raw_buffer_load_b64(rsm, soff, sso, 0);
+        }
+    };
+
+    stage_activation<M, FMT, MODE, kThreads, true>(a, act, dq_s, qsum_s, [&]() {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+            issue(d);
+    });
+    __syncthreads();
+
+    // ---- compute side
+    const int col = li, hsel = col >> 3, mcol = col & 7;
+    const int mB = mcol < M ? mcol : M - 1;            // dq / code-sum row of this D column
+    // this lane's B: the columns of its block half, rows < M; others read the zero region
+    const bool bval = hsel == (lg >> 1) && mcol < M;
+    auto consume = [&](int d) {
+        const int mat = rit[d] >> 30, tile = (rit[d] >> 16) & 0x3fff, step = rit[d] & 0xffff;
+        // this item's scales to the wave's scratch, [block in step][row in tile]
+        if (!kIsum) {
+            if (kTern) {
+                sc_s[(2 * lg) * 16 + li] = (uint16_t)(rs[d].x & 0xffffu);
+                sc_s[(2 * lg + 1) * 16 + li] = (uint16_t)(rs[d].x >> 16);
+            } else {
+                sc_s[(4 * lg) * 16 + li] = (uint16_t)(rs[d].x & 0xffffu);
+                sc_s[(4 * lg + 1) * 16 + li] = (uint16_t)(rs[d].x >> 16);
+                sc_s[(4 * lg + 2) * 16 + li] = (uint16_t)(rs[d].y & 0xffffu);
+                sc_s[(4 * lg + 3) * 16 + li] = (uint16_t)(rs[d].y >> 16);
+            }
+        }
+        const uint8_t *sact = act + (size_t)step * L::kStepBytes;
+        constexpr int kPairs = kBps / 2;
+        float t[kPairs][4];
+        // one block pair: 4 MFMAs, then the terms of D
+        auto pair = [&](int p, int blk_hi, const uint8_t *bbase, auto &&a_operand) {
+            v4i acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                v4i av, bv;
+                a_operand(s, av, bv, bbase);
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
+            }
+            const int blk = step * kBps + blk_hi;   // this lane's D block
+            const int qs = kTern ? 0 : qsum_s[blk * M + mB];
+            if constexpr (kIsum) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = R0 + tile * 16 + 4 * lg + r;
+                    const bool wr = mcol < M && row < R1 && blk < nb;
+                    const int v = kTern ? acc[r] : 2 * acc[r] - qs;
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        (uint32_t)v, rout, wr ? (uint32_t)(((mcol * n + row) * nb + blk) * 4) : kOutOfRange, 0, 0);
+                }
+            } else {
+                const float dqv = dq_s[blk * M + mB];
+                const uint2 sw = *reinterpret_cast<const uint2 *>(sc_s + (blk - step * kBps) * 16 + 4 * lg);
+                const uint32_t s4[2] = {sw.x, sw.y};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sv = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(s4[r >> 1], (r & 1) * 16, 16));
+                    const int isum = kTern ? acc[r] : 2 * acc[r] - qs;
+                    t[p][r] = (sv * dqv) * (float)isum;
+                }
+            }
+        };
+        if constexpr (kTern) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t cw[4] = {rc[d][q].x, rc[d][q].y, rc[d][q].z, rc[d][q].w};
+                // B: chunk 4 q + g, code word s, row mB: [chunk][word][row] x 16 bytes
+                const uint8_t *bb = bval ? sact + ((size_t)((4 * q + lg) * 4) * M + mB) * 16 : zero_s;
+                pair(q, 2 * q + hsel, bb, [&](int s, v4i &av, v4i &bv, const uint8_t *b) {
+                    uint32_t d0, d1, d2, d3;
+                    decode_ternary(cw[s], d0, d1, d2, d3);
+                    av = v4i{(int)d0, (int)d1, (int)d2, (int)d3};
+                    bv = *reinterpret_cast<const v4i *>(b + s * M * 16);
+                });
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // pair A = (4 q, 4 q - 1) in H', pair B = (4 q + 2, 4 q + 1) in L'
+                const u32x2 s0 = __builtin_amdgcn_permlane16_swap(rc[d][q].z, rc[d][q].x, false, false);
+                const u32x2 s1 = __builtin_amdgcn_permlane16_swap(rc[d][q].w, rc[d][q].y, false, false);
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const uint32_t dw[2] = {h2 == 0 ? s0.x : s0.y, h2 == 0 ? s1.x : s1.y};
+                    const int e = 4 * q + 2 * h2;                       // the pair's even block
+                    const int myblk = (lg < 2) ? e : ((e + 15) & 15);   // this lane's A block
+                    const int dblk = hsel == 0 ? e : ((e + 15) & 15);   // this lane's D block
+                    // B: block myblk, dword (odd group: 0, 1; even group: 2, 3) + s, half h
+                    const int dbase = (lg & 1) ? 0 : 2;
+                    const uint8_t *bb =
+                        bval ? sact + ((size_t)(2 * (4 * myblk + dbase)) * M + mB) * 16 : zero_s;
+                    pair(2 * q + h2, dblk, bb, [&](int s, v4i &av, v4i &bv, const uint8_t *b) {
+                        const uint32_t w = dw[s >> 1];
+                        const int h = s & 1;
+                        av = v4i{(int)((w >> (4 * h + 0)) & 0x01010101u), (int)((w >> (4 * h + 1)) & 0x01010101u),
+                                 (int)((w >> (4 * h + 2)) & 0x01010101u), (int)((w >> (4 * h + 3)) & 0x01010101u)};
+                        // dword dbase + (s >> 1), half h: slots (2 * (4 blk + dword) + h) * M + m
+                        bv = *reinterpret_cast<const v4i *>(b + (size_t)(2 * (s >> 1) + h) * M * 16);
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        if constexpr (!kIsum) {
+            float tot[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (kTern) {
+                    // pairs p = (2p, 2p + 1); even lanes hold t(2p), the lane 8 over t(2p + 1)
+                    const float P3 = t[0][r] + row_down(t[3][r], 8);   // t0 + t7
+                    const float P2 = t[3][r] + row_down(t[2][r], 8);   // t6 + t5
+                    const float P1 = t[2][r] + row_down(t[1][r], 8);   // t4 + t3
+                    const float P0 = t[1][r] + row_down(t[0][r], 8);   // t2 + t1
+                    tot[r] = (P3 + P2) + (P1 + P0);
+                } else {
+                    // pair p = 2 q + h2 has blocks (2p, 2p - 1): P_2p = t(2p) + t(2p - 1)
+                    float P[8];
+#pragma unroll
+                    for (int p = 0; p < 8; ++p)
+                        P[p] = t[p][r] + row_down(t[p][r], 8);
+                    tot[r] = ((P[0] + P[7]) + (P[6] + P[5])) + ((P[4] + P[3]) + (P[2] + P[1]));
+                }
+            }
+            if (hsel == 0 && mcol < M) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int lrow = tile * 16 + 4 * lg + r;   // row - R0
+                    if (R0 + lrow < R1)
+                        part_s[((size_t)(lrow * I + step) * M + mcol) * kParts + mat] = tot[r];
+                }
+            }
+        }
+    };
+    for (;;) {
+        bool any = false;
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            if (rit[d] >= 0) {
+                consume(d);
+                any = true;
+            }
+            issue(d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!any)
+            break;
+    }
+    if (kIsum)
+        return;
+    // ---- every row: its step partials in step order, from +0
+    __syncthreads();
+    for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
+        const int lrow = i / M, m = i % M;
+        const float *ps = part_s + ((size_t)lrow * I * M + m) * kParts;
+        float g = 0.0f, u = 0.0f;
+        for (int st = 0; st < I; ++st) {
+            g += ps[(size_t)st * M * kParts];
+            if (kTwo)
+                u += ps[(size_t)st * M * kParts + 1];
+        }
+        a.out[(size_t)m * n + R0 + lrow] = kTwo ? silu_gate(g, u) : g;
+    }
+}
+
+// ------------------------------------------------------------------------------------
 // Sliced GEMV: for a K * M too large to stage at once. The activation is staged in
 // slices of S chunks; each workgroup covers 16 rows. The per-row arithmetic is the same
 // as in the ring kernel: lane cl folds chunks 16 i + cl in order of i.
@@ -885,9 +1246,23 @@ GemvFn gemv_mfma_pick_m(int m)
     default: return nullptr;
     }
 }
-static_assert(mfma_min_rows(true, true) >= 4 && mfma_min_rows(true, false) >= 4 &&
-                  mfma_min_rows(false, true) >= 4 && mfma_min_rows(false, false) >= 4,
-              "gemv_mfma_kernel is instantiated for M = 4 .. 8");
+template <int FMT, int MODE>
+GemvFn gemv_mfma_pack_pick_m(int m)
+{
+    switch (m) {
+    case 2: return gemv_mfma_pack_kernel<2, FMT, MODE>;
+    case 3: return gemv_mfma_pack_kernel<3, FMT, MODE>;
+    case 4: return gemv_mfma_pack_kernel<4, FMT, MODE>;
+    case 5: return gemv_mfma_pack_kernel<5, FMT, MODE>;
+    case 6: return gemv_mfma_pack_kernel<6, FMT, MODE>;
+    case 7: return gemv_mfma_pack_kernel<7, FMT, MODE>;
+    case 8: return gemv_mfma_pack_kernel<8, FMT, MODE>;
+    default: return nullptr;
+    }
+}
+static_assert(mfma_min_rows(true, true) >= 2 && mfma_min_rows(true, false) >= 2 &&
+                  mfma_min_rows(false, true) >= 2 && mfma_min_rows(false, false) >= 2,
+              "gemv_mfma_pack_kernel is instantiated for M = 2 .. 8");
 
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
@@ -1044,8 +1419,28 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     if (nb % (tern ? 2 : 4) == 0 && m >= mfma_min_rows(tern, mode != kModeY)) {
         const size_t rows_cu = (size_t)((tiles + ring_grid - 1) / ring_grid) * kRowsPerWave;
         const size_t bps = tern ? 8 : 16;
+        const size_t parts = rows_cu * steps * m * (mode == kModeGateUp ? 2 : 1) * 4;
+#if TB_MFMA_PACK
+        // two blocks per MFMA (every M here is at most 8)
+        const size_t pack_lds_bytes =
+            pack_lds(m, w0->fmt, w0->k, pack_threads(w0->fmt) / 64).part + parts;
+        if (pack_lds_bytes <= (size_t)info.lds_limit) {
+            GemvFn fn = tern ? (mode == kModeGateUp ? gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
+                                : mode == kModeY  ? gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeY>(m)
+                                                  : gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeIsum>(m))
+                             : (mode == kModeGateUp ? gemv_mfma_pack_pick_m<TB_FMT_SIGN1, kModeGateUp>(m)
+                                : mode == kModeY  ? gemv_mfma_pack_pick_m<TB_FMT_SIGN1, kModeY>(m)
+                                                  : gemv_mfma_pack_pick_m<TB_FMT_SIGN1, kModeIsum>(m));
+            if (!fn)
+                return TB_EINVAL;
+            if ((rc = set_lds(fn, pack_lds_bytes)))
+                return rc;
+            hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(pack_threads(w0->fmt)), pack_lds_bytes, stream, a);
+            return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+        }
+#endif
         const size_t mfma_lds = (size_t)steps * step_bytes + (size_t)m * (nb + bps) * 4 * (tern ? 1 : 2) +
-                                16 + rows_cu * steps * m * (mode == kModeGateUp ? 2 : 1) * 4;
+                                16 + parts;
         if (mfma_lds <= (size_t)info.lds_limit) {
             GemvFn fn = tern ? (mode == kModeGateUp ? gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
                                 : mode == kModeY  ? gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeY>(m)
