@@ -60,6 +60,7 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--skip-sign", action="store_true")
     p.add_argument("--skip-m8", action="store_true")
+    p.add_argument("--skip-batch", action="store_true", help="no M=16 / M=32 stream")
     p.add_argument("--cpu-seconds", type=float, default=8.0,
                    help="target CPU time of the single-thread oracle sample")
     p.add_argument("--cpu-threads", type=int, default=0,
@@ -82,8 +83,8 @@ class Stream64:
     Every layer writes its own q, dq, h, rotquant(h) and y (the same kernels and bytes as
     with shared buffers), so all of a timed step's intermediates can be checked after it."""
 
-    def __init__(self, tb, layers_dev, xs, m, torch):
-        self.tb, self.layers, self.m = tb, layers_dev, m
+    def __init__(self, tb, layers_dev, xs, m, torch, batch=False):
+        self.tb, self.layers, self.m, self.batch = tb, layers_dev, m, batch
         dev = "cuda"
         k = layers_dev[0][0].k
         n = layers_dev[0][0].n
@@ -98,6 +99,12 @@ class Stream64:
 
     def step(self):
         tb = self.tb
+        if self.batch:   # the *_batch calls (up to 32 rows)
+            for l, (wg, wu, wd) in enumerate(self.layers):
+                tb.tb_rotate_quant_i8_batch(self.x[l], self.q[l], self.dq[l])
+                tb.tb_ffn_gateup_silu_batch(wg, wu, self.q[l], self.dq[l], self.h[l])
+                tb.tb_ffn_down_batch(wd, self.h[l], self.qh[l], self.dqh[l], self.y[l])
+            return
         for l, (wg, wu, wd) in enumerate(self.layers):
             tb.tb_rotate_quant_i8(self.x[l], self.q[l], self.dq[l])
             tb.tb_ffn_gateup_silu(wg, wu, self.q[l], self.dq[l], self.h[l])
@@ -351,15 +358,20 @@ def cpu_single_thread(layers_host, xs, seconds: float, m: int = 1):
                       f"({nbytes} weight bytes, {dt:.1f} s, 1 thread)"}
 
 
-def cpu_all_cores(layers_host, xs, m: int, threads: int):
-    """The oracle over every layer of the stream at m rows, one layer per task on `threads`
-    host threads (its C calls release the GIL). Returns (results per layer, seconds)."""
+def cpu_all_cores(layers_host, xs, m: int, threads: int, which=None):
+    """The oracle over every layer of the stream (or the layers in `which`) at m rows, one
+    layer per task on `threads` host threads (its C calls release the GIL). Returns
+    (results per layer, or None for layers not run; seconds)."""
     from concurrent.futures import ThreadPoolExecutor
     import oracle
     o = oracle.default()
+    which = list(range(len(layers_host))) if which is None else list(which)
     t0 = time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
-        res = list(ex.map(lambda l: o.ffn(layers_host[l], xs[l][:m]), range(len(layers_host))))
+        part = list(ex.map(lambda l: o.ffn(layers_host[l], xs[l][:m]), which))
+    res = [None] * len(layers_host)
+    for l, r in zip(which, part):
+        res[l] = r
     return res, time.perf_counter() - t0
 
 
@@ -397,9 +409,10 @@ def oracle_parity(layers_host, res, got, threads: int):
             bad.append("y")
         return bad, wh, wy
 
+    which = [l for l in range(len(res)) if res[l] is not None]
     with ThreadPoolExecutor(threads) as ex:
-        out = list(ex.map(one, range(len(res))))
-    fails = [f"layer {l}: {','.join(b)}" for l, (b, _, _) in enumerate(out) if b]
+        out = list(ex.map(one, which))
+    fails = [f"layer {l}: {','.join(b)}" for l, (b, _, _) in zip(which, out) if b]
     return (not fails, max(w for _, w, _ in out), max(w for _, _, w in out), fails[:8])
 
 
@@ -477,7 +490,7 @@ def main():
 
     t0 = time.perf_counter()
     layers = synth.ffn_stream(SEED, args.layers, synth.FMT_TERNARY2, threads=16)
-    xs = [synth.normal_rows(8, synth.HIDDEN, SEED, l) for l in range(args.layers)]
+    xs = [synth.normal_rows(32, synth.HIDDEN, SEED, l) for l in range(args.layers)]
     layer_bytes = layers[0].nbytes
     step_bytes = layer_bytes * args.layers
     log(f"generated {args.layers} layers ({step_bytes} B) in {time.perf_counter() - t0:.1f} s")
@@ -588,6 +601,24 @@ def main():
         log(f"M=8: fused {t8 / args.layers * 1e6:.2f} us/layer, separate "
             f"{t8s / args.layers * 1e6:.2f} us/layer")
 
+    res_big = None
+    got16 = None
+    if not args.skip_batch:
+        res_big = {}
+        for m in (16, 32):
+            sb = Stream64(tb, dev_layers, xs, m, torch, batch=True)
+            tb_s, pb = time_stream(torch, sb, args.steps, args.warmup, use_graph)
+            torch.cuda.synchronize()
+            gotb = sb.outputs()
+            ye = eager_reference(torch, sb)
+            parity[f"m{m}_timed_graph_equals_eager"] = bool(gotb["y"].tobytes() == ye.tobytes())
+            if m == 16:
+                got16 = gotb
+            del sb, gotb
+            res_big[f"m{m}"] = dict(summary(tb_s, pb), entry_point="tb_*_batch calls, hip graph replay")
+            log(f"M={m} (batch calls): {tb_s / args.layers * 1e6:.2f} us/layer, "
+                f"{step_bytes / tb_s / 1e9:.1f} GB/s")
+
     res_sign = None
     if not args.skip_sign:
         del dev_layers
@@ -661,6 +692,17 @@ def main():
                      "sample": f"all {args.layers} layers at M=8 on {threads} threads ({dt8:.1f} s)"}
         log(f"cpu oracle M=8: {cpu['m8']['value']} GB/s; M=8 parity vs oracle: {ok8} "
             f"(worst h {wh8:.3g}, y {wy8:.3g} of bound)")
+    if got16 is not None:
+        sample = list(range(0, args.layers, max(1, args.layers // 8)))
+        res16, _ = cpu_all_cores(layers, xs, 16, threads, which=sample)
+        ok16, wh16, wy16, f16s = oracle_parity(layers, res16, got16, threads)
+        parity["m16_oracle_layers"] = sample
+        parity["m16_oracle_ok"] = ok16
+        parity["m16_oracle_worst_y_over_bound"] = round(wy16, 4)
+        if f16s:
+            parity["m16_oracle_failures"] = f16s
+        log(f"M=16 parity vs oracle on layers {sample}: {ok16} (worst y {wy16:.3g} of bound)")
+        del res16, got16
     parity_ok = all(v for k, v in parity.items() if isinstance(v, bool))
     parity["all_ok"] = parity_ok
 
@@ -693,6 +735,7 @@ def main():
         "paths_m1": paths,
         "m8": res_m8,
         "sign1_stream": res_sign,
+        "batch_m16_m32": res_big,
         "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(k_key),

@@ -53,9 +53,10 @@
 extern "C" {
 #endif
 
-#define TB_ABI_VERSION 1
+#define TB_ABI_VERSION 2
 #define TB_BLOCK 128
 #define TB_MAX_ROWS 8
+#define TB_MAX_BATCH_ROWS 32
 
 enum tb_status {
     TB_OK = 0,
@@ -150,6 +151,33 @@ int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float
  *   isum int32 [m][w->n][w->k/128] output; m * n * (k/128) * 4 must be below
  *   2 GiB (else TB_EUNSUPPORTED). */
 int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream);
+
+/* ---- Batches above 8 rows ------------------------------------------------
+ * The same five operations for 1 <= m <= TB_MAX_BATCH_ROWS (32) rows: for
+ * concurrent decodes beyond the packed steps of 8 that the calls above take
+ * (PR #1154, Proof of speedup, where the ternary copy left 16 and 32
+ * concurrent requests unchanged; bonsai-edge-serve README, speculative-decoding
+ * section, on an integer-dot batch kernel for these formats). Arguments,
+ * layouts, outputs and errors are those of the call without the suffix, with
+ * m up to 32; each row's outputs are bit-identical to the same row run alone
+ * through either family.
+ * The rows run as balanced chunks: chunks of up to 16 rows on the matrix-core
+ * kernel with all 16 B columns live (one read of the weights per chunk) where
+ * the shape's activation and step partials fit the device's LDS and k/128 is a
+ * multiple of 2 (ternary) or 4 (sign); otherwise chunks of up to 8 rows on the
+ * kernels of the calls above. At hidden 5120, intermediate 17408: gate/up
+ * takes 16 rows per chunk, the down GEMV 8.
+ * tb_gemv_block_sums_batch: (chunk rows) * n * (k/128) * 4 must be below
+ * 2 GiB. */
+int tb_rotate_quant_i8_batch(const float *x, int m, int k, int8_t *q, float *dq, void *stream);
+int tb_gemv_ternary_batch(const tb_matrix *w, const int8_t *q, const float *dq, int m, float *y,
+                          void *stream);
+int tb_ffn_gateup_silu_batch(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q,
+                             const float *dq, int m, float *h, void *stream);
+int tb_ffn_down_batch(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,
+                      float *y, void *stream);
+int tb_gemv_block_sums_batch(const tb_matrix *w, const int8_t *q, int m, int32_t *isum,
+                             void *stream);
 
 /* ---- Fused FFN layers ----------------------------------------------------
  * One launch runs num_layers whole FFN layers of the same shape: for each

@@ -21,10 +21,14 @@ TB_OK, TB_EINVAL, TB_EALIGN, TB_EUNSUPPORTED, TB_EHIP = 0, -1, -2, -3, -4
 TB_FMT_TERNARY2, TB_FMT_SIGN1 = 0, 1
 BLOCK = 128
 MAX_ROWS = 8
+MAX_BATCH_ROWS = 32
+ABI_VERSION = 2
 
 # every symbol include/tb.h declares
 ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_ffn_gateup_silu", "tb_ffn_down",
-               "tb_gemv_block_sums", "tb_ffn_workspace_bytes", "tb_ffn_workspace_init",
+               "tb_gemv_block_sums", "tb_rotate_quant_i8_batch", "tb_gemv_ternary_batch",
+               "tb_ffn_gateup_silu_batch", "tb_ffn_down_batch", "tb_gemv_block_sums_batch",
+               "tb_ffn_workspace_bytes", "tb_ffn_workspace_init",
                "tb_ffn_layers", "tb_ffn_workspace_error", "tb_status_str", "tb_abi_version")
 TB_FFN_CHAIN = 1
 
@@ -53,6 +57,11 @@ _SIGS = {
     "tb_ffn_gateup_silu": ([_MP, _MP, _P, _P, _I, _P, _P], _I),
     "tb_ffn_down": ([_MP, _P, _I, _P, _P, _P, _P], _I),
     "tb_gemv_block_sums": ([_MP, _P, _I, _P, _P], _I),
+    "tb_rotate_quant_i8_batch": ([_P, _I, _I, _P, _P, _P], _I),
+    "tb_gemv_ternary_batch": ([_MP, _P, _P, _I, _P, _P], _I),
+    "tb_ffn_gateup_silu_batch": ([_MP, _MP, _P, _P, _I, _P, _P], _I),
+    "tb_ffn_down_batch": ([_MP, _P, _I, _P, _P, _P, _P], _I),
+    "tb_gemv_block_sums_batch": ([_MP, _P, _I, _P, _P], _I),
     "tb_ffn_workspace_bytes": ([_I, _I, _I], ctypes.c_size_t),
     "tb_ffn_workspace_init": ([_P, ctypes.c_size_t, ctypes.c_uint32, _P], _I),
     "tb_ffn_layers": ([ctypes.POINTER(CFfnWeights), _I, _P, _I, ctypes.c_uint, _P, ctypes.c_size_t,
@@ -161,6 +170,37 @@ def tb_ffn_down(wd: Matrix, h, qh_ws, dqh_ws, y, stream=None) -> None:
 def tb_gemv_block_sums(w: Matrix, q, isum, stream=None) -> None:
     """isum int32 [m][w.n][w.k/128]: the integer block sums before the scale fold."""
     _call("tb_gemv_block_sums", ctypes.byref(w.c), q.data_ptr(), _rows(q), isum.data_ptr(),
+          _stream(stream))
+
+
+def tb_rotate_quant_i8_batch(x, q, dq, stream=None) -> None:
+    """tb_rotate_quant_i8 for up to 32 rows."""
+    m, k = _rows(x), int(x.shape[-1])
+    _call("tb_rotate_quant_i8_batch", x.data_ptr(), m, k, q.data_ptr(), dq.data_ptr(),
+          _stream(stream))
+
+
+def tb_gemv_ternary_batch(w: Matrix, q, dq, y, stream=None) -> None:
+    """tb_gemv_ternary for up to 32 rows."""
+    _call("tb_gemv_ternary_batch", ctypes.byref(w.c), q.data_ptr(), dq.data_ptr(), _rows(q),
+          y.data_ptr(), _stream(stream))
+
+
+def tb_ffn_gateup_silu_batch(wg: Matrix, wu: Matrix, q, dq, h, stream=None) -> None:
+    """tb_ffn_gateup_silu for up to 32 rows."""
+    _call("tb_ffn_gateup_silu_batch", ctypes.byref(wg.c), ctypes.byref(wu.c), q.data_ptr(),
+          dq.data_ptr(), _rows(q), h.data_ptr(), _stream(stream))
+
+
+def tb_ffn_down_batch(wd: Matrix, h, qh_ws, dqh_ws, y, stream=None) -> None:
+    """tb_ffn_down for up to 32 rows."""
+    _call("tb_ffn_down_batch", ctypes.byref(wd.c), h.data_ptr(), _rows(h), qh_ws.data_ptr(),
+          dqh_ws.data_ptr(), y.data_ptr(), _stream(stream))
+
+
+def tb_gemv_block_sums_batch(w: Matrix, q, isum, stream=None) -> None:
+    """tb_gemv_block_sums for up to 32 rows."""
+    _call("tb_gemv_block_sums_batch", ctypes.byref(w.c), q.data_ptr(), _rows(q), isum.data_ptr(),
           _stream(stream))
 
 

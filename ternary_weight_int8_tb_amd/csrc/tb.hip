@@ -1243,6 +1243,14 @@ GemvFn gemv_mfma_pick_m(int m)
     case 6: return gemv_mfma_kernel<6, FMT, MODE>;
     case 7: return gemv_mfma_kernel<7, FMT, MODE>;
     case 8: return gemv_mfma_kernel<8, FMT, MODE>;
+    case 9: return gemv_mfma_kernel<9, FMT, MODE>;
+    case 10: return gemv_mfma_kernel<10, FMT, MODE>;
+    case 11: return gemv_mfma_kernel<11, FMT, MODE>;
+    case 12: return gemv_mfma_kernel<12, FMT, MODE>;
+    case 13: return gemv_mfma_kernel<13, FMT, MODE>;
+    case 14: return gemv_mfma_kernel<14, FMT, MODE>;
+    case 15: return gemv_mfma_kernel<15, FMT, MODE>;
+    case 16: return gemv_mfma_kernel<16, FMT, MODE>;
     default: return nullptr;
     }
 }
@@ -1264,6 +1272,7 @@ static_assert(mfma_min_rows(true, true) >= 2 && mfma_min_rows(true, false) >= 2 
                   mfma_min_rows(false, true) >= 2 && mfma_min_rows(false, false) >= 2,
               "gemv_mfma_pack_kernel is instantiated for M = 2 .. 8");
 
+constexpr int kMaxWideRows = 16;   // rows of one gemv_mfma_kernel launch in the batch calls
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
     int lds_limit = 0;   // 0 = not queried yet
@@ -1333,7 +1342,7 @@ size_t codes_bytes(const tb_matrix *w)
 }
 size_t scales_bytes(const tb_matrix *w) { return (size_t)w->n * (size_t)(w->k / kBlock) * 2; }
 
-int check_rows(int m) { return (m >= 1 && m <= TB_MAX_ROWS) ? TB_OK : TB_EINVAL; }
+int check_rows(int m, int max_rows = TB_MAX_ROWS) { return (m >= 1 && m <= max_rows) ? TB_OK : TB_EINVAL; }
 
 float dq_unit() { return static_cast<float>(1.0 / (127.0 * std::sqrt(128.0))); }
 
@@ -1379,6 +1388,32 @@ int raise_lds(const void *fn, size_t lds)
 
 int set_lds(GemvFn fn, size_t lds) { return raise_lds(reinterpret_cast<const void *>(fn), lds); }
 
+// LDS bytes of gemv_mfma_kernel for m rows of a matrix of n rows and k inputs on a grid of
+// `grid` workgroups (activation, block terms, code sums, item counter, step partials).
+size_t mfma_lds_bytes(int fmt, int mode, int n, int k, int m, int grid)
+{
+    const bool tern = fmt == TB_FMT_TERNARY2;
+    const int wpc = tern ? 64 : 128, nb = k / kBlock;
+    const int steps = (k / wpc + kChunkLanes - 1) / kChunkLanes;
+    const long tiles = (n + kRowsPerWave - 1) / kRowsPerWave;
+    const size_t rows_cu = (size_t)((tiles + grid - 1) / grid) * kRowsPerWave;
+    const size_t bps = tern ? 8 : 16;
+    return (size_t)steps * (tern ? 1024 : 2048) * m + (size_t)m * (nb + bps) * 4 * (tern ? 1 : 2) + 16 +
+           rows_cu * steps * m * (mode == kModeGateUp ? 2 : 1) * 4;
+}
+
+// Rows of a batch above 8 run on gemv_mfma_kernel with all 16 B columns live: whether m
+// such rows fit this device and shape.
+bool wide_fits(const DeviceInfo &info, int mode, const tb_matrix *w, int m)
+{
+    const bool tern = w->fmt == TB_FMT_TERNARY2;
+    if ((w->k / kBlock) % (tern ? 2 : 4))
+        return false;
+    const long tiles = (w->n + kRowsPerWave - 1) / kRowsPerWave;
+    const int grid = (int)(tiles < info.cus ? tiles : info.cus);
+    return mfma_lds_bytes(w->fmt, mode, w->n, w->k, m, grid) <= (size_t)info.lds_limit;
+}
+
 int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t *q,
                 const float *dq, int m, float *out, int32_t *isum, hipStream_t stream)
 {
@@ -1421,10 +1456,10 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
         const size_t bps = tern ? 8 : 16;
         const size_t parts = rows_cu * steps * m * (mode == kModeGateUp ? 2 : 1) * 4;
 #if TB_MFMA_PACK
-        // two blocks per MFMA (every M here is at most 8)
-        const size_t pack_lds_bytes =
+        // two blocks per MFMA, for at most 8 rows
+        const size_t pack_lds_bytes = m > 8 ? ~(size_t)0 :
             pack_lds(m, w0->fmt, w0->k, pack_threads(w0->fmt) / 64).part + parts;
-        if (pack_lds_bytes <= (size_t)info.lds_limit) {
+        if (m <= 8 && pack_lds_bytes <= (size_t)info.lds_limit) {
             GemvFn fn = tern ? (mode == kModeGateUp ? gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
                                 : mode == kModeY  ? gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeY>(m)
                                                   : gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeIsum>(m))
@@ -1439,8 +1474,9 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
             return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
         }
 #endif
-        const size_t mfma_lds = (size_t)steps * step_bytes + (size_t)m * (nb + bps) * 4 * (tern ? 1 : 2) +
-                                16 + parts;
+        (void)bps;
+        (void)step_bytes;
+        const size_t mfma_lds = mfma_lds_bytes(w0->fmt, mode, w0->n, w0->k, m, ring_grid);
         if (mfma_lds <= (size_t)info.lds_limit) {
             GemvFn fn = tern ? (mode == kModeGateUp ? gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
                                 : mode == kModeY  ? gemv_mfma_pick_m<TB_FMT_TERNARY2, kModeY>(m)
@@ -1457,6 +1493,8 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
         }
     }
 
+    if (m > 8)
+        return TB_EUNSUPPORTED;   // the batch launcher only passes rows that fit
     // whole activation in LDS: the persistent ring kernel, one workgroup per CU
     const size_t pad_blocks = (size_t)(kChunkLanes / (w0->fmt == TB_FMT_TERNARY2 ? 2 : 1));
     const size_t ring_terms = (size_t)m * (nb + pad_blocks) * 4 * (w0->fmt == TB_FMT_TERNARY2 ? 1 : 2);
@@ -1496,6 +1534,36 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
+
+// A batch of m (1..32) independent rows as balanced chunks: chunks of up to 16 rows on
+// gemv_mfma_kernel (all 16 B columns live) where they fit the device's LDS, else of up to 8
+// rows on the kernels of the 1..8-row calls. Every kernel folds a row the same way, so a
+// row's outputs do not depend on the chunk it lands in.
+int launch_gemv_batch(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t *q,
+                      const float *dq, int m, float *out, int32_t *isum, hipStream_t stream)
+{
+    DeviceInfo info;
+    int rc = device_info(&info);
+    if (rc)
+        return rc;
+    int cmax = 8;
+    for (int c = m < kMaxWideRows ? m : kMaxWideRows; c > 8; --c)
+        if (wide_fits(info, mode, w0, c)) {
+            cmax = c;
+            break;
+        }
+    const int chunks = (m + cmax - 1) / cmax;
+    const size_t k = (size_t)w0->k, n = (size_t)w0->n, nb = k / kBlock;
+    for (int i = 0, r0 = 0; i < chunks; ++i) {
+        const int mc = (m * (i + 1)) / chunks - (m * i) / chunks;
+        rc = launch_gemv(mode, w0, w1, q + r0 * k, dq ? dq + r0 * nb : nullptr, mc,
+                         out ? out + r0 * n : nullptr, isum ? isum + r0 * n * nb : nullptr, stream);
+        if (rc)
+            return rc;
+        r0 += mc;
+    }
+    return TB_OK;
+}
 
 // ------------------------------------------------------------------------------------
 // Fused FFN layers
@@ -1581,9 +1649,10 @@ const char *tb_status_str(int status)
     }
 }
 
-int tb_rotate_quant_i8(const float *x, int m, int k, int8_t *q, float *dq, void *stream)
+static int rotate_quant_impl(const float *x, int m, int k, int8_t *q, float *dq, void *stream,
+                             int max_rows)
 {
-    if (check_rows(m) || k < kBlock || k % kBlock || !x || !q || !dq)
+    if (check_rows(m, max_rows) || k < kBlock || k % kBlock || !x || !q || !dq)
         return TB_EINVAL;
     if (!aligned16(x) || !aligned16(q) || !aligned16(dq))
         return TB_EALIGN;
@@ -1594,13 +1663,23 @@ int tb_rotate_quant_i8(const float *x, int m, int k, int8_t *q, float *dq, void 
     return launch_rotquant(x, m, k, q, dq, static_cast<hipStream_t>(stream));
 }
 
-int tb_gemv_ternary(const tb_matrix *w, const int8_t *q, const float *dq, int m, float *y,
-                    void *stream)
+int tb_rotate_quant_i8(const float *x, int m, int k, int8_t *q, float *dq, void *stream)
+{
+    return rotate_quant_impl(x, m, k, q, dq, stream, TB_MAX_ROWS);
+}
+
+int tb_rotate_quant_i8_batch(const float *x, int m, int k, int8_t *q, float *dq, void *stream)
+{
+    return rotate_quant_impl(x, m, k, q, dq, stream, TB_MAX_BATCH_ROWS);
+}
+
+static int gemv_impl(const tb_matrix *w, const int8_t *q, const float *dq, int m, float *y,
+                     void *stream, bool batch)
 {
     int rc = check_matrix(w);
     if (rc)
         return rc;
-    if (check_rows(m) || !y || !q || !dq)
+    if (check_rows(m, batch ? TB_MAX_BATCH_ROWS : TB_MAX_ROWS) || !y || !q || !dq)
         return TB_EINVAL;
     if (!aligned16(q) || !aligned16(dq) || !aligned16(y))
         return TB_EALIGN;
@@ -1610,11 +1689,24 @@ int tb_gemv_ternary(const tb_matrix *w, const int8_t *q, const float *dq, int m,
         overlaps(ry, range_of(q, (size_t)m * w->k)) ||
         overlaps(ry, range_of(dq, (size_t)m * (w->k / kBlock) * 4)))
         return TB_EINVAL;
-    return launch_gemv(kModeY, w, nullptr, q, dq, m, y, nullptr, static_cast<hipStream_t>(stream));
+    return (batch ? launch_gemv_batch : launch_gemv)(kModeY, w, nullptr, q, dq, m, y, nullptr,
+                                                     static_cast<hipStream_t>(stream));
 }
 
-int tb_ffn_gateup_silu(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q,
-                       const float *dq, int m, float *h, void *stream)
+int tb_gemv_ternary(const tb_matrix *w, const int8_t *q, const float *dq, int m, float *y,
+                    void *stream)
+{
+    return gemv_impl(w, q, dq, m, y, stream, false);
+}
+
+int tb_gemv_ternary_batch(const tb_matrix *w, const int8_t *q, const float *dq, int m, float *y,
+                          void *stream)
+{
+    return gemv_impl(w, q, dq, m, y, stream, true);
+}
+
+static int gateup_impl(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q,
+                       const float *dq, int m, float *h, void *stream, bool batch)
 {
     int rc = check_matrix(wg);
     if (rc)
@@ -1623,7 +1715,7 @@ int tb_ffn_gateup_silu(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q
         return rc;
     if (wg->n != wu->n || wg->k != wu->k || wg->fmt != wu->fmt)
         return TB_EINVAL;
-    if (check_rows(m) || !h || !q || !dq)
+    if (check_rows(m, batch ? TB_MAX_BATCH_ROWS : TB_MAX_ROWS) || !h || !q || !dq)
         return TB_EINVAL;
     if (!aligned16(q) || !aligned16(dq) || !aligned16(h))
         return TB_EALIGN;
@@ -1635,17 +1727,29 @@ int tb_ffn_gateup_silu(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q
         overlaps(rh, range_of(q, (size_t)m * wg->k)) ||
         overlaps(rh, range_of(dq, (size_t)m * (wg->k / kBlock) * 4)))
         return TB_EINVAL;
-    return launch_gemv(kModeGateUp, wg, wu, q, dq, m, h, nullptr,
-                       static_cast<hipStream_t>(stream));
+    return (batch ? launch_gemv_batch : launch_gemv)(kModeGateUp, wg, wu, q, dq, m, h, nullptr,
+                                                     static_cast<hipStream_t>(stream));
 }
 
-int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,
-                float *y, void *stream)
+int tb_ffn_gateup_silu(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q,
+                       const float *dq, int m, float *h, void *stream)
+{
+    return gateup_impl(wg, wu, q, dq, m, h, stream, false);
+}
+
+int tb_ffn_gateup_silu_batch(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q,
+                             const float *dq, int m, float *h, void *stream)
+{
+    return gateup_impl(wg, wu, q, dq, m, h, stream, true);
+}
+
+static int down_impl(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,
+                     float *y, void *stream, bool batch)
 {
     int rc = check_matrix(wd);
     if (rc)
         return rc;
-    if (check_rows(m) || !h || !qh_ws || !dqh_ws || !y)
+    if (check_rows(m, batch ? TB_MAX_BATCH_ROWS : TB_MAX_ROWS) || !h || !qh_ws || !dqh_ws || !y)
         return TB_EINVAL;
     if (!aligned16(h) || !aligned16(qh_ws) || !aligned16(dqh_ws) || !aligned16(y))
         return TB_EALIGN;
@@ -1666,28 +1770,53 @@ int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = launch_rotquant(h, m, k, qh_ws, dqh_ws, s)))
         return rc;
-    return launch_gemv(kModeY, wd, nullptr, qh_ws, dqh_ws, m, y, nullptr, s);
+    return (batch ? launch_gemv_batch : launch_gemv)(kModeY, wd, nullptr, qh_ws, dqh_ws, m, y,
+                                                     nullptr, s);
 }
 
-int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream)
+int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,
+                float *y, void *stream)
+{
+    return down_impl(wd, h, m, qh_ws, dqh_ws, y, stream, false);
+}
+
+int tb_ffn_down_batch(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,
+                      float *y, void *stream)
+{
+    return down_impl(wd, h, m, qh_ws, dqh_ws, y, stream, true);
+}
+
+static int block_sums_impl(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream,
+                           bool batch)
 {
     int rc = check_matrix(w);
     if (rc)
         return rc;
-    if (check_rows(m) || !q || !isum)
+    if (check_rows(m, batch ? TB_MAX_BATCH_ROWS : TB_MAX_ROWS) || !q || !isum)
         return TB_EINVAL;
     if (!aligned16(q) || !aligned16(isum))
         return TB_EALIGN;
-    // the sums are written with 32-bit buffer offsets
-    if ((size_t)m * w->n * (w->k / kBlock) * 4 >= ((size_t)1 << 31))
+    // the sums of one launch (at most 16 rows) are written with 32-bit buffer offsets
+    if ((size_t)(m < kMaxWideRows ? m : kMaxWideRows) * w->n * (w->k / kBlock) * 4 >= ((size_t)1 << 31))
         return TB_EUNSUPPORTED;
     const Range ri = range_of(isum, (size_t)m * w->n * (w->k / kBlock) * 4);
     if (overlaps(ri, range_of(w->codes, codes_bytes(w))) ||
         overlaps(ri, range_of(w->scales, scales_bytes(w))) ||
         overlaps(ri, range_of(q, (size_t)m * w->k)))
         return TB_EINVAL;
-    return launch_gemv(kModeIsum, w, nullptr, q, nullptr, m, nullptr, isum,
-                       static_cast<hipStream_t>(stream));
+    return (batch ? launch_gemv_batch : launch_gemv)(kModeIsum, w, nullptr, q, nullptr, m, nullptr,
+                                                     isum, static_cast<hipStream_t>(stream));
+}
+
+int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream)
+{
+    return block_sums_impl(w, q, m, isum, stream, false);
+}
+
+int tb_gemv_block_sums_batch(const tb_matrix *w, const int8_t *q, int m, int32_t *isum,
+                             void *stream)
+{
+    return block_sums_impl(w, q, m, isum, stream, true);
 }
 
 

@@ -37,7 +37,7 @@ def test_header_declares_the_binding_names():
 def test_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.tb_abi_version() == 1
+    assert L.tb_abi_version() == tb.ABI_VERSION
 
 
 def test_status_strings(L):
@@ -189,3 +189,29 @@ def test_valid_calls_without_a_device_return_ehip(L):
     assert L.tb_ffn_gateup_silu(ctypes.byref(w), ctypes.byref(w2), ALIGNED3, ALIGNED4, 1, y,
                                 None) == tb.TB_EHIP
     assert L.tb_gemv_block_sums(ctypes.byref(w), ALIGNED3, 1, ALIGNED4, None) == tb.TB_EHIP
+
+
+def test_batch_calls_validate_rows_and_arguments(L):
+    # the batch family takes 1..32 rows; everything else is checked as in the 1..8 calls
+    assert L.tb_rotate_quant_i8_batch(ALIGNED, 0, 512, ALIGNED2, ALIGNED3, None) == tb.TB_EINVAL
+    assert L.tb_rotate_quant_i8_batch(ALIGNED, 33, 512, ALIGNED2, ALIGNED3, None) == tb.TB_EINVAL
+    assert L.tb_rotate_quant_i8_batch(ALIGNED, 32, 100, ALIGNED2, ALIGNED3, None) == tb.TB_EINVAL
+    assert L.tb_rotate_quant_i8_batch(ALIGNED + 4, 16, 512, ALIGNED2, ALIGNED3, None) == tb.TB_EALIGN
+    w = mat()
+    y = ALIGNED4 + 0x100000
+    for m in (0, 33):
+        assert L.tb_gemv_ternary_batch(ctypes.byref(w), ALIGNED3, ALIGNED4, m, y, None) == tb.TB_EINVAL
+        assert L.tb_ffn_gateup_silu_batch(ctypes.byref(w), ctypes.byref(w), ALIGNED3, ALIGNED4, m,
+                                          y, None) == tb.TB_EINVAL
+        assert L.tb_ffn_down_batch(ctypes.byref(mat(n=64, k=256)), ALIGNED3, m, ALIGNED4,
+                                   ALIGNED4 + 0x10000, y, None) == tb.TB_EINVAL
+        assert L.tb_gemv_block_sums_batch(ctypes.byref(w), ALIGNED3, m, y, None) == tb.TB_EINVAL
+    assert L.tb_gemv_ternary_batch(ctypes.byref(mat(k=500)), ALIGNED3, ALIGNED4, 16, y,
+                                   None) == tb.TB_EINVAL
+    assert L.tb_gemv_ternary_batch(ctypes.byref(w), ALIGNED3 + 8, ALIGNED4, 16, y,
+                                   None) == tb.TB_EALIGN
+    # y overlapping q
+    assert L.tb_gemv_ternary_batch(ctypes.byref(w), ALIGNED3, ALIGNED4, 16, ALIGNED3,
+                                   None) == tb.TB_EINVAL
+    # the 1..8 calls still reject 9 rows
+    assert L.tb_gemv_ternary(ctypes.byref(w), ALIGNED3, ALIGNED4, 9, y, None) == tb.TB_EINVAL

@@ -42,7 +42,7 @@ def o():
 @pytest.fixture(scope="module", autouse=True)
 def gpu():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
-    assert tb.tb_abi_version() == 1
+    assert tb.tb_abi_version() == tb.ABI_VERSION
     yield
 
 
