@@ -63,7 +63,8 @@ enum tb_status {
     TB_EINVAL = -1,       /* bad shape, null pointer, unknown format, aliasing */
     TB_EALIGN = -2,       /* a pointer is not 16-byte aligned */
     TB_EUNSUPPORTED = -3, /* valid arguments this build cannot run (e.g. LDS too small) */
-    TB_EHIP = -4          /* the HIP runtime reported an error */
+    TB_EHIP = -4,         /* the HIP runtime reported an error */
+    TB_ESCRATCH = -5      /* input larger than the library's static scratch (tb_ffn_down_noalloc) */
 };
 
 enum tb_format {
@@ -178,6 +179,26 @@ int tb_ffn_down_batch(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws,
                       float *y, void *stream);
 int tb_gemv_block_sums_batch(const tb_matrix *w, const int8_t *q, int m, int32_t *isum,
                              void *stream);
+
+/* ---- No allocation -------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * tb_ffn_down without the workspace arguments. rotquant(h) and its scales go
+ * to a device array inside the library (TB_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the first call on that GPU until the process ends), so the call
+ * allocates nothing. Same arguments, kernels and outputs as tb_ffn_down; y is
+ * bit-identical to it.
+ *   Limit    round_up(m * k, 256) + m * (k/128) * 4 <= TB_NOALLOC_SCRATCH_BYTES
+ *            (for m = 8: k up to 126,976); larger inputs return TB_ESCRATCH and
+ *            enqueue nothing.
+ *   Sharing  Every call on one GPU uses that GPU's one array, which keeps the
+ *            last call's contents. Calls that overlap in time on one GPU (on
+ *            different streams, or from several host threads) race on it and
+ *            must be serialised by the caller. Nothing in it needs clearing:
+ *            each call overwrites what it reads.
+ *   First call on a GPU looks up the array's device address (no allocation). */
+#define TB_NOALLOC_SCRATCH_BYTES (1u << 20)
+int tb_ffn_down_noalloc(const tb_matrix *wd, const float *h, int m, float *y, void *stream);
 
 /* ---- Fused FFN layers ----------------------------------------------------
  * One launch runs num_layers whole FFN layers of the same shape: for each

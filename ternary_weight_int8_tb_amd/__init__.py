@@ -17,7 +17,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libtb.so")
 
-TB_OK, TB_EINVAL, TB_EALIGN, TB_EUNSUPPORTED, TB_EHIP = 0, -1, -2, -3, -4
+TB_OK, TB_EINVAL, TB_EALIGN, TB_EUNSUPPORTED, TB_EHIP, TB_ESCRATCH = 0, -1, -2, -3, -4, -5
 TB_FMT_TERNARY2, TB_FMT_SIGN1 = 0, 1
 BLOCK = 128
 MAX_ROWS = 8
@@ -28,6 +28,7 @@ ABI_VERSION = 2
 ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_ffn_gateup_silu", "tb_ffn_down",
                "tb_gemv_block_sums", "tb_rotate_quant_i8_batch", "tb_gemv_ternary_batch",
                "tb_ffn_gateup_silu_batch", "tb_ffn_down_batch", "tb_gemv_block_sums_batch",
+               "tb_ffn_down_noalloc",
                "tb_ffn_workspace_bytes", "tb_ffn_workspace_init",
                "tb_ffn_layers", "tb_ffn_workspace_error", "tb_status_str", "tb_abi_version")
 TB_FFN_CHAIN = 1
@@ -62,6 +63,7 @@ _SIGS = {
     "tb_ffn_gateup_silu_batch": ([_MP, _MP, _P, _P, _I, _P, _P], _I),
     "tb_ffn_down_batch": ([_MP, _P, _I, _P, _P, _P, _P], _I),
     "tb_gemv_block_sums_batch": ([_MP, _P, _I, _P, _P], _I),
+    "tb_ffn_down_noalloc": ([_MP, _P, _I, _P, _P], _I),
     "tb_ffn_workspace_bytes": ([_I, _I, _I], ctypes.c_size_t),
     "tb_ffn_workspace_init": ([_P, ctypes.c_size_t, ctypes.c_uint32, _P], _I),
     "tb_ffn_layers": ([ctypes.POINTER(CFfnWeights), _I, _P, _I, ctypes.c_uint, _P, ctypes.c_size_t,
@@ -201,6 +203,12 @@ def tb_ffn_down_batch(wd: Matrix, h, qh_ws, dqh_ws, y, stream=None) -> None:
 def tb_gemv_block_sums_batch(w: Matrix, q, isum, stream=None) -> None:
     """tb_gemv_block_sums for up to 32 rows."""
     _call("tb_gemv_block_sums_batch", ctypes.byref(w.c), q.data_ptr(), _rows(q), isum.data_ptr(),
+          _stream(stream))
+
+
+def tb_ffn_down_noalloc(wd: Matrix, h, y, stream=None) -> None:
+    """tb_ffn_down with the library's static scratch instead of a caller workspace."""
+    _call("tb_ffn_down_noalloc", ctypes.byref(wd.c), h.data_ptr(), _rows(h), y.data_ptr(),
           _stream(stream))
 
 

@@ -42,6 +42,12 @@
 #include "tb_device.h"
 #include "tb_layers.h"
 
+// Device scratch of tb_ffn_down_noalloc: rotquant(h) and its block scales, for callers that
+// cannot allocate. Each GPU holds its own copy until the process ends. Host code never uses
+// this name as an address: the device address comes from hipGetSymbolAddress, per device.
+constexpr size_t kNoAllocScratchBytes = TB_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace {
 
 using namespace tbk;
@@ -1289,6 +1295,24 @@ struct Raised {
 };
 Raised g_raised[kMaxDevices][kMaxRaised];
 int g_nraised[kMaxDevices];
+uint8_t *g_scratch[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The current device's address of `scratch` (looked up once per device, with it current).
+int scratch_address(uint8_t **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return TB_EHIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return TB_EHIP;
+        g_scratch[dev] = static_cast<uint8_t *>(p);
+    }
+    *out = g_scratch[dev];
+    return TB_OK;
+}
 
 int device_info(DeviceInfo *out)
 {
@@ -1645,6 +1669,7 @@ const char *tb_status_str(int status)
     case TB_EALIGN: return "pointer not 16-byte aligned";
     case TB_EUNSUPPORTED: return "unsupported shape for this build or device";
     case TB_EHIP: return "HIP runtime error";
+    case TB_ESCRATCH: return "input larger than the library's static scratch";
     default: return "unknown status";
     }
 }
@@ -1784,6 +1809,35 @@ int tb_ffn_down_batch(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws,
                       float *y, void *stream)
 {
     return down_impl(wd, h, m, qh_ws, dqh_ws, y, stream, true);
+}
+
+int tb_ffn_down_noalloc(const tb_matrix *wd, const float *h, int m, float *y, void *stream)
+{
+    int rc = check_matrix(wd);
+    if (rc)
+        return rc;
+    if (check_rows(m) || !h || !y)
+        return TB_EINVAL;
+    if (!aligned16(h) || !aligned16(y))
+        return TB_EALIGN;
+    const int k = wd->k;
+    const Range rh = range_of(h, (size_t)m * k * 4), ry = range_of(y, (size_t)m * wd->n * 4);
+    if (overlaps(ry, rh) || overlaps(ry, range_of(wd->codes, codes_bytes(wd))) ||
+        overlaps(ry, range_of(wd->scales, scales_bytes(wd))))
+        return TB_EINVAL;
+    // rotquant(h) codes, then its block scales, each 256-byte aligned, inside the scratch
+    const size_t q_bytes = ((size_t)m * k + 255) & ~(size_t)255;
+    if (q_bytes + (size_t)m * (k / kBlock) * 4 > kNoAllocScratchBytes)
+        return TB_ESCRATCH;
+    uint8_t *base = nullptr;
+    if ((rc = scratch_address(&base)))
+        return rc;
+    int8_t *qh = reinterpret_cast<int8_t *>(base);
+    float *dqh = reinterpret_cast<float *>(base + q_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = launch_rotquant(h, m, k, qh, dqh, s)))
+        return rc;
+    return launch_gemv(kModeY, wd, nullptr, qh, dqh, m, y, nullptr, s);
 }
 
 static int block_sums_impl(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream,
