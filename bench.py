@@ -61,6 +61,7 @@ def parse():
     p.add_argument("--skip-sign", action="store_true")
     p.add_argument("--skip-m8", action="store_true")
     p.add_argument("--skip-batch", action="store_true", help="no M=16 / M=32 stream")
+    p.add_argument("--skip-attn", action="store_true", help="no attention-projection stream")
     p.add_argument("--cpu-seconds", type=float, default=8.0,
                    help="target CPU time of the single-thread oracle sample")
     p.add_argument("--cpu-threads", type=int, default=0,
@@ -114,6 +115,59 @@ class Stream64:
         """Every intermediate and output of the last step, on the host."""
         return {name: getattr(self, name).cpu().numpy().copy()
                 for name in ("q", "dq", "h", "qh", "dqh", "y")}
+
+
+class AttnStream:
+    """Second workload: the full-attention projections of the model's 16 full-attention
+    layers at m rows. Per layer: rotate + quantise x, the fused query/gate/key/value
+    GEMV (9216 x 5120), rotate + quantise the attention output (stand-in rows), the
+    output GEMV (5120 x 4096). Every layer writes its own outputs."""
+
+    def __init__(self, tb, mats_dev, xs, os_, m, torch):
+        self.tb, self.mats, self.m = tb, mats_dev, m
+        dev = "cuda"
+        L = len(mats_dev)
+        H, Q, G = mats_dev[0][0].k, mats_dev[0][1].k, mats_dev[0][0].n
+        self.x = [torch.from_numpy(v[:m].copy()).to(dev) for v in xs]
+        self.oin = [torch.from_numpy(v[:m].copy()).to(dev) for v in os_]
+        self.q = torch.empty(L, m, H, dtype=torch.int8, device=dev)
+        self.dq = torch.empty(L, m, H // 128, dtype=torch.float32, device=dev)
+        self.qo = torch.empty(L, m, Q, dtype=torch.int8, device=dev)
+        self.dqo = torch.empty(L, m, Q // 128, dtype=torch.float32, device=dev)
+        self.yg = torch.empty(L, m, G, dtype=torch.float32, device=dev)
+        self.y = torch.empty(L, m, H, dtype=torch.float32, device=dev)
+
+    def step(self):
+        tb = self.tb
+        for l, (wg, wo) in enumerate(self.mats):
+            tb.tb_rotate_quant_i8(self.x[l], self.q[l], self.dq[l])
+            tb.tb_gemv_ternary(wg, self.q[l], self.dq[l], self.yg[l])
+            tb.tb_rotate_quant_i8(self.oin[l], self.qo[l], self.dqo[l])
+            tb.tb_gemv_ternary(wo, self.qo[l], self.dqo[l], self.y[l])
+
+    def outputs(self):
+        return {name: getattr(self, name).cpu().numpy().copy()
+                for name in ("q", "dq", "yg", "qo", "dqo", "y")}
+
+
+def attn_oracle_parity(mats_host, xs, os_, got, m, which):
+    """Layers `which` of the attention stream against the oracle: rotquant of both inputs
+    bit-exact, both GEMVs within 1e-4 * sum|terms|. Returns (ok, worst y over its bound)."""
+    import oracle
+    from tests import bounds
+    o = oracle.default()
+    ok, worst = True, 0.0
+    for l in which:
+        q, dq = o.rotate_quant(xs[l][:m])
+        qo, dqo = o.rotate_quant(os_[l][:m])
+        ok &= np.array_equal(got["q"][l], q) and np.array_equal(got["dq"][l], dq)
+        ok &= np.array_equal(got["qo"][l], qo) and np.array_equal(got["dqo"][l], dqo)
+        for key, w, qq, dd in (("yg", mats_host[l].qkvg, q, dq), ("y", mats_host[l].o, qo, dqo)):
+            yo, sabs = o.gemv(w, qq, dd)
+            g_ok, g_w = bounds.gemv_ok(got[key][l], yo, sabs)
+            ok &= g_ok
+            worst = max(worst, g_w)
+    return bool(ok), worst
 
 
 class Fused64:
@@ -619,6 +673,36 @@ def main():
             log(f"M={m} (batch calls): {tb_s / args.layers * 1e6:.2f} us/layer, "
                 f"{step_bytes / tb_s / 1e9:.1f} GB/s")
 
+    # ---- second workload: the full-attention projections (16 layers)
+    res_attn = None
+    attn_got = {}
+    if not args.skip_attn:
+        al = synth.attn_stream(SEED + 200, synth.ATTN_LAYERS, synth.FMT_TERNARY2, threads=16)
+        axs = [synth.normal_rows(8, synth.HIDDEN, SEED + 200, l) for l in range(len(al))]
+        aos = [synth.normal_rows(8, synth.ATTN_Q, SEED + 200, l, synth.T_ATTN_OUT) for l in range(len(al))]
+        adev = [(tb.Matrix.upload(a.qkvg), tb.Matrix.upload(a.o)) for a in al]
+        abytes = al[0].nbytes * len(al)
+        res_attn = {"layers": len(al), "bytes_per_step": abytes,
+                    "shapes": {"qkvg": [synth.ATTN_QKVG, synth.HIDDEN], "o": [synth.HIDDEN, synth.ATTN_Q]}}
+        for m in (1, 8):
+            st = AttnStream(tb, adev, axs, aos, m, torch)
+            ta, pa = time_stream(torch, st, args.steps, args.warmup, use_graph)
+            torch.cuda.synchronize()
+            attn_got[m] = st.outputs()
+            st.y.fill_(float("nan"))
+            st.step()
+            torch.cuda.synchronize()
+            parity[f"attn_m{m}_timed_graph_equals_eager"] = bool(
+                attn_got[m]["y"].tobytes() == st.y.cpu().numpy().tobytes())
+            del st
+            res_attn[f"m{m}"] = {"value": round(abytes / ta / 1e9, 2), "unit": "GB/s",
+                                 "us_per_layer": round(ta / len(al) * 1e6, 3),
+                                 "pct_hbm_peak": round(100 * abytes / ta / 1e9 / HBM_PEAK_GBS, 2)}
+            log(f"attention projections M={m}: {ta / len(al) * 1e6:.2f} us/layer, "
+                f"{abytes / ta / 1e9:.1f} GB/s")
+        del adev
+        torch.cuda.empty_cache()
+
     res_sign = None
     if not args.skip_sign:
         del dev_layers
@@ -703,6 +787,11 @@ def main():
             parity["m16_oracle_failures"] = f16s
         log(f"M=16 parity vs oracle on layers {sample}: {ok16} (worst y {wy16:.3g} of bound)")
         del res16, got16
+    for m, got in attn_got.items():
+        a_ok, a_w = attn_oracle_parity(al, axs, aos, got, m, (0, len(al) - 1))
+        parity[f"attn_m{m}_oracle_layers_0_15"] = a_ok
+        parity[f"attn_m{m}_oracle_worst_y_over_bound"] = round(a_w, 4)
+        log(f"attention M={m} parity vs oracle (layers 0, {len(al) - 1}): {a_ok} (worst {a_w:.3g})")
     parity_ok = all(v for k, v in parity.items() if isinstance(v, bool))
     parity["all_ok"] = parity_ok
 
@@ -736,6 +825,7 @@ def main():
         "m8": res_m8,
         "sign1_stream": res_sign,
         "batch_m16_m32": res_big,
+        "attention_projections": res_attn,
         "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(k_key),

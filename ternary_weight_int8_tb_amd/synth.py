@@ -229,3 +229,45 @@ def ffn_stream(seed: int, layers: int, fmt: int = FMT_TERNARY2, threads: int = 8
     with ThreadPoolExecutor(max(1, threads)) as ex:
         return list(ex.map(lambda l: ffn_layer(seed, l, fmt, hidden, inter, threads=1),
                            range(layers)))
+
+
+# ---------------------------------------------------------------------------
+# Second workload: the projections of a full-attention layer of the same model
+# (hidden 5120; head dim 256, 8:1 grouped-query attention with 2 key/value heads,
+# so 16 query heads; gated queries). The input projection is one fused matrix of
+# query (4096), gate (4096), key (512) and value (512) rows; the output projection
+# maps the 4096 attention outputs back to the hidden size. Every 4th of the 64
+# layers is a full-attention layer: 16 such layers.
+# ---------------------------------------------------------------------------
+
+HEAD_DIM = 256
+Q_HEADS = 16
+KV_HEADS = 2
+ATTN_Q = Q_HEADS * HEAD_DIM                          # 4096
+ATTN_QKVG = 2 * ATTN_Q + 2 * KV_HEADS * HEAD_DIM     # 9216: query, gate, key, value rows
+ATTN_LAYERS = 16
+
+T_QKVG = 6       # fused input projection [ATTN_QKVG x HIDDEN]
+T_OPROJ = 7      # output projection [HIDDEN x ATTN_Q]
+T_ATTN_OUT = 8   # stand-in rows for the attention output fed to the output projection
+
+
+@dataclass
+class AttnLayer:
+    qkvg: PackedMatrix   # [ATTN_QKVG x HIDDEN]
+    o: PackedMatrix      # [HIDDEN x ATTN_Q]
+
+    @property
+    def nbytes(self) -> int:
+        return self.qkvg.nbytes + self.o.nbytes
+
+
+def attn_layer(seed: int, layer: int, fmt: int = FMT_TERNARY2) -> AttnLayer:
+    return AttnLayer(matrix(fmt, ATTN_QKVG, HIDDEN, seed, layer, T_QKVG),
+                     matrix(fmt, HIDDEN, ATTN_Q, seed, layer, T_OPROJ))
+
+
+def attn_stream(seed: int, layers: int = ATTN_LAYERS, fmt: int = FMT_TERNARY2,
+                threads: int = 8) -> list[AttnLayer]:
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        return list(ex.map(lambda l: attn_layer(seed, l, fmt), range(layers)))
