@@ -107,8 +107,7 @@ class Stream64:
                 tb.tb_ffn_down_batch(wd, self.h[l], self.qh[l], self.dqh[l], self.y[l])
             return
         for l, (wg, wu, wd) in enumerate(self.layers):
-            tb.tb_rotate_quant_i8(self.x[l], self.q[l], self.dq[l])
-            tb.tb_ffn_gateup_silu(wg, wu, self.q[l], self.dq[l], self.h[l])
+            tb.tb_ffn_gateup_silu_x(wg, wu, self.x[l], self.q[l], self.dq[l], self.h[l])
             tb.tb_ffn_down(wd, self.h[l], self.qh[l], self.dqh[l], self.y[l])
 
     def outputs(self):
@@ -119,9 +118,10 @@ class Stream64:
 
 class AttnStream:
     """Second workload: the full-attention projections of the model's 16 full-attention
-    layers at m rows. Per layer: rotate + quantise x, the fused query/gate/key/value
-    GEMV (9216 x 5120), rotate + quantise the attention output (stand-in rows), the
-    output GEMV (5120 x 4096). Every layer writes its own outputs."""
+    layers at m rows. Per layer: the fused query/gate/key/value GEMV (9216 x 5120) of the
+    rotated, quantised x, and the output GEMV (5120 x 4096) of the rotated, quantised
+    attention output (stand-in rows), each one tb_gemv_ternary_x call. Every layer writes
+    its own outputs."""
 
     def __init__(self, tb, mats_dev, xs, os_, m, torch):
         self.tb, self.mats, self.m = tb, mats_dev, m
@@ -140,10 +140,8 @@ class AttnStream:
     def step(self):
         tb = self.tb
         for l, (wg, wo) in enumerate(self.mats):
-            tb.tb_rotate_quant_i8(self.x[l], self.q[l], self.dq[l])
-            tb.tb_gemv_ternary(wg, self.q[l], self.dq[l], self.yg[l])
-            tb.tb_rotate_quant_i8(self.oin[l], self.qo[l], self.dqo[l])
-            tb.tb_gemv_ternary(wo, self.qo[l], self.dqo[l], self.y[l])
+            tb.tb_gemv_ternary_x(wg, self.x[l], self.q[l], self.dq[l], self.yg[l])
+            tb.tb_gemv_ternary_x(wo, self.oin[l], self.qo[l], self.dqo[l], self.y[l])
 
     def outputs(self):
         return {name: getattr(self, name).cpu().numpy().copy()
@@ -257,11 +255,11 @@ def read_probe(torch, nbytes: int, reps: int = 5):
 
 
 def gateup_event_timing(torch, s: Stream64, reps: int):
-    """Mean gate/up kernel duration (s): HIP events around back-to-back gate/up launches
-    over every layer's weights (each launch streams its 47 MB from HBM), on the current
-    stream, which is the stream the library launches on."""
+    """Mean duration (s) of the gate/up launch of the separate-call path at M=1 (the
+    rotation of x inside it): HIP events around back-to-back launches over every layer's
+    weights (each launch streams its 47 MB from HBM), on the current stream, which is the
+    stream the library launches on."""
     tb = s.tb
-    tb.tb_rotate_quant_i8(s.x[0], s.q[0], s.dq[0])
     torch.cuda.synchronize()
     n = len(s.layers)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -269,7 +267,7 @@ def gateup_event_timing(torch, s: Stream64, reps: int):
     for _ in range(reps):
         e0.record()
         for wg, wu, _wd in s.layers:
-            tb.tb_ffn_gateup_silu(wg, wu, s.q[0], s.dq[0], s.h[0])
+            tb.tb_ffn_gateup_silu_x(wg, wu, s.x[0], s.q[0], s.dq[0], s.h[0])
         e1.record()
         torch.cuda.synchronize()
         total += e0.elapsed_time(e1) * 1e-3
@@ -282,8 +280,9 @@ def call_breakdown(torch, s: Stream64, layer_s: float, reps: int):
     Each call type is captured 64 times back to back (one per layer's weights) in a HIP
     graph and timed with HIP events around `reps` replays, so a figure is the kernel's
     duration plus the dependency between two launches on one stream. The stream's layer
-    time minus the sum of its three calls is what changes when the calls alternate
-    (caches, launch shapes). Returns microseconds per call and kernel-only GB/s."""
+    time minus the sum of its two calls (gate/up from x, down) is what changes when the
+    calls alternate (caches, launch shapes). The int8-input calls and the separate
+    rotations are timed beside them. Returns microseconds per call and kernel-only GB/s."""
     tb, n = s.tb, len(s.layers)
     tb.tb_rotate_quant_i8(s.x[0], s.q[0], s.dq[0])
     tb.tb_ffn_gateup_silu(*s.layers[0][:2], s.q[0], s.dq[0], s.h[0])
@@ -292,6 +291,8 @@ def call_breakdown(torch, s: Stream64, layer_s: float, reps: int):
     calls = {
         "rotate_quant_x": lambda l, w: tb.tb_rotate_quant_i8(s.x[l], s.q[l], s.dq[l]),
         "gateup_silu": lambda l, w: tb.tb_ffn_gateup_silu(w[0], w[1], s.q[0], s.dq[0], s.h[l]),
+        "gateup_silu_x": lambda l, w: tb.tb_ffn_gateup_silu_x(w[0], w[1], s.x[0], s.q[l], s.dq[l],
+                                                              s.h[l]),
         "rotate_quant_h": lambda l, w: tb.tb_rotate_quant_i8(s.h[0], s.qh[l], s.dqh[l]),
         "down_gemv": lambda l, w: tb.tb_gemv_ternary(w[2], s.qh[0], s.dqh[0], s.y[l]),
         "ffn_down": lambda l, w: tb.tb_ffn_down(w[2], s.h[0], s.qh[l], s.dqh[l], s.y[l]),
@@ -315,7 +316,7 @@ def call_breakdown(torch, s: Stream64, layer_s: float, reps: int):
     w = s.layers[0]
     gu_bytes = w[0].nbytes + w[1].nbytes
     res = {k + "_us": round(v * 1e6, 3) for k, v in out.items()}
-    summed = out["rotate_quant_x"] + out["gateup_silu"] + out["ffn_down"]
+    summed = out["gateup_silu_x"] + out["ffn_down"]
     res.update({
         "layer_us": round(layer_s * 1e6, 3),
         "sum_of_calls_us": round(summed * 1e6, 3),
@@ -617,9 +618,11 @@ def main():
         k_key = "ffn_layers_kernel<1, 0>"
     else:
         k_s = gateup_event_timing(torch, s1, max(2, args.steps // 4))
-        k_bytes = layers[0].gate.nbytes + layers[0].up.nbytes + synth.HIDDEN + 40 * 4 + synth.INTER * 4
-        k_name = "gemv_ring_kernel<1,TERNARY2,GATEUP> (tb_ffn_gateup_silu)"
-        k_key = "gemv_ring_kernel<1, 0, 1>"
+        # weights, x read, its int8 copy and block scales written, h written
+        k_bytes = (layers[0].gate.nbytes + layers[0].up.nbytes + synth.HIDDEN * 4 + synth.HIDDEN
+                   + (synth.HIDDEN // 128) * 4 + synth.INTER * 4)
+        k_name = "gemv_ring_kernel<1,TERNARY2,GATEUP,ROTX> (tb_ffn_gateup_silu_x)"
+        k_key = "gemv_ring_kernel<1, 0, 1, true>"
     k_gbs = k_bytes / k_s / 1e9
     log(f"dominant kernel {k_name}: {k_s * 1e6:.2f} us/launch, {k_gbs:.1f} GB/s")
     breakdown = call_breakdown(torch, s1, ts / args.layers, max(3, args.steps // 4))
@@ -813,8 +816,7 @@ def main():
                    "rows": 1, "format": "ternary 2-bit, 128-weight blocks, fp16 scales",
                    "bytes_per_step": step_bytes,
                    "entry_point": {"fused": "tb_ffn_layers (one persistent launch per 32 layers)",
-                                   "separate": "tb_rotate_quant_i8 + tb_ffn_gateup_silu + "
-                                               "tb_ffn_down per layer, "
+                                   "separate": "tb_ffn_gateup_silu_x + tb_ffn_down per layer, "
                                                + ("hip graph replay" if use_graph else "eager")}[head],
                    "layer_order": "strict: layer l+1 starts after layer l's outputs are written"},
         "us_per_layer": round(t1 / args.layers * 1e6, 3),

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TB_ABI_VERSION 2
+#define TB_ABI_VERSION 3
 #define TB_BLOCK 128
 #define TB_MAX_ROWS 8
 #define TB_MAX_BATCH_ROWS 32
@@ -128,16 +128,47 @@ int tb_gemv_ternary(const tb_matrix *w, const int8_t *q, const float *dq, int m,
 int tb_ffn_gateup_silu(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q,
                        const float *dq, int m, float *h, void *stream);
 
+/* Gate/up from the fp32 activation: tb_rotate_quant_i8(x) into qx, dqx, then
+ * tb_ffn_gateup_silu on them, as one call. The rotated int8 copy is made once
+ * per step and shared by the two projections (PR #1154, commit message); for
+ * up to 4 rows on the dot-product core every workgroup makes its own copy in
+ * LDS while its first weight loads are in flight, which saves the separate
+ * launch, and workgroup 0 writes the copy to qx, dqx. Results are
+ * bit-identical to the two calls (same rotation arithmetic, same fold).
+ *   x    float [m][wg->k]     input, 16-byte aligned
+ *   qx   int8  [m][wg->k]     output: rotquant(x) codes
+ *   dqx  float [m][wg->k/128] output: their block scales
+ *   h    float [m][wg->n]     output
+ * 1 <= m <= 8; the outputs may not overlap one another or the inputs. */
+int tb_ffn_gateup_silu_x(const tb_matrix *wg, const tb_matrix *wu, const float *x, int m,
+                         int8_t *qx, float *dqx, float *h, void *stream);
+
 /* Down projection of the FFN: rotate and quantise h exactly like
  * tb_rotate_quant_i8, into caller-owned workspace, then the GEMV. The pages'
  * int8 scratch is allocated with the weight copy, never as hidden static
  * memory (PR #1154, Summary), so here the caller passes it in.
+ * Up to 4 rows on the dot-product core rotate h inside the GEMV's own launch
+ * (as tb_ffn_gateup_silu_x does with x); the batch variant always runs the
+ * two steps as separate launches. Either way the results are the same bits.
  *   h       float [m][wd->k]    input (the output of tb_ffn_gateup_silu)
  *   qh_ws   int8  [m][wd->k]    workspace; holds rotquant(h) on return
  *   dqh_ws  float [m][wd->k/128] workspace; holds its scales on return
  *   y       float [m][wd->n]    output */
 int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,
                 float *y, void *stream);
+
+/* GEMV of fp32 rows: tb_rotate_quant_i8(x) into qx, dqx, then tb_gemv_ternary
+ * on them, as one call; the same operation and code as tb_ffn_down, for any
+ * projection whose input arrives in fp32 (the attention projections of the
+ * same model). Up to 4 rows on the dot-product core rotate x inside the
+ * GEMV's launch; results are bit-identical to the two calls.
+ *   x    float [m][w->k]     input, 16-byte aligned
+ *   qx   int8  [m][w->k]     output: rotquant(x) codes
+ *   dqx  float [m][w->k/128] output: their block scales
+ *   y    float [m][w->n]     output
+ * 1 <= m <= 8; the outputs may not overlap one another or the inputs. */
+int tb_gemv_ternary_x(const tb_matrix *w, const float *x, int m, int8_t *qx, float *dqx, float *y,
+                      void *stream);
 
 /* Test export: the per-block integer sums, before the scale fold, computed by
  * the integer core that production runs:

@@ -22,10 +22,12 @@ TB_FMT_TERNARY2, TB_FMT_SIGN1 = 0, 1
 BLOCK = 128
 MAX_ROWS = 8
 MAX_BATCH_ROWS = 32
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # every symbol include/tb.h declares
-ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_ffn_gateup_silu", "tb_ffn_down",
+ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_gemv_ternary_x", "tb_ffn_gateup_silu",
+               "tb_ffn_gateup_silu_x",
+               "tb_ffn_down",
                "tb_gemv_block_sums", "tb_rotate_quant_i8_batch", "tb_gemv_ternary_batch",
                "tb_ffn_gateup_silu_batch", "tb_ffn_down_batch", "tb_gemv_block_sums_batch",
                "tb_ffn_down_noalloc",
@@ -56,6 +58,8 @@ _SIGS = {
     "tb_rotate_quant_i8": ([_P, _I, _I, _P, _P, _P], _I),
     "tb_gemv_ternary": ([_MP, _P, _P, _I, _P, _P], _I),
     "tb_ffn_gateup_silu": ([_MP, _MP, _P, _P, _I, _P, _P], _I),
+    "tb_ffn_gateup_silu_x": ([_MP, _MP, _P, _I, _P, _P, _P, _P], _I),
+    "tb_gemv_ternary_x": ([_MP, _P, _I, _P, _P, _P, _P], _I),
     "tb_ffn_down": ([_MP, _P, _I, _P, _P, _P, _P], _I),
     "tb_gemv_block_sums": ([_MP, _P, _I, _P, _P], _I),
     "tb_rotate_quant_i8_batch": ([_P, _I, _I, _P, _P, _P], _I),
@@ -157,10 +161,22 @@ def tb_gemv_ternary(w: Matrix, q, dq, y, stream=None) -> None:
           y.data_ptr(), _stream(stream))
 
 
+def tb_gemv_ternary_x(w: Matrix, x, qx, dqx, y, stream=None) -> None:
+    """y = GEMV of w against rotquant(x), written to qx, dqx; one call."""
+    _call("tb_gemv_ternary_x", ctypes.byref(w.c), x.data_ptr(), _rows(x), qx.data_ptr(),
+          dqx.data_ptr(), y.data_ptr(), _stream(stream))
+
+
 def tb_ffn_gateup_silu(wg: Matrix, wu: Matrix, q, dq, h, stream=None) -> None:
     """h float32 [m][wg.n] = silu(wg q) * (wu q), from one shared int8 copy."""
     _call("tb_ffn_gateup_silu", ctypes.byref(wg.c), ctypes.byref(wu.c), q.data_ptr(),
           dq.data_ptr(), _rows(q), h.data_ptr(), _stream(stream))
+
+
+def tb_ffn_gateup_silu_x(wg: Matrix, wu: Matrix, x, qx, dqx, h, stream=None) -> None:
+    """h = silu(wg q) * (wu q) with (q, dq) = rotquant(x), written to qx, dqx; one call."""
+    _call("tb_ffn_gateup_silu_x", ctypes.byref(wg.c), ctypes.byref(wu.c), x.data_ptr(), _rows(x),
+          qx.data_ptr(), dqx.data_ptr(), h.data_ptr(), _stream(stream))
 
 
 def tb_ffn_down(wd: Matrix, h, qh_ws, dqh_ws, y, stream=None) -> None:

@@ -149,6 +149,12 @@ struct GemvArgs {
     int slice_chunks;        // LDS slots per pass (sliced kernel)
     uint32_t codes_bytes;    // per matrix, < 2^31 (buffer addressing)
     uint32_t scales_bytes;
+    // fp32 input rotated in the kernel (gemv_ring_kernel with ROTX): x [M][k]; workgroup 0
+    // writes its codes and block terms to qx [M][k] and dqx [M][k/128]
+    const float *x;
+    int8_t *qx;
+    float *dqx;
+    float unit;              // fp32(1 / (127 sqrt(128)))
 };
 
 // Writes the results of one finished row (lane 0 of the row's 16 lanes).
@@ -258,6 +264,74 @@ __device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act
 }
 
 // ------------------------------------------------------------------------------------
+// Staging from the fp32 input x[M][k]: every workgroup rotates and quantises all M k/128
+// blocks itself, one 16-lane group per block, with rotquant_regs (the arithmetic of
+// rotquant_kernel, so codes and terms are bit-identical to a separate rotate-quantise
+// call), and stores the codes straight into the step-major layout, the block terms into
+// dq_s (zero padded by one step of blocks) and, sign format, the code sums into qsum_s.
+// Workgroup 0 also writes the codes and terms to qx and dqx. The x loads of the first
+// kXRounds rounds go out before `prologue` (the weight stream's first loads), so they
+// are not queued behind them; later rounds load after it.
+// ------------------------------------------------------------------------------------
+template <int M, int FMT, int NTHREADS, class Prologue>
+__device__ __forceinline__ void stage_rotate(const GemvArgs &a, uint8_t *act, float *dq_s,
+                                             int *qsum_s, Prologue &&prologue)
+{
+    constexpr int kGroups = NTHREADS / 16, kXRounds = 2;
+    constexpr int kBlocksPerStep = kChunkLanes / Fmt<FMT>::kChunksPerBlock;
+    const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
+    const int k = a.k, nb = k / kBlock, Z = M * nb;
+    const bool out = blockIdx.x == 0;
+    auto load = [&](float (&v)[8], int z) {
+        const float *src = a.x + (size_t)(z / nb) * k + (size_t)(z % nb) * kBlock + l16 * 8;
+        const float4 lo = *reinterpret_cast<const float4 *>(src);
+        const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    };
+    auto block = [&](float (&v)[8], int z) {
+        const int m = z / nb, b = z % nb;
+        uint32_t pk[2];
+        float dq;
+        int qsum;
+        rotquant_regs(v, l16, a.unit, pk, dq, qsum);
+        store_block_step<M, FMT>(act, m, b, l16, pk);
+        if (l16 == 0) {
+            dq_s[b * M + m] = dq;
+            if (FMT == TB_FMT_SIGN1)
+                qsum_s[b * M + m] = qsum;
+        }
+        if (out) {
+            *reinterpret_cast<uint2 *>(a.qx + (size_t)m * k + (size_t)b * kBlock + l16 * 8) =
+                make_uint2(pk[0], pk[1]);
+            if (l16 == 0)
+                a.dqx[m * nb + b] = dq;
+        }
+    };
+    // (a 16-lane group takes or skips a block as a whole: its row shuffles stay inside it)
+    float xv[kXRounds][8];
+#pragma unroll
+    for (int r = 0; r < kXRounds; ++r)
+        if (grp + r * kGroups < Z)
+            load(xv[r], grp + r * kGroups);
+    for (int i = Z + tid; i < (nb + kBlocksPerStep) * M; i += NTHREADS) {
+        dq_s[i] = 0.0f;
+        if (FMT == TB_FMT_SIGN1)
+            qsum_s[i] = 0;
+    }
+    prologue();
+#pragma unroll
+    for (int r = 0; r < kXRounds; ++r)
+        if (grp + r * kGroups < Z)
+            block(xv[r], grp + r * kGroups);
+    for (int z = grp + kXRounds * kGroups; z < Z; z += kGroups) {
+        float v[8];
+        load(v, z);
+        block(v, z);
+    }
+}
+
+// ------------------------------------------------------------------------------------
 // Streaming GEMV: one workgroup per CU, the whole activation staged once in LDS
 // (step-major layout).
 //   * A row tile is 4 rows; workgroup c owns the contiguous tiles [tA, tB) of a near-equal
@@ -276,10 +350,13 @@ __device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act
 // The loop is written for the VALU budget: at M = 1 one 1 KB wave item needs 52 VALU ops
 // of decode and dot products, so the rest is kept to a handful. Rows past n, empty slots
 // and ragged chunks use out-of-range buffer offsets, which read zeros.
+// ROTX: the activation arrives as fp32 x and each workgroup rotates and quantises it
+// itself (stage_rotate), which saves a launch on the decode path.
 // ------------------------------------------------------------------------------------
-template <int M, int FMT, int MODE>
+template <int M, int FMT, int MODE, bool ROTX = false>
 __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
 {
+    static_assert(!ROTX || MODE != kModeIsum, "the block-sum export takes int8 input");
     extern __shared__ __align__(16) uint8_t lds[];
     using L = StepLayout<M, FMT>;
     constexpr bool kTwo = MODE == kModeGateUp;
@@ -385,11 +462,15 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     };
 
     // ---- staging (q and the block terms; the ring prologue between loads and stores)
-    stage_activation<M, FMT, MODE, kRingThreads, false>(a, act, dq_s, qsum_s, [&]() {
+    auto prologue = [&]() {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
             issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
-    });
+    };
+    if constexpr (ROTX)
+        stage_rotate<M, FMT, kRingThreads>(a, act, dq_s, qsum_s, prologue);
+    else
+        stage_activation<M, FMT, MODE, kRingThreads, false>(a, act, dq_s, qsum_s, prologue);
     __syncthreads();
 
     // ---- compute side -----------------------------------------------------------------
@@ -1438,6 +1519,23 @@ bool wide_fits(const DeviceInfo &info, int mode, const tb_matrix *w, int m)
     return mfma_lds_bytes(w->fmt, mode, w->n, w->k, m, grid) <= (size_t)info.lds_limit;
 }
 
+// LDS bytes of gemv_ring_kernel for m rows on a grid of `grid` workgroups: the step-major
+// activation, the block terms (and sign code sums) zero padded by one step of blocks, the
+// item counter, and the step partials of the largest workgroup's items.
+size_t ring_lds_bytes(const tb_matrix *w, int mode, int m, int grid)
+{
+    const bool tern = w->fmt == TB_FMT_TERNARY2;
+    const int C = w->k / (tern ? 64 : 128), nb = w->k / kBlock;
+    const int steps = (C + kChunkLanes - 1) / kChunkLanes;
+    const long tiles = (w->n + kRowsPerWave - 1) / kRowsPerWave;
+    const size_t step_bytes = (size_t)(tern ? 1024 : 2048) * m;
+    const size_t pad_blocks = (size_t)(kChunkLanes / (tern ? 2 : 1));
+    const size_t ring_terms = (size_t)m * (nb + pad_blocks) * 4 * (tern ? 1 : 2);
+    const size_t ring_items = (size_t)((tiles + grid - 1) / grid) * steps;
+    const size_t ring_part = 16 + ring_items * kRowsPerWave * m * (mode == kModeGateUp ? 2 : 1) * 4;
+    return (size_t)steps * step_bytes + ring_terms + ring_part;
+}
+
 int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t *q,
                 const float *dq, int m, float *out, int32_t *isum, hipStream_t stream)
 {
@@ -1445,7 +1543,7 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     int rc = device_info(&info);
     if (rc)
         return rc;
-    GemvArgs a;
+    GemvArgs a = {};
     a.codes0 = static_cast<const uint8_t *>(w0->codes);
     a.scales0 = w0->scales;
     a.codes1 = w1 ? static_cast<const uint8_t *>(w1->codes) : nullptr;
@@ -1520,12 +1618,7 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     if (m > 8)
         return TB_EUNSUPPORTED;   // the batch launcher only passes rows that fit
     // whole activation in LDS: the persistent ring kernel, one workgroup per CU
-    const size_t pad_blocks = (size_t)(kChunkLanes / (w0->fmt == TB_FMT_TERNARY2 ? 2 : 1));
-    const size_t ring_terms = (size_t)m * (nb + pad_blocks) * 4 * (w0->fmt == TB_FMT_TERNARY2 ? 1 : 2);
-    // item counter, then the step partials of the largest workgroup's items
-    const size_t ring_items = (size_t)((tiles + ring_grid - 1) / ring_grid) * steps;
-    const size_t ring_part = 16 + ring_items * kRowsPerWave * m * (mode == kModeGateUp ? 2 : 1) * 4;
-    const size_t ring_lds = (size_t)steps * step_bytes + ring_terms + ring_part;
+    const size_t ring_lds = ring_lds_bytes(w0, mode, m, ring_grid);
     // (both kernels fold every row in the same order, so the choice never changes a result)
     if (ring_lds <= (size_t)info.lds_limit) {
         GemvFn fn = gemv_ring_kernel_pick(w0->fmt, mode, m);
@@ -1558,6 +1651,79 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
+
+// gemv_ring_kernel with the rotation of x inside (ROTX), for the row counts it is built for
+// Each 16-lane group of a workgroup rotates up to this many blocks (a workgroup of 1024
+// lanes: m * k/128 <= 128). Separate-call FFN stream at 64 layers, µs per layer, with 1 / 2
+// / 3 blocks per group: M=1 21.64 / 21.66 / 22.54 (the down stage's 136 blocks inside cost
+// 1 µs more than the launch they save), M=2 26.14 / 25.43 / 25.42, M=3 30.51 / 30.00 /
+// 29.97, M=4 32.98 / 32.99 / 34.15; two launches per layer before: 23.06, 25.90, 30.44, 32.92.
+#ifndef TB_ROTX_MAX_ROUNDS
+#define TB_ROTX_MAX_ROUNDS 2
+#endif
+#ifndef TB_ROTX_MAX_ROWS
+#define TB_ROTX_MAX_ROWS 4
+#endif
+template <int FMT, int MODE>
+GemvFn gemv_ring_rotx_pick_m(int m)
+{
+    static_assert(TB_ROTX_MAX_ROWS >= 1 && TB_ROTX_MAX_ROWS <= 4, "built for 1..4 rows");
+    switch (m) {
+    case 1: return gemv_ring_kernel<1, FMT, MODE, true>;
+    case 2: return TB_ROTX_MAX_ROWS >= 2 ? gemv_ring_kernel<2, FMT, MODE, true> : nullptr;
+    case 3: return TB_ROTX_MAX_ROWS >= 3 ? gemv_ring_kernel<3, FMT, MODE, true> : nullptr;
+    case 4: return TB_ROTX_MAX_ROWS >= 4 ? gemv_ring_kernel<4, FMT, MODE, true> : nullptr;
+    default: return nullptr;
+    }
+}
+
+// One launch that rotates and quantises x[m][k] inside the GEMV (mode y or gate/up), when
+// the rows take the ring kernel (below the matrix-core thresholds, LDS plan fits, at most
+// TB_ROTX_MAX_ROWS rows); TB_EUNSUPPORTED otherwise, and then nothing was launched.
+// Workgroup 0 writes rotquant(x) to qx, dqx.
+int launch_gemv_rotx(int mode, const tb_matrix *w0, const tb_matrix *w1, const float *x, int m,
+                     int8_t *qx, float *dqx, float *out, hipStream_t stream)
+{
+    DeviceInfo info;
+    int rc = device_info(&info);
+    if (rc)
+        return rc;
+    const bool tern = w0->fmt == TB_FMT_TERNARY2;
+    const int nb = w0->k / kBlock;
+    if (m > TB_ROTX_MAX_ROWS || (long)m * nb > (long)TB_ROTX_MAX_ROUNDS * (kRingThreads / 16) ||
+        (nb % (tern ? 2 : 4) == 0 && m >= mfma_min_rows(tern, mode != kModeY)))
+        return TB_EUNSUPPORTED;
+    const long tiles = (w0->n + kRowsPerWave - 1) / kRowsPerWave;
+    const int grid = (int)(tiles < info.cus ? tiles : info.cus);
+    const size_t lds = ring_lds_bytes(w0, mode, m, grid);
+    if (lds > (size_t)info.lds_limit)
+        return TB_EUNSUPPORTED;
+    GemvFn fn = tern ? (mode == kModeGateUp ? gemv_ring_rotx_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
+                                            : gemv_ring_rotx_pick_m<TB_FMT_TERNARY2, kModeY>(m))
+                     : (mode == kModeGateUp ? gemv_ring_rotx_pick_m<TB_FMT_SIGN1, kModeGateUp>(m)
+                                            : gemv_ring_rotx_pick_m<TB_FMT_SIGN1, kModeY>(m));
+    if (!fn)
+        return TB_EUNSUPPORTED;
+    if ((rc = set_lds(fn, lds)))
+        return rc;
+    GemvArgs a = {};
+    a.codes0 = static_cast<const uint8_t *>(w0->codes);
+    a.scales0 = w0->scales;
+    a.codes1 = w1 ? static_cast<const uint8_t *>(w1->codes) : nullptr;
+    a.scales1 = w1 ? w1->scales : nullptr;
+    a.n = w0->n;
+    a.k = w0->k;
+    a.out = out;
+    a.codes_bytes = (uint32_t)codes_bytes(w0);
+    a.scales_bytes = (uint32_t)((scales_bytes(w0) + 3) & ~(size_t)3);
+    a.slice_chunks = w0->k / (tern ? 64 : 128);
+    a.x = x;
+    a.qx = qx;
+    a.dqx = dqx;
+    a.unit = dq_unit();
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kRingThreads), lds, stream, a);
+    return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+}
 
 // A batch of m (1..32) independent rows as balanced chunks: chunks of up to 16 rows on
 // gemv_mfma_kernel (all 16 B columns live) where they fit the device's LDS, else of up to 8
@@ -1768,6 +1934,42 @@ int tb_ffn_gateup_silu_batch(const tb_matrix *wg, const tb_matrix *wu, const int
     return gateup_impl(wg, wu, q, dq, m, h, stream, true);
 }
 
+int tb_ffn_gateup_silu_x(const tb_matrix *wg, const tb_matrix *wu, const float *x, int m,
+                         int8_t *qx, float *dqx, float *h, void *stream)
+{
+    int rc = check_matrix(wg);
+    if (rc)
+        return rc;
+    if ((rc = check_matrix(wu)))
+        return rc;
+    if (wg->n != wu->n || wg->k != wu->k || wg->fmt != wu->fmt)
+        return TB_EINVAL;
+    if (check_rows(m, TB_MAX_ROWS) || !x || !qx || !dqx || !h)
+        return TB_EINVAL;
+    if (!aligned16(x) || !aligned16(qx) || !aligned16(dqx) || !aligned16(h))
+        return TB_EALIGN;
+    const int k = wg->k;
+    const Range rx = range_of(x, (size_t)m * k * 4), rq = range_of(qx, (size_t)m * k),
+                rd = range_of(dqx, (size_t)m * (k / kBlock) * 4),
+                rh = range_of(h, (size_t)m * wg->n * 4);
+    const Range outs[3] = {rq, rd, rh};
+    const Range ins[5] = {rx, range_of(wg->codes, codes_bytes(wg)), range_of(wg->scales, scales_bytes(wg)),
+                          range_of(wu->codes, codes_bytes(wu)), range_of(wu->scales, scales_bytes(wu))};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return TB_EINVAL;
+    if (overlaps(rq, rd) || overlaps(rq, rh) || overlaps(rd, rh))
+        return TB_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = launch_gemv_rotx(kModeGateUp, wg, wu, x, m, qx, dqx, h, s);
+    if (rc != TB_EUNSUPPORTED)
+        return rc;
+    if ((rc = launch_rotquant(x, m, k, qx, dqx, s)))
+        return rc;
+    return launch_gemv(kModeGateUp, wg, wu, qx, dqx, m, h, nullptr, s);
+}
+
 static int down_impl(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,
                      float *y, void *stream, bool batch)
 {
@@ -1793,6 +1995,11 @@ static int down_impl(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, 
     if (overlaps(rq, rd) || overlaps(rq, ry) || overlaps(rd, ry))
         return TB_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!batch) {
+        rc = launch_gemv_rotx(kModeY, wd, nullptr, h, m, qh_ws, dqh_ws, y, s);
+        if (rc != TB_EUNSUPPORTED)
+            return rc;
+    }
     if ((rc = launch_rotquant(h, m, k, qh_ws, dqh_ws, s)))
         return rc;
     return (batch ? launch_gemv_batch : launch_gemv)(kModeY, wd, nullptr, qh_ws, dqh_ws, m, y,
@@ -1803,6 +2010,12 @@ int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float
                 float *y, void *stream)
 {
     return down_impl(wd, h, m, qh_ws, dqh_ws, y, stream, false);
+}
+
+int tb_gemv_ternary_x(const tb_matrix *w, const float *x, int m, int8_t *qx, float *dqx, float *y,
+                      void *stream)
+{
+    return down_impl(w, x, m, qx, dqx, y, stream, false);
 }
 
 int tb_ffn_down_batch(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float *dqh_ws,

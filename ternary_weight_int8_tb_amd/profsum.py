@@ -47,11 +47,15 @@ def short_name(name: str) -> str:
 
 # Algorithmic bytes per launch at M=1 (weights + activations read + outputs written).
 ALGORITHMIC = {
+    # gate/up with the rotation of x inside: x read, its int8 copy and scales written
+    "gemv_ring_kernel<1, 0, 1, true>": 2 * MATRIX_BYTES + HIDDEN * 4 + HIDDEN + NB_H * 4 + INTER * 4,
     "gemv_ring_kernel<1, 0, 1>": 2 * MATRIX_BYTES + HIDDEN + NB_H * 4 + INTER * 4,
     "gemv_ring_kernel<1, 0, 0>": MATRIX_BYTES + INTER + NB_N * 4 + HIDDEN * 4,
     "ffn_layers_kernel<1, 0>": 32 * (3 * MATRIX_BYTES + 2 * HIDDEN * 4),
 }
 WHAT = {
+    "gemv_ring_kernel<1, 0, 1, true>": "tb_ffn_gateup_silu_x at M=1 (gate and up, 47,349,760 weight "
+                                       "bytes, the rotation of x inside)",
     "gemv_ring_kernel<1, 0, 1>": "tb_ffn_gateup_silu at M=1 (gate and up, 47,349,760 weight bytes)",
     "gemv_ring_kernel<1, 0, 0>": "the GEMV of tb_ffn_down at M=1 (23,674,880 weight bytes)",
     "ffn_layers_kernel<1, 0>": "one tb_ffn_layers launch of 32 layers at M=1",
@@ -73,13 +77,18 @@ def read_stats(d: str):
 
 
 SIGN_MATRIX_BYTES = INTER * HIDDEN // 8 + INTER * NB_H * 2
-# the four kernels of one layer of the separate-call stream: rotquant(x), gate/up,
-# rotquant(h), down GEMV; weight bytes of the two GEMV launches
+# the kernels of one layer of the separate-call stream (tb_ffn_gateup_silu_x, tb_ffn_down),
+# each with the weight bytes it streams: at M=1 the gate/up launch rotates x itself and the
+# down call is rotquant(h) + GEMV; at M=8 both calls are rotquant + GEMV
 STREAMS = {
-    "ternary M=1": ("gemv_ring_kernel<1, 0, 1>", "gemv_ring_kernel<1, 0, 0>", MATRIX_BYTES),
-    "ternary M=8": ("gemv_mfma_kernel<8, 0, 1>", "gemv_mfma_kernel<8, 0, 0>", MATRIX_BYTES),
-    "sign M=1": ("gemv_ring_kernel<1, 1, 1>", "gemv_ring_kernel<1, 1, 0>", SIGN_MATRIX_BYTES),
-    "sign M=8": ("gemv_mfma_kernel<8, 1, 1>", "gemv_mfma_kernel<8, 1, 0>", SIGN_MATRIX_BYTES),
+    "ternary M=1": [("gemv_ring_kernel<1, 0, 1, true>", 2 * MATRIX_BYTES), ("rotquant_kernel", 0),
+                    ("gemv_ring_kernel<1, 0, 0>", MATRIX_BYTES)],
+    "ternary M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 0, 1>", 2 * MATRIX_BYTES),
+                    ("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 0, 0>", MATRIX_BYTES)],
+    "sign M=1": [("gemv_ring_kernel<1, 1, 1, true>", 2 * SIGN_MATRIX_BYTES), ("rotquant_kernel", 0),
+                 ("gemv_ring_kernel<1, 1, 0>", SIGN_MATRIX_BYTES)],
+    "sign M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 1, 1>", 2 * SIGN_MATRIX_BYTES),
+                 ("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 1, 0>", SIGN_MATRIX_BYTES)],
 }
 
 
@@ -91,7 +100,7 @@ def median(v):
 def stream_passes(d: str):
     """Graph passes of each 64-layer stream in a kernel trace.
 
-    A pass is 256 consecutive dispatches in the layer order above. Eager passes (host
+    A pass is 64 layers of consecutive dispatches in the layer order above. Eager passes (host
     launch gaps between kernels) are dropped: a graph pass is one whose median gap between
     consecutive dispatches is at most zero. Returns, per stream, the number of passes
     and per position the median duration and the median gap to the next dispatch (us),
@@ -104,8 +113,9 @@ def stream_passes(d: str):
                       for r in csv.DictReader(fh)))
     names = [n for _, _, n in seq]
     out = {}
-    for label, (gu, dn, _) in STREAMS.items():
-        pat = ["rotquant_kernel", gu, "rotquant_kernel", dn] * LAYERS
+    for label, layer in STREAMS.items():
+        per = len(layer)
+        pat = [name for name, _ in layer] * LAYERS
         passes, i = [], 0
         while i + len(pat) <= len(seq):
             if names[i:i + len(pat)] == pat:
@@ -118,10 +128,10 @@ def stream_passes(d: str):
         if not passes:
             continue
         pos = []
-        for k in range(4):
-            dur = [(p[j][1] - p[j][0]) / 1e3 for p in passes for j in range(k, len(pat), 4)]
-            gap = [(p[j + 1][0] - p[j][1]) / 1e3 for p in passes for j in range(k, len(pat) - 1, 4)]
-            pos.append((pat[k], median(dur), median(gap), sum(gap) / len(gap)))
+        for k in range(per):
+            dur = [(p[j][1] - p[j][0]) / 1e3 for p in passes for j in range(k, len(pat), per)]
+            gap = [(p[j + 1][0] - p[j][1]) / 1e3 for p in passes for j in range(k, len(pat) - 1, per)]
+            pos.append((pat[k], median(dur), median(gap), sum(gap) / len(gap), layer[k][1]))
         span = median([(p[-1][1] - p[0][0]) / 1e3 / LAYERS for p in passes])
         busy = median([sum(e - b for b, e, _ in p) / 1e3 / LAYERS for p in passes])
         out[label] = {"passes": len(passes), "positions": pos, "span_us": span, "busy_us": busy}
@@ -174,10 +184,13 @@ def main():
     for r in stats[:16]:
         lines.append(f"| `{r['name']}` | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | "
                      f"{r['max_us']:.2f} | {r['pct']:.1f} |")
-    lines += ["", "Template arguments: gemv_ring_kernel<M, FMT, MODE>, FMT 0 = ternary, 1 = sign; "
-              "MODE 0 = single GEMV (down), 1 = gate/up + SiLU, 2 = block-sum export. "
-              "gemv_mfma_kernel<M, FMT, MODE> runs on the matrix cores (ternary: gate/up for "
-              "M >= 5, a single GEMV for M >= 6; sign: gate/up for M >= 5, a single GEMV for M >= 7). "
+    lines += ["", "Template arguments: gemv_ring_kernel<M, FMT, MODE[, ROTX]>, FMT 0 = ternary, 1 = sign; "
+              "MODE 0 = single GEMV (down), 1 = gate/up + SiLU, 2 = block-sum export; ROTX true = "
+              "the fp32 input rotated and quantised inside the launch. "
+              "gemv_mfma_pack_kernel<M, FMT, MODE> (two blocks per MFMA, M <= 8) and "
+              "gemv_mfma_kernel<M, FMT, MODE> (one block per MFMA, batches above 8 rows) run on the "
+              "matrix cores (ternary: gate/up for M >= 5, a single GEMV for M >= 6; sign: gate/up "
+              "for M >= 5, a single GEMV for M >= 7). "
               "ffn_layers_kernel<M, FMT> is one tb_ffn_layers launch of up to 32 whole layers. "
               "stream_read_kernel is the 4 GiB read probe."]
     if bench:
@@ -189,7 +202,8 @@ def main():
     passes = stream_passes(a.stats)
     if passes:
         lines += ["", "Graph passes of the 64-layer separate-call stream in the same trace (per layer: "
-                  "rotquant(x), gate/up, rotquant(h), down GEMV). Durations and gaps are medians over "
+                  "tb_ffn_gateup_silu_x, then tb_ffn_down; at M=1 the gate/up launch rotates x "
+                  "itself, at M=8 each call is rotquant + GEMV). Durations and gaps are medians over "
                   "every layer of every graph pass; a negative gap means the tracer stamped the next "
                   "start before the previous end. Kernel-only GB/s counts weight bytes over the "
                   "traced duration. The tracer's completion signal per dispatch lengthens passes, "
@@ -197,9 +211,7 @@ def main():
                   "", "| stream | passes | kernel | median us | kernel-only GB/s | median gap after us "
                   "| mean gap after us |", "|---|---|---|---|---|---|---|"]
         for label, r in passes.items():
-            mbytes = STREAMS[label][2]
-            for k, (name, dur, gap, mgap) in enumerate(r["positions"]):
-                wb = {1: 2 * mbytes, 3: mbytes}.get(k)
+            for name, dur, gap, mgap, wb in r["positions"]:
                 gbs = f"{wb / dur / 1e3:.0f}" if wb else "-"
                 lines.append(f"| {label} | {r['passes']} | `{name}` | {dur:.2f} | {gbs} | {gap:.2f} | "
                              f"{mgap:.2f} |")

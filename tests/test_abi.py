@@ -95,6 +95,43 @@ def test_gateup_validation(L):
     assert gu(mat(), up, h=0x10000000) == tb.TB_EINVAL       # h overlaps up's codes
 
 
+def test_gateup_x_validation(L):
+    # tb_ffn_gateup_silu_x(wg, wu, x, m, qx, dqx, h): the x call checks what both of the
+    # calls it replaces check, and that its three outputs overlap nothing
+    wg, wu = mat(), mat(codes=0x10000000, scales=0x14000000)
+
+    def gx(wg=wg, wu=wu, x=0x20000000, m=1, qx=0x30000000, dqx=0x34000000, h=0x38000000):
+        return L.tb_ffn_gateup_silu_x(ctypes.byref(wg), ctypes.byref(wu), x, m, qx, dqx, h, None)
+    assert gx(wu=mat(codes=0x10000000, scales=0x14000000, n=128)) == tb.TB_EINVAL
+    assert gx(wu=mat(codes=0x10000000, scales=0x14000000, fmt=1)) == tb.TB_EINVAL
+    assert gx(m=0) == tb.TB_EINVAL
+    assert gx(m=9) == tb.TB_EINVAL
+    for name in ("x", "qx", "dqx", "h"):
+        assert gx(**{name: 0}) == tb.TB_EINVAL, name
+    assert gx(x=0x20000004) == tb.TB_EALIGN
+    assert gx(qx=0x30000008) == tb.TB_EALIGN
+    assert gx(dqx=0x34000004) == tb.TB_EALIGN
+    assert gx(h=0x38000004) == tb.TB_EALIGN
+    assert gx(qx=0x20000000) == tb.TB_EINVAL                 # qx overlaps x
+    assert gx(h=0x10000000) == tb.TB_EINVAL                  # h overlaps up's codes
+    assert gx(dqx=0x30000000) == tb.TB_EINVAL                # dqx overlaps qx
+    assert gx(h=0x34000000) == tb.TB_EINVAL                  # h overlaps dqx
+
+
+def test_gemv_x_validation(L):
+    # tb_gemv_ternary_x shares tb_ffn_down's checks
+    w = mat()
+
+    def gx(x=0x20000000, m=1, qx=0x30000000, dqx=0x34000000, y=0x38000000):
+        return L.tb_gemv_ternary_x(ctypes.byref(w), x, m, qx, dqx, y, None)
+    assert gx(m=0) == tb.TB_EINVAL
+    assert gx(m=9) == tb.TB_EINVAL
+    assert gx(qx=0) == tb.TB_EINVAL
+    assert gx(x=0x20000004) == tb.TB_EALIGN
+    assert gx(qx=0x20000000) == tb.TB_EINVAL                 # qx overlaps x
+    assert gx(y=0x30000000) == tb.TB_EINVAL                  # y overlaps qx
+
+
 def test_down_validation(L):
     wd = mat(n=5120, k=17408)
 
@@ -189,6 +226,10 @@ def test_valid_calls_without_a_device_return_ehip(L):
     assert L.tb_ffn_gateup_silu(ctypes.byref(w), ctypes.byref(w2), ALIGNED3, ALIGNED4, 1, y,
                                 None) == tb.TB_EHIP
     assert L.tb_gemv_block_sums(ctypes.byref(w), ALIGNED3, 1, ALIGNED4, None) == tb.TB_EHIP
+    assert L.tb_ffn_gateup_silu_x(ctypes.byref(w), ctypes.byref(w2), 0x20000000, 1, 0x30000000,
+                                  0x34000000, 0x38000000, None) == tb.TB_EHIP
+    assert L.tb_gemv_ternary_x(ctypes.byref(w), 0x20000000, 1, 0x30000000, 0x34000000,
+                               0x38000000, None) == tb.TB_EHIP
 
 
 def test_batch_calls_validate_rows_and_arguments(L):

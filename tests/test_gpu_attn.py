@@ -83,3 +83,24 @@ def test_attention_projection_batch16(o, layers, fmt):
     assert bounds.gemv_ok(yn, yo, sabs)[0]
     for r in (0, 9, 15):
         assert gu.gemv(wd, q[r:r + 1], dq[r:r + 1])[0].tobytes() == yn[r].tobytes(), r
+
+
+@pytest.mark.parametrize("fmt", [TERN, SIGN])
+@pytest.mark.parametrize("which", ["qkvg", "o"])
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_attention_projection_from_fp32(o, layers, fmt, which, m):
+    # tb_gemv_ternary_x (the rotation inside the GEMV's launch up to 4 rows) against the
+    # oracle's rotquant and the two separate calls
+    w = getattr(layers[fmt], which)
+    say(f"attention {which} from fp32 fmt={fmt} m={m}")
+    tensor = synth.T_ACT if which == "qkvg" else synth.T_ATTN_OUT
+    x = synth.normal_rows(8, w.k, 83, 0, tensor)[:m]
+    wd = tb.Matrix.upload(w)
+    qx, dqx, y = gu.i8_out(m, w.k), gu.f32_out(m, w.k // 128), gu.f32_out(m, w.n)
+    tb.tb_gemv_ternary_x(wd, gu.dev(x), qx, dqx, y)
+    qn, dqn, yn = gu.host(qx), gu.host(dqx), gu.host(y)
+    qo, dqo = o.rotate_quant(x)
+    assert np.array_equal(qn, qo) and np.array_equal(dqn.view(np.uint32), dqo.view(np.uint32))
+    assert yn.tobytes() == gu.gemv(wd, qo, dqo).tobytes()
+    yo, sabs = o.gemv(w, qo, dqo)
+    assert bounds.gemv_ok(yn, yo, sabs)[0]
