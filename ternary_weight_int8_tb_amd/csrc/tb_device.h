@@ -467,12 +467,11 @@ __device__ __forceinline__ void stage_unit_store_mfma(const StageUnit<FMT> &u, u
     }
 }
 
-// One rotated-quantised block into the step-major layout (or, MFMA_LAYOUT, the layout of
-// the matrix-core kernels, [chunk][code word][row] x 16 bytes (sign: [chunk][dword][half]
-// [row])). The 16-lane group holds block b of row m; lane L has codes 8L .. 8L+7 packed
-// little-endian in pk[0], pk[1] (the registers rotquant_regs returns). Lanes exchange codes
-// so that each writes 8 bytes of the layout that the staging from global memory writes.
-template <int M, int FMT, bool MFMA_LAYOUT = false>
+// One rotated-quantised block into the step-major layout. The 16-lane group holds block b
+// of row m; lane L has codes 8L .. 8L+7 packed little-endian in pk[0], pk[1] (the
+// registers rotquant_regs returns). Lanes exchange codes so that each writes 8 bytes of
+// the layout that stage_unit_store_step writes from global memory.
+template <int M, int FMT>
 __device__ __forceinline__ void store_block_step(uint8_t *act, int m, int b, int lane16,
                                                  const uint32_t (&pk)[2])
 {
@@ -517,15 +516,8 @@ __device__ __forceinline__ void store_block_step(uint8_t *act, int m, int b, int
         plane = 2 * (lane16 >> 2) + (i >> 1);
         half = i & 1;
     }
-    if constexpr (MFMA_LAYOUT) {
-        // 16-byte group (chunk c, plane) of row m: slot (4 c + plane) M + m (ternary; a
-        // plane is a code word) or (8 c + plane) M + m (sign; a plane is a dword half)
-        const int slot = ((FMT == TB_FMT_TERNARY2 ? 4 : 8) * c + plane) * M + m;
-        *reinterpret_cast<uint2 *>(act + (size_t)slot * 16 + half * 8) = make_uint2(o[0], o[1]);
-    } else {
-        *reinterpret_cast<uint2 *>(act + (size_t)(c >> 4) * L::kStepBytes + (c & 15) * 16 +
-                                   L::offset(plane, m) + half * 8) = make_uint2(o[0], o[1]);
-    }
+    *reinterpret_cast<uint2 *>(act + (size_t)(c >> 4) * L::kStepBytes + (c & 15) * 16 +
+                               L::offset(plane, m) + half * 8) = make_uint2(o[0], o[1]);
 }
 
 // Integer sums of one chunk against all M rows, step-major layout; `lds` is this lane's
