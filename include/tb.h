@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TB_ABI_VERSION 3
+#define TB_ABI_VERSION 4
 #define TB_BLOCK 128
 #define TB_MAX_ROWS 8
 #define TB_MAX_BATCH_ROWS 32
@@ -74,7 +74,14 @@ enum tb_format {
     TB_FMT_TERNARY2 = 0,
     /* 1-bit signs. Weight i is bit i&7 of byte i>>3; 1 -> +1, 0 -> -1.
      * codes: uint8[n][nb][16]. */
-    TB_FMT_SIGN1 = 1
+    TB_FMT_SIGN1 = 1,
+    /* The same signs, rows interleaved by four for the lookup-table GEMV
+     * (bonsai-edge-serve README, kernels/ section: a 1-bit lookup-table kernel
+     * needs a row-interleaved layout). n % 4 == 0. codes: uint32[n/4][nb][16],
+     * byte r of word j = byte j of row 4*(quad)+r's block; scales:
+     * uint16[n/4][nb][4]. Made by tb_sign_interleave; taken by tb_gemv_ternary
+     * and tb_gemv_block_sums (and their _batch forms) for m <= 2 only. */
+    TB_FMT_SIGN1_RI4 = 2
 };
 
 /* One weight matrix with n output rows and k inputs.
@@ -183,6 +190,17 @@ int tb_gemv_ternary_x(const tb_matrix *w, const float *x, int m, int8_t *qx, flo
  *   isum int32 [m][w->n][w->k/128] output; m * n * (k/128) * 4 must be below
  *   2 GiB (else TB_EUNSUPPORTED). */
 int tb_gemv_block_sums(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream);
+
+/* Row-interleave a TB_FMT_SIGN1 matrix (n % 4 == 0) into TB_FMT_SIGN1_RI4:
+ * codes_ri receives n*k/8 bytes, scales_ri n*(k/128) fp16 values, both
+ * caller-owned device buffers, 16-byte aligned, overlapping nothing. The
+ * interleaved matrix is {codes_ri, scales_ri, n, k, TB_FMT_SIGN1_RI4}. With
+ * it tb_gemv_ternary runs a lookup-table kernel (v_perm_b32 looks up the
+ * sums of a pair of activations for four rows at once) whose y is
+ * bit-identical to the bit-mask kernel on the original matrix; m > 2 returns
+ * TB_EUNSUPPORTED (the tables of one row take 32 registers per lane), and
+ * the gate/up, down and fused calls return TB_EUNSUPPORTED for this layout. */
+int tb_sign_interleave(const tb_matrix *w, void *codes_ri, uint16_t *scales_ri, void *stream);
 
 /* ---- Batches above 8 rows ------------------------------------------------
  * The same five operations for 1 <= m <= TB_MAX_BATCH_ROWS (32) rows: for

@@ -18,11 +18,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libtb.so")
 
 TB_OK, TB_EINVAL, TB_EALIGN, TB_EUNSUPPORTED, TB_EHIP, TB_ESCRATCH = 0, -1, -2, -3, -4, -5
-TB_FMT_TERNARY2, TB_FMT_SIGN1 = 0, 1
+TB_FMT_TERNARY2, TB_FMT_SIGN1, TB_FMT_SIGN1_RI4 = 0, 1, 2
 BLOCK = 128
 MAX_ROWS = 8
 MAX_BATCH_ROWS = 32
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # every symbol include/tb.h declares
 ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_gemv_ternary_x", "tb_ffn_gateup_silu",
@@ -30,7 +30,7 @@ ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_gemv_ternary_x", "tb
                "tb_ffn_down",
                "tb_gemv_block_sums", "tb_rotate_quant_i8_batch", "tb_gemv_ternary_batch",
                "tb_ffn_gateup_silu_batch", "tb_ffn_down_batch", "tb_gemv_block_sums_batch",
-               "tb_ffn_down_noalloc",
+               "tb_ffn_down_noalloc", "tb_sign_interleave",
                "tb_ffn_workspace_bytes", "tb_ffn_workspace_init",
                "tb_ffn_layers", "tb_ffn_workspace_error", "tb_status_str", "tb_abi_version")
 TB_FFN_CHAIN = 1
@@ -68,6 +68,7 @@ _SIGS = {
     "tb_ffn_down_batch": ([_MP, _P, _I, _P, _P, _P, _P], _I),
     "tb_gemv_block_sums_batch": ([_MP, _P, _I, _P, _P], _I),
     "tb_ffn_down_noalloc": ([_MP, _P, _I, _P, _P], _I),
+    "tb_sign_interleave": ([_MP, _P, _P, _P], _I),
     "tb_ffn_workspace_bytes": ([_I, _I, _I], ctypes.c_size_t),
     "tb_ffn_workspace_init": ([_P, ctypes.c_size_t, ctypes.c_uint32, _P], _I),
     "tb_ffn_layers": ([ctypes.POINTER(CFfnWeights), _I, _P, _I, ctypes.c_uint, _P, ctypes.c_size_t,
@@ -220,6 +221,17 @@ def tb_gemv_block_sums_batch(w: Matrix, q, isum, stream=None) -> None:
     """tb_gemv_block_sums for up to 32 rows."""
     _call("tb_gemv_block_sums_batch", ctypes.byref(w.c), q.data_ptr(), _rows(q), isum.data_ptr(),
           _stream(stream))
+
+
+def tb_sign_interleave(w: Matrix, stream=None) -> Matrix:
+    """The TB_FMT_SIGN1_RI4 copy of a sign matrix (rows interleaved by four), in new device
+    tensors, for the lookup-table GEMV."""
+    import torch
+    codes = torch.empty_like(w.codes)
+    scales = torch.empty_like(w.scales)
+    _call("tb_sign_interleave", ctypes.byref(w.c), codes.data_ptr(), scales.data_ptr(),
+          _stream(stream))
+    return Matrix(codes, scales, w.n, w.k, TB_FMT_SIGN1_RI4)
 
 
 def tb_ffn_down_noalloc(wd: Matrix, h, y, stream=None) -> None:

@@ -41,6 +41,7 @@
 #include "tb.h"
 #include "tb_device.h"
 #include "tb_layers.h"
+#include "tb_lut.h"
 
 // Device scratch of tb_ffn_down_noalloc: rotquant(h) and its block scales, for callers that
 // cannot allocate. Each GPU holds its own copy until the process ends. Host code never uses
@@ -1429,7 +1430,9 @@ int check_matrix(const tb_matrix *w)
         return TB_EINVAL;
     if (w->n < 1 || w->k < kBlock || w->k % kBlock)
         return TB_EINVAL;
-    if (w->fmt != TB_FMT_TERNARY2 && w->fmt != TB_FMT_SIGN1)
+    if (w->fmt != TB_FMT_TERNARY2 && w->fmt != TB_FMT_SIGN1 && w->fmt != TB_FMT_SIGN1_RI4)
+        return TB_EINVAL;
+    if (w->fmt == TB_FMT_SIGN1_RI4 && w->n % 4)
         return TB_EINVAL;
     if (!aligned16(w->codes) || !aligned16(w->scales))
         return TB_EALIGN;
@@ -1725,6 +1728,42 @@ int launch_gemv_rotx(int mode, const tb_matrix *w0, const tb_matrix *w1, const f
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
+// The lookup-table GEMV (block sums when isum is given) over row-interleaved sign weights,
+// for 1 <= m <= 2 rows; one 16-wave workgroup per CU.
+int launch_lut(const tb_matrix *w, const int8_t *q, const float *dq, int m, float *y,
+               int32_t *isum, hipStream_t stream)
+{
+    if (m > tblut::kMaxRows)
+        return TB_EUNSUPPORTED;
+    DeviceInfo info;
+    int rc = device_info(&info);
+    if (rc)
+        return rc;
+    const int T = w->n / 4, nb = w->k / kBlock, I = (nb + 15) / 16;
+    const int grid = T < info.cus ? T : info.cus;
+    const size_t lds = (size_t)((T + grid - 1) / grid) * I * 4 * m * 4;
+    if (lds > (size_t)info.lds_limit)
+        return TB_EUNSUPPORTED;
+    tblut::LutArgs a = {};
+    a.codes = static_cast<const uint8_t *>(w->codes);
+    a.scales = w->scales;
+    a.n = w->n;
+    a.k = w->k;
+    a.q = q;
+    a.dq = dq;
+    a.out = y;
+    a.isum = isum;
+    a.codes_bytes = (uint32_t)codes_bytes(w);
+    a.scales_bytes = (uint32_t)scales_bytes(w);
+    using LutFn = void (*)(tblut::LutArgs);
+    LutFn fn = isum ? (m == 1 ? tblut::gemv_lut_kernel<1, true> : tblut::gemv_lut_kernel<2, true>)
+                    : (m == 1 ? tblut::gemv_lut_kernel<1, false> : tblut::gemv_lut_kernel<2, false>);
+    if ((rc = raise_lds(reinterpret_cast<const void *>(fn), lds)))
+        return rc;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(tblut::kThreads), lds, stream, a);
+    return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+}
+
 // A batch of m (1..32) independent rows as balanced chunks: chunks of up to 16 rows on
 // gemv_mfma_kernel (all 16 B columns live) where they fit the device's LDS, else of up to 8
 // rows on the kernels of the 1..8-row calls. Every kernel folds a row the same way, so a
@@ -1805,6 +1844,8 @@ int check_ffn_shapes(const tb_ffn_weights *L, int n, int *hidden, int *inter, in
             (rc = check_matrix(&L[i].down)))
             return rc;
         const int H = L[i].gate.k, N = L[i].gate.n, F = L[i].gate.fmt;
+        if (F == TB_FMT_SIGN1_RI4)
+            return TB_EUNSUPPORTED;
         if (L[i].up.k != H || L[i].up.n != N || L[i].down.k != N || L[i].down.n != H ||
             L[i].up.fmt != F || L[i].down.fmt != F || N % kBlock)
             return TB_EINVAL;
@@ -1880,6 +1921,8 @@ static int gemv_impl(const tb_matrix *w, const int8_t *q, const float *dq, int m
         overlaps(ry, range_of(q, (size_t)m * w->k)) ||
         overlaps(ry, range_of(dq, (size_t)m * (w->k / kBlock) * 4)))
         return TB_EINVAL;
+    if (w->fmt == TB_FMT_SIGN1_RI4)
+        return launch_lut(w, q, dq, m, y, nullptr, static_cast<hipStream_t>(stream));
     return (batch ? launch_gemv_batch : launch_gemv)(kModeY, w, nullptr, q, dq, m, y, nullptr,
                                                      static_cast<hipStream_t>(stream));
 }
@@ -1906,6 +1949,8 @@ static int gateup_impl(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q
         return rc;
     if (wg->n != wu->n || wg->k != wu->k || wg->fmt != wu->fmt)
         return TB_EINVAL;
+    if (wg->fmt == TB_FMT_SIGN1_RI4)
+        return TB_EUNSUPPORTED;
     if (check_rows(m, batch ? TB_MAX_BATCH_ROWS : TB_MAX_ROWS) || !h || !q || !dq)
         return TB_EINVAL;
     if (!aligned16(q) || !aligned16(dq) || !aligned16(h))
@@ -1944,6 +1989,8 @@ int tb_ffn_gateup_silu_x(const tb_matrix *wg, const tb_matrix *wu, const float *
         return rc;
     if (wg->n != wu->n || wg->k != wu->k || wg->fmt != wu->fmt)
         return TB_EINVAL;
+    if (wg->fmt == TB_FMT_SIGN1_RI4)
+        return TB_EUNSUPPORTED;
     if (check_rows(m, TB_MAX_ROWS) || !x || !qx || !dqx || !h)
         return TB_EINVAL;
     if (!aligned16(x) || !aligned16(qx) || !aligned16(dqx) || !aligned16(h))
@@ -1978,6 +2025,8 @@ static int down_impl(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, 
         return rc;
     if (check_rows(m, batch ? TB_MAX_BATCH_ROWS : TB_MAX_ROWS) || !h || !qh_ws || !dqh_ws || !y)
         return TB_EINVAL;
+    if (wd->fmt == TB_FMT_SIGN1_RI4)
+        return TB_EUNSUPPORTED;
     if (!aligned16(h) || !aligned16(qh_ws) || !aligned16(dqh_ws) || !aligned16(y))
         return TB_EALIGN;
     const int k = wd->k;
@@ -2029,6 +2078,8 @@ int tb_ffn_down_noalloc(const tb_matrix *wd, const float *h, int m, float *y, vo
     int rc = check_matrix(wd);
     if (rc)
         return rc;
+    if (wd->fmt == TB_FMT_SIGN1_RI4)
+        return TB_EUNSUPPORTED;
     if (check_rows(m) || !h || !y)
         return TB_EINVAL;
     if (!aligned16(h) || !aligned16(y))
@@ -2071,6 +2122,8 @@ static int block_sums_impl(const tb_matrix *w, const int8_t *q, int m, int32_t *
         overlaps(ri, range_of(w->scales, scales_bytes(w))) ||
         overlaps(ri, range_of(q, (size_t)m * w->k)))
         return TB_EINVAL;
+    if (w->fmt == TB_FMT_SIGN1_RI4)
+        return launch_lut(w, q, nullptr, m, nullptr, isum, static_cast<hipStream_t>(stream));
     return (batch ? launch_gemv_batch : launch_gemv)(kModeIsum, w, nullptr, q, nullptr, m, nullptr,
                                                      isum, static_cast<hipStream_t>(stream));
 }
@@ -2084,6 +2137,30 @@ int tb_gemv_block_sums_batch(const tb_matrix *w, const int8_t *q, int m, int32_t
                              void *stream)
 {
     return block_sums_impl(w, q, m, isum, stream, true);
+}
+
+int tb_sign_interleave(const tb_matrix *w, void *codes_ri, uint16_t *scales_ri, void *stream)
+{
+    int rc = check_matrix(w);
+    if (rc)
+        return rc;
+    if (w->fmt != TB_FMT_SIGN1 || w->n % 4 || !codes_ri || !scales_ri)
+        return TB_EINVAL;
+    if (!aligned16(codes_ri) || !aligned16(scales_ri))
+        return TB_EALIGN;
+    const Range rco = range_of(codes_ri, codes_bytes(w)), rso = range_of(scales_ri, scales_bytes(w));
+    if (overlaps(rco, rso) || overlaps(rco, range_of(w->codes, codes_bytes(w))) ||
+        overlaps(rco, range_of(w->scales, scales_bytes(w))) ||
+        overlaps(rso, range_of(w->codes, codes_bytes(w))) ||
+        overlaps(rso, range_of(w->scales, scales_bytes(w))))
+        return TB_EINVAL;
+    const int nb = w->k / kBlock;
+    const size_t words = (size_t)(w->n / 4) * nb * 16;
+    const int grid = (int)std::min<size_t>((words + 255) / 256, 65536);
+    hipLaunchKernelGGL(tblut::sign_interleave_kernel, dim3(grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint8_t *>(w->codes),
+                       w->scales, w->n, nb, static_cast<uint32_t *>(codes_ri), scales_ri);
+    return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
 

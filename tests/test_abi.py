@@ -74,7 +74,7 @@ def test_gemv_validation(L):
     assert g(mat(k=500)) == tb.TB_EINVAL
     assert g(mat(k=0)) == tb.TB_EINVAL
     assert g(mat(n=0)) == tb.TB_EINVAL
-    assert g(mat(fmt=2)) == tb.TB_EINVAL
+    assert g(mat(fmt=3)) == tb.TB_EINVAL
     assert g(mat(codes=0)) == tb.TB_EINVAL
     assert g(mat(codes=ALIGNED + 2)) == tb.TB_EALIGN
     assert g(mat(), q=0) == tb.TB_EINVAL
@@ -130,6 +130,36 @@ def test_gemv_x_validation(L):
     assert gx(x=0x20000004) == tb.TB_EALIGN
     assert gx(qx=0x20000000) == tb.TB_EINVAL                 # qx overlaps x
     assert gx(y=0x30000000) == tb.TB_EINVAL                  # y overlaps qx
+
+
+def test_sign_interleave_validation(L):
+    # tb_sign_interleave(w, codes_ri, scales_ri): a sign matrix with n % 4 == 0, aligned,
+    # non-overlapping outputs
+    def si(w, co=0x20000000, so=0x30000000):
+        return L.tb_sign_interleave(ctypes.byref(w), co, so, None)
+    assert si(mat(fmt=0)) == tb.TB_EINVAL                    # ternary
+    assert si(mat(fmt=1, n=254)) == tb.TB_EINVAL             # n % 4
+    assert si(mat(fmt=1), co=0) == tb.TB_EINVAL
+    assert si(mat(fmt=1), co=0x20000004) == tb.TB_EALIGN
+    assert si(mat(fmt=1), so=0x20000000) == tb.TB_EINVAL     # outputs overlap
+    assert si(mat(fmt=1), co=ALIGNED) == tb.TB_EINVAL        # overwrites the codes
+    assert si(mat(fmt=3)) == tb.TB_EINVAL                    # unknown format
+
+
+def test_row_interleaved_layout_only_for_the_gemv(L):
+    # the interleaved layout (fmt 2, n % 4 == 0) is checked like the others and refused by
+    # the calls other than the GEMV and the block sums
+    ri = mat(fmt=2)
+    assert L.tb_gemv_ternary(ctypes.byref(mat(fmt=2, n=254)), ALIGNED3, ALIGNED4, 1,
+                             0x20000000, None) == tb.TB_EINVAL
+    h = 0x20000000
+    assert L.tb_ffn_gateup_silu(ctypes.byref(ri), ctypes.byref(mat(fmt=2, codes=0x10000000,
+                                scales=0x14000000)), ALIGNED3, ALIGNED4, 1, h,
+                                None) == tb.TB_EUNSUPPORTED
+    assert L.tb_ffn_down(ctypes.byref(mat(fmt=2, n=64, k=256)), 0x20000000, 1, 0x30000000,
+                         0x34000000, 0x38000000, None) == tb.TB_EUNSUPPORTED
+    assert L.tb_ffn_down_noalloc(ctypes.byref(mat(fmt=2, n=64, k=256)), 0x20000000, 1,
+                                 0x38000000, None) == tb.TB_EUNSUPPORTED
 
 
 def test_down_validation(L):

@@ -136,6 +136,57 @@ def test_fused_full_size_layers(o, fmt, m):
     check_first_layer_vs_oracle(o, hl[0], xs[0], y[0])
 
 
+# Shapes whose steps are whole (hidden and intermediate multiples of 1024 for ternary, 2048
+# for sign), with shares of 1 to 8 row tiles per CU, at one and two rows.
+WHOLE_STEP_CASES = [
+    # (hidden, inter, layers, fmt, m)
+    (1024, 2048, 3, TERN, 1),
+    (2048, 8192, 3, TERN, 2),
+    (1024, 3072, 4, TERN, 2),
+    (2048, 4096, 3, SIGN, 1),
+    (2048, 4096, 3, SIGN, 2),
+]
+
+
+@pytest.mark.parametrize("hidden,inter,count,fmt,m", WHOLE_STEP_CASES)
+@pytest.mark.parametrize("chain", [False, True])
+def test_fused_whole_step_shapes(o, hidden, inter, count, fmt, m, chain):
+    say(f"fused {hidden}x{inter} layers={count} fmt={fmt} m={m} chain={chain}")
+    hl, dl = make_layers(90 + fmt, count, hidden, inter, fmt)
+    if chain:
+        x = synth.normal_rows(m, hidden, 90 + fmt, 0)
+    else:
+        x = np.stack([synth.normal_rows(m, hidden, 90 + fmt, l) for l in range(count)])
+    y = fused(dl, x, m, workspace(m, hidden, inter), chain=chain)
+    ref = separate(dl, x, m, chain=chain)
+    assert y.tobytes() == ref.tobytes()
+    check_first_layer_vs_oracle(o, hl[0], x if chain else x[0], y[0])
+
+
+def test_fused_one_row_more_than_32_layers_and_replay():
+    say("fused: one row, 34 layers (two launches), then graph replays")
+    _, dl = make_layers(95, 34, 1024, 2048, TERN)
+    xs = np.stack([synth.normal_rows(1, 1024, 95, l) for l in range(34)])
+    ws = workspace(1, 1024, 2048)
+    ref = separate(dl, xs, 1)
+    assert fused(dl, xs, 1, ws).tobytes() == ref.tobytes()
+    arr = tb.FfnLayers([(g.gate, g.up, g.down) for g in dl])
+    xd = gu.dev(xs)
+    y = gu.f32_out(34, 1, 1024)
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(graph, stream=cs):
+            tb.tb_ffn_layers(arr, xd, ws, y, stream=cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    for rep in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        assert gu.host(y).tobytes() == ref.tobytes(), rep
+
+
 def test_fused_rows_bit_identical_to_row_alone():
     say("fused: M=8 rows vs each row alone")
     _, dl = make_layers(40, 2, 640, 2176, TERN)
