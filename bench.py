@@ -71,8 +71,8 @@ def parse():
                    help="no all-cores oracle pass (and oracle parity check) at M=8")
     p.add_argument("--profile-only", action="store_true",
                    help="one eager pass of each path and exit (for rocprofv3 counter runs)")
-    p.add_argument("--profile-m", type=int, default=1,
-                   help="rows of the --profile-only pass (1..8)")
+    p.add_argument("--profile-m", default="1,8",
+                   help="rows of the --profile-only passes, comma-separated (each 1..8)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -430,6 +430,54 @@ def cpu_all_cores(layers_host, xs, m: int, threads: int, which=None):
     return res, time.perf_counter() - t0
 
 
+def lut_comparison(torch, tb, synth, sdev, layers: int):
+    """The lookup-table GEMV (row-interleaved sign weights) against the bit-mask kernel on
+    the same matrices: the gate and down projections of the first `layers` sign layers,
+    each call kind captured back to back in a graph and timed with events, at one and
+    two rows. Checks that both produce the same y bytes. Returns the report dict."""
+    out = {"layers": layers, "note": "graph replay of back-to-back calls, us per call; "
+           "tb_gemv_ternary on TB_FMT_SIGN1 (bit-mask decode) and on TB_FMT_SIGN1_RI4 "
+           "(lookup tables through v_perm_b32)"}
+    same = True
+    for label, pick in (("gate_17408x5120", 0), ("down_5120x17408", 2)):
+        ws = [sdev[l][pick] for l in range(layers)]
+        ri = [tb.tb_sign_interleave(w) for w in ws]
+        k, n = ws[0].k, ws[0].n
+        for m in (1, 2):
+            x = torch.from_numpy(synth.student_t_rows(m, k, SEED + 300, pick)).cuda()
+            q = torch.empty(m, k, dtype=torch.int8, device="cuda")
+            dq = torch.empty(m, k // 128, dtype=torch.float32, device="cuda")
+            tb.tb_rotate_quant_i8(x, q, dq)
+            row = {}
+            ys = {}
+            for name, mats in (("bitmask", ws), ("lut", ri)):
+                y = torch.empty(layers, m, n, device="cuda")
+                for l, w in enumerate(mats):
+                    tb.tb_gemv_ternary(w, q, dq, y[l])
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for l, w in enumerate(mats):
+                        tb.tb_gemv_ternary(w, q, dq, y[l])
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / 10 / layers * 1e3
+                row[name + "_us"] = round(us, 3)
+                row[name + "_gbs"] = round(ws[0].nbytes / us / 1e3, 1)
+                ys[name] = y.cpu().numpy().tobytes()
+                del g
+            same = same and ys["bitmask"] == ys["lut"]
+            out[f"{label}_m{m}"] = row
+        del ri
+    return out, same
+
+
 def oracle_parity(layers_host, res, got, threads: int):
     """Every layer of a timed step against the oracle, stagewise (the bars of the tests):
       q, dq                  bit-exact against the oracle's rotquant(x);
@@ -557,13 +605,15 @@ def main():
     torch.cuda.synchronize()
 
     if args.profile_only:
-        fp = Fused64(tb, dev_layers, xs, args.profile_m, torch)
-        sp = Stream64(tb, dev_layers, xs, args.profile_m, torch)
-        fp.step()
-        sp.step()
-        torch.cuda.synchronize()
-        fp.check()
-        log(f"profile pass done at M={args.profile_m} (one fused step, one pass of separate calls)")
+        for pm in (int(v) for v in args.profile_m.split(",")):
+            fp = Fused64(tb, dev_layers, xs, pm, torch)
+            sp = Stream64(tb, dev_layers, xs, pm, torch)
+            fp.step()
+            sp.step()
+            torch.cuda.synchronize()
+            fp.check()
+            del fp, sp
+            log(f"profile pass done at M={pm} (one fused step, one pass of separate calls)")
         return
     f1 = Fused64(tb, dev_layers, xs, 1, torch)
     s1 = Stream64(tb, dev_layers, xs, 1, torch)
@@ -738,6 +788,11 @@ def main():
             res_sign[f"m{m}"] = row
             log(f"sign M={m}: fused {tfs / args.layers * 1e6:.2f}, separate "
                 f"{tss / args.layers * 1e6:.2f} us/layer")
+        res_sign["lookup_table_gemv"], lut_same = lut_comparison(torch, tb, synth, sdev, 16)
+        parity["sign_lut_equals_bitmask"] = bool(lut_same)
+        log("sign GEMV, bit-mask vs lookup table (us/call): " + ", ".join(
+            f"{k} {v['bitmask_us']}/{v['lut_us']}" for k, v in res_sign["lookup_table_gemv"].items()
+            if isinstance(v, dict)) + f"; same bytes: {lut_same}")
         del sdev, sl
         torch.cuda.empty_cache()
 

@@ -4,7 +4,7 @@
 
 --stats: the directory of a `rocprofv3 --kernel-trace --stats --output-format csv -o bench`
 run of bench.py; --pmc: the parent directory of the four counter runs pmc_FETCH_SIZE,
-pmc_WRITE_SIZE (bench.py --profile-only) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE
+pmc_WRITE_SIZE (bench.py --profile-only: one pass of each path at M=1 and at M=8) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE
 (bench.py --copy-probe-mib 1024); --bench: bench.py's stdout (the JSON line) from the same
 box. Writes ffn64_stream_kernel_stats.md, ffn64_stream_traffic.md and
 ffn64_stream_traffic.json. The traffic file carries a sha256 of the kernel sources, and
@@ -52,6 +52,10 @@ ALGORITHMIC = {
     "gemv_ring_kernel<1, 0, 1>": 2 * MATRIX_BYTES + HIDDEN + NB_H * 4 + INTER * 4,
     "gemv_ring_kernel<1, 0, 0>": MATRIX_BYTES + INTER + NB_N * 4 + HIDDEN * 4,
     "ffn_layers_kernel<1, 0>": 32 * (3 * MATRIX_BYTES + 2 * HIDDEN * 4),
+    # M=8: matrix-core kernels with two blocks per MFMA
+    "gemv_mfma_pack_kernel<8, 0, 1>": 2 * MATRIX_BYTES + 8 * (HIDDEN + NB_H * 4 + INTER * 4),
+    "gemv_mfma_pack_kernel<8, 0, 0>": MATRIX_BYTES + 8 * (INTER + NB_N * 4 + HIDDEN * 4),
+    "ffn_layers_kernel<8, 0>": 32 * (3 * MATRIX_BYTES + 8 * 2 * HIDDEN * 4),
 }
 WHAT = {
     "gemv_ring_kernel<1, 0, 1, true>": "tb_ffn_gateup_silu_x at M=1 (gate and up, 47,349,760 weight "
@@ -59,6 +63,9 @@ WHAT = {
     "gemv_ring_kernel<1, 0, 1>": "tb_ffn_gateup_silu at M=1 (gate and up, 47,349,760 weight bytes)",
     "gemv_ring_kernel<1, 0, 0>": "the GEMV of tb_ffn_down at M=1 (23,674,880 weight bytes)",
     "ffn_layers_kernel<1, 0>": "one tb_ffn_layers launch of 32 layers at M=1",
+    "gemv_mfma_pack_kernel<8, 0, 1>": "tb_ffn_gateup_silu at M=8 (matrix cores)",
+    "gemv_mfma_pack_kernel<8, 0, 0>": "the GEMV of tb_ffn_down at M=8 (matrix cores)",
+    "ffn_layers_kernel<8, 0>": "one tb_ffn_layers launch of 32 layers at M=8",
 }
 
 
@@ -176,7 +183,7 @@ def main():
     stats = read_stats(a.stats)
 
     cmd_stats = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-                 "-d <out>/prof -o bench -- python3 /root/repo/bench.py")
+                 "-d <out>/prof -o bench -- python3 /root/repo/bench.py --steps 5 --warmup 2")
     lines = ["# FFN 64-layer weight stream (hidden 5120, intermediate 17408): kernel statistics",
              "", "Command (on the GPU box; /root/repo is the repository):", "", "```", cmd_stats, "```",
              "", "Kernel statistics (all dispatches of the run: both paths, M=1 and M=8, ternary and sign):",
@@ -258,7 +265,7 @@ def main():
                     "python3 /root/repo/bench.py --profile-only")
         cmds.append(f"rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_copy_{c} -o run -- "
                     "python3 /root/repo/bench.py --copy-probe-mib 1024")
-    md = ["# HBM traffic per launch: 64-layer FFN stream at M=1 (hidden 5120, intermediate 17408)", "",
+    md = ["# HBM traffic per launch: 64-layer FFN stream at M=1 and M=8 (hidden 5120, intermediate 17408)", "",
           "Commands (on the GPU box, from /tmp with TMPDIR=/tmp; one counter per run; the copy runs "
           "calibrate the counters):", "", "```", *cmds, "```", "",
           f"Calibration: a device copy of 1 GiB (reads 1 GiB, writes 1 GiB) reads FETCH_SIZE x{ff:.4f} "
