@@ -5,8 +5,8 @@
 --stats: the directory of a `rocprofv3 --kernel-trace --stats --output-format csv -o bench`
 run of bench.py; --pmc: the parent directory of the four counter runs pmc_FETCH_SIZE,
 pmc_WRITE_SIZE (bench.py --profile-only: one pass of each path at M=1 and at M=8) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE
-(bench.py --copy-probe-mib 1024); --bench: bench.py's stdout (the JSON line) from the same
-box. Writes ffn64_stream_kernel_stats.md, ffn64_stream_traffic.md and
+(bench.py --copy-probe-mib 1024); --bench: the JSON line of an untraced bench.py run of
+the same code. Writes ffn64_stream_kernel_stats.md, ffn64_stream_traffic.md and
 ffn64_stream_traffic.json. The traffic file carries a sha256 of the kernel sources, and
 bench.py reports the traffic figure only while the sources still hash to it.
 """
@@ -23,7 +23,7 @@ import re
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = ["ternary_weight_int8_tb_amd/csrc/tb.hip", "ternary_weight_int8_tb_amd/csrc/tb_device.h",
-           "ternary_weight_int8_tb_amd/csrc/tb_layers.h"]
+           "ternary_weight_int8_tb_amd/csrc/tb_layers.h", "ternary_weight_int8_tb_amd/csrc/tb_lut.h"]
 COPY_BYTES = 1 << 30
 
 HIDDEN, INTER, LAYERS = 5120, 17408, 64
@@ -49,8 +49,8 @@ def short_name(name: str) -> str:
 ALGORITHMIC = {
     # gate/up with the rotation of x inside: x read, its int8 copy and scales written
     "gemv_ring_kernel<1, 0, 1, true>": 2 * MATRIX_BYTES + HIDDEN * 4 + HIDDEN + NB_H * 4 + INTER * 4,
-    "gemv_ring_kernel<1, 0, 1>": 2 * MATRIX_BYTES + HIDDEN + NB_H * 4 + INTER * 4,
-    "gemv_ring_kernel<1, 0, 0>": MATRIX_BYTES + INTER + NB_N * 4 + HIDDEN * 4,
+    "gemv_ring_kernel<1, 0, 1, false>": 2 * MATRIX_BYTES + HIDDEN + NB_H * 4 + INTER * 4,
+    "gemv_ring_kernel<1, 0, 0, false>": MATRIX_BYTES + INTER + NB_N * 4 + HIDDEN * 4,
     "ffn_layers_kernel<1, 0>": 32 * (3 * MATRIX_BYTES + 2 * HIDDEN * 4),
     # M=8: matrix-core kernels with two blocks per MFMA
     "gemv_mfma_pack_kernel<8, 0, 1>": 2 * MATRIX_BYTES + 8 * (HIDDEN + NB_H * 4 + INTER * 4),
@@ -60,8 +60,8 @@ ALGORITHMIC = {
 WHAT = {
     "gemv_ring_kernel<1, 0, 1, true>": "tb_ffn_gateup_silu_x at M=1 (gate and up, 47,349,760 weight "
                                        "bytes, the rotation of x inside)",
-    "gemv_ring_kernel<1, 0, 1>": "tb_ffn_gateup_silu at M=1 (gate and up, 47,349,760 weight bytes)",
-    "gemv_ring_kernel<1, 0, 0>": "the GEMV of tb_ffn_down at M=1 (23,674,880 weight bytes)",
+    "gemv_ring_kernel<1, 0, 1, false>": "tb_ffn_gateup_silu at M=1 (gate and up, 47,349,760 weight bytes)",
+    "gemv_ring_kernel<1, 0, 0, false>": "the GEMV of tb_ffn_down at M=1 (23,674,880 weight bytes)",
     "ffn_layers_kernel<1, 0>": "one tb_ffn_layers launch of 32 layers at M=1",
     "gemv_mfma_pack_kernel<8, 0, 1>": "tb_ffn_gateup_silu at M=8 (matrix cores)",
     "gemv_mfma_pack_kernel<8, 0, 0>": "the GEMV of tb_ffn_down at M=8 (matrix cores)",
@@ -89,13 +89,13 @@ SIGN_MATRIX_BYTES = INTER * HIDDEN // 8 + INTER * NB_H * 2
 # down call is rotquant(h) + GEMV; at M=8 both calls are rotquant + GEMV
 STREAMS = {
     "ternary M=1": [("gemv_ring_kernel<1, 0, 1, true>", 2 * MATRIX_BYTES), ("rotquant_kernel", 0),
-                    ("gemv_ring_kernel<1, 0, 0>", MATRIX_BYTES)],
+                    ("gemv_ring_kernel<1, 0, 0, false>", MATRIX_BYTES)],
     "ternary M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 0, 1>", 2 * MATRIX_BYTES),
                     ("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 0, 0>", MATRIX_BYTES)],
     "sign M=1": [("gemv_ring_kernel<1, 1, 1, true>", 2 * SIGN_MATRIX_BYTES), ("rotquant_kernel", 0),
-                 ("gemv_ring_kernel<1, 1, 0>", SIGN_MATRIX_BYTES)],
+                 ("gemv_ring_kernel<1, 1, 0, false>", SIGN_MATRIX_BYTES)],
     "sign M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 1, 1>", 2 * SIGN_MATRIX_BYTES),
-                 ("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 1, 0>", SIGN_MATRIX_BYTES)],
+                 ("rotquant_kernel", 0), ("gemv_mfma_kernel<8, 1, 0>", SIGN_MATRIX_BYTES)],
 }
 
 
@@ -204,7 +204,8 @@ def main():
         keep = {k: bench.get(k) for k in ("value", "unit", "ms_per_step", "us_per_layer", "pct_hbm_peak",
                                            "read_probe_gbs")}
         keep["entry_point"] = bench.get("config", {}).get("entry_point")
-        lines += ["", "Bench line of a run on the same box (headline fields and roofline):", "", "```",
+        lines += ["", "Bench line of an untraced run of the same code (bench.py without the profiler; "
+                  "headline fields and roofline):", "", "```",
                   json.dumps(keep), json.dumps(bench.get("roofline")), "```"]
     passes = stream_passes(a.stats)
     if passes:
@@ -227,7 +228,7 @@ def main():
         for label, r in passes.items():
             lines.append(f"| {label} | {r['span_us']:.2f} | {r['busy_us']:.2f} |")
     if bench and bench.get("m1_call_breakdown"):
-        lines += ["", "Untraced per-call device time at M=1 from the same bench run (HIP events around "
+        lines += ["", "Untraced per-call device time at M=1 from that bench run (HIP events around "
                   "graph replays of 64 back-to-back calls of one kind):", "", "```",
                   json.dumps(bench["m1_call_breakdown"]), "```"]
     os.makedirs(a.out, exist_ok=True)
