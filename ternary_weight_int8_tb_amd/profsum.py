@@ -1,13 +1,16 @@
 """Summaries of rocprofv3 output for profiles/: kernel statistics and calibrated HBM traffic.
 
     python -m ternary_weight_int8_tb_amd.profsum --stats DIR --pmc DIR --bench FILE --out profiles
+    python -m ternary_weight_int8_tb_amd.profsum --sq DIR --out profiles
 
 --stats: the directory of a `rocprofv3 --kernel-trace --stats --output-format csv -o bench`
 run of bench.py; --pmc: the parent directory of the four counter runs pmc_FETCH_SIZE,
 pmc_WRITE_SIZE (bench.py --profile-only: one pass of each path at M=1 and at M=8) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE
 (bench.py --copy-probe-mib 1024); --bench: the JSON line of an untraced bench.py run of
 the same code. Writes ffn64_stream_kernel_stats.md, ffn64_stream_traffic.md and
-ffn64_stream_traffic.json. The traffic file carries a sha256 of the kernel sources, and
+ffn64_stream_traffic.json. --sq: the parent directory of two SQ counter runs (pmc_sq_a,
+pmc_sq_b; the counter sets are in SQ_SETS) over the same profile pass; writes
+ffn64_stream_sq_counters.md. The traffic file carries a sha256 of the kernel sources, and
 bench.py reports the traffic figure only while the sources still hash to it.
 """
 
@@ -166,13 +169,91 @@ def copy_factor(d: str, counter: str, true_bytes: int) -> float:
     return best[0] * 1024 / true_bytes
 
 
+SQ_SETS = {
+    "a": "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_SALU "
+         "SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "b": "SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT "
+         "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_ANY SQ_WAIT_ANY GRBM_GUI_ACTIVE",
+}
+CUS = 256
+
+
+def read_all_counters(d: str):
+    """Per kernel (short name): {counter: mean over dispatches}, and the dispatch count."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            key = (short_name(r["Kernel_Name"]), r["Dispatch_Id"])
+            d_ = per.setdefault(key, {})
+            d_[r["Counter_Name"]] = d_.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg = {}
+    for (k, _), cs in per.items():
+        e = agg.setdefault(k, {"n": 0, "sum": {}})
+        e["n"] += 1
+        for c, v in cs.items():
+            e["sum"][c] = e["sum"].get(c, 0.0) + v
+    return {k: ({c: v / e["n"] for c, v in e["sum"].items()}, e["n"]) for k, e in agg.items()}
+
+
+def write_sq(sq_dir: str, out: str):
+    """SQ counters of the M=1 and M=8 kernels: instruction mix per wave and where wave time
+    goes (waiting on memory counters, waiting to issue, issuing VALU)."""
+    a = read_all_counters(os.path.join(sq_dir, "pmc_sq_a"))
+    b = read_all_counters(os.path.join(sq_dir, "pmc_sq_b"))
+    keep = [k for k in a if k in b and ("gemv" in k or "ffn_layers" in k)]
+    lines = ["# FFN 64-layer stream: SQ counters of the M=1 and M=8 kernels", "",
+             "Commands (on the GPU box, from /tmp with TMPDIR=/tmp; one counter set per run):", "", "```"]
+    for name, cs in SQ_SETS.items():
+        lines.append(f"rocprofv3 --pmc {cs} --output-format csv -d <out>/pmc_sq_{name} -o run -- "
+                     "python3 /root/repo/bench.py --profile-only")
+    lines += ["```", "",
+              "Means per dispatch over every dispatch of the kernel in one pass of each path at M=1 "
+              "and M=8 (bench.py --profile-only). Instruction counts are wave instructions per wave. "
+              "SQ_WAVE_CYCLES, SQ_WAIT_ANY (waiting on s_waitcnt: memory and LDS counters), "
+              "SQ_WAIT_INST_ANY (waiting to issue the next instruction) and SQ_ACTIVE_INST_VALU "
+              "share one unit (quad-cycles), so their ratios are fractions of resident wave time. "
+              f"Bank conflicts and MFMA busy cycles are per CU ({CUS} CUs). Wave time is "
+              "SQ_WAVE_CYCLES x 4 / waves, in shader cycles (about 2.1 GHz under load; counter "
+              "runs serialise dispatches, so these kernels run a little slower than in the "
+              "stream).", "",
+              "| kernel | dispatches | waves | VALU / wave | MFMA / wave | LDS / wave | VMEM loads / wave "
+              "| wave time (kcycles) | waiting on memory % | waiting to issue % | VALU active % "
+              "| LDS bank-conflict cycles / CU | MFMA busy cycles / CU |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(keep, key=lambda k: (("<8" in k), k)):
+        ca, n = a[k]
+        cb, _ = b[k]
+        w = ca["SQ_WAVES"]
+        wc = cb["SQ_WAVE_CYCLES"]
+        lines.append(
+            f"| `{k}` | {n} | {w:.0f} | {ca['SQ_INSTS_VALU'] / w:.0f} | {ca['SQ_INSTS_MFMA'] / w:.0f} | "
+            f"{ca['SQ_INSTS_LDS'] / w:.0f} | {ca['SQ_INSTS_VMEM_RD'] / w:.0f} | {wc * 4 / w / 1e3:.1f} | "
+            f"{100 * cb['SQ_WAIT_ANY'] / wc:.0f} | {100 * cb['SQ_WAIT_INST_ANY'] / wc:.0f} | "
+            f"{100 * cb['SQ_ACTIVE_INST_VALU'] / wc:.0f} | {cb['SQ_LDS_BANK_CONFLICT'] / CUS:.0f} | "
+            f"{cb['SQ_VALU_MFMA_BUSY_CYCLES'] / CUS:.0f} |")
+    lines += ["", "Kernel names as in the kernel statistics: gemv_ring_kernel<M, FMT, MODE, ROTX> "
+              "(dot products), gemv_mfma_pack_kernel<M, FMT, MODE> (matrix cores), "
+              "ffn_layers_kernel<M, FMT> (32 layers per launch)."]
+    with open(os.path.join(out, "ffn64_stream_sq_counters.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}/ffn64_stream_sq_counters.md")
+
+
 def main():
     p = argparse.ArgumentParser()
-    p.add_argument("--stats", required=True)
-    p.add_argument("--pmc", required=True)
-    p.add_argument("--bench", required=True)
+    p.add_argument("--stats")
+    p.add_argument("--pmc")
+    p.add_argument("--bench")
+    p.add_argument("--sq", help="parent directory of the SQ counter runs pmc_sq_a and pmc_sq_b")
     p.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = p.parse_args()
+    if a.sq:
+        write_sq(a.sq, a.out)
+    if not a.stats:
+        return
 
     bench = None
     with open(a.bench) as fh:
