@@ -137,11 +137,13 @@ int tb_ffn_gateup_silu(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q
 
 /* Gate/up from the fp32 activation: tb_rotate_quant_i8(x) into qx, dqx, then
  * tb_ffn_gateup_silu on them, as one call. The rotated int8 copy is made once
- * per step and shared by the two projections (PR #1154, commit message); for
- * up to 4 rows on the dot-product core every workgroup makes its own copy in
- * LDS while its first weight loads are in flight, which saves the separate
- * launch, and workgroup 0 writes the copy to qx, dqx. Results are
- * bit-identical to the two calls (same rotation arithmetic, same fold).
+ * per step and shared by the two projections (PR #1154, commit message). For
+ * up to 4 rows on the dot-product kernel with m * k/128 <= 128 (two blocks per
+ * 16-lane group of a workgroup; at k = 5120, m <= 3) every workgroup makes its
+ * own copy in LDS while its first weight loads are in flight, which saves the
+ * separate launch, and workgroup 0 writes the copy to qx, dqx; otherwise the
+ * call runs the two launches. Results are bit-identical to the two calls
+ * (same rotation arithmetic, same fold).
  *   x    float [m][wg->k]     input, 16-byte aligned
  *   qx   int8  [m][wg->k]     output: rotquant(x) codes
  *   dqx  float [m][wg->k/128] output: their block scales
@@ -154,9 +156,11 @@ int tb_ffn_gateup_silu_x(const tb_matrix *wg, const tb_matrix *wu, const float *
  * tb_rotate_quant_i8, into caller-owned workspace, then the GEMV. The pages'
  * int8 scratch is allocated with the weight copy, never as hidden static
  * memory (PR #1154, Summary), so here the caller passes it in.
- * Up to 4 rows on the dot-product core rotate h inside the GEMV's own launch
- * (as tb_ffn_gateup_silu_x does with x); the batch variant always runs the
- * two steps as separate launches. Either way the results are the same bits.
+ * Where tb_ffn_gateup_silu_x would rotate inside its launch (up to 4 rows on
+ * the dot-product kernel, m * k/128 <= 128; not at k = 17408) the rotation of
+ * h runs inside the GEMV's launch; otherwise, and always in the batch
+ * variant, the two steps are separate launches. Either way the results are
+ * the same bits.
  *   h       float [m][wd->k]    input (the output of tb_ffn_gateup_silu)
  *   qh_ws   int8  [m][wd->k]    workspace; holds rotquant(h) on return
  *   dqh_ws  float [m][wd->k/128] workspace; holds its scales on return
@@ -167,8 +171,9 @@ int tb_ffn_down(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws, float
 /* GEMV of fp32 rows: tb_rotate_quant_i8(x) into qx, dqx, then tb_gemv_ternary
  * on them, as one call; the same operation and code as tb_ffn_down, for any
  * projection whose input arrives in fp32 (the attention projections of the
- * same model). Up to 4 rows on the dot-product core rotate x inside the
- * GEMV's launch; results are bit-identical to the two calls.
+ * same model). Where the rows allow it (as for tb_ffn_gateup_silu_x) x is
+ * rotated inside the GEMV's launch; results are bit-identical to the two
+ * calls.
  *   x    float [m][w->k]     input, 16-byte aligned
  *   qx   int8  [m][w->k]     output: rotquant(x) codes
  *   dqx  float [m][w->k/128] output: their block scales
