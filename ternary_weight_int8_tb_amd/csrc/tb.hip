@@ -2,32 +2,35 @@
 //
 // The path, after "perf(bonsai): decode and small packed batches read the FFN from a
 // ternary copy through a dp4a GEMV" (sparkinfer PR #1154, Summary and commit message):
-//   1. a Hadamard rotation emits one int8 copy of the activation, which gate and up share
-//      (rotquant_kernel);
+//   1. the activation is rotated (block Hadamard) and quantised to int8 once, and both gate
+//      and up read that copy (rotquant_kernel, or inside the gate/up launch: stage_rotate);
 //   2. an integer dot-product GEMV streams the stored ternary blocks, stages the int8
 //      activation once per workgroup, folds each block's scale into its integer sum, and
 //      reduces with a lane shuffle tree (gemv_ring_kernel, gemv_sliced_kernel);
 //   3. packed steps of up to 8 rows give every row the bytes it gets alone: each row's lane
-//      walk, block fold and reduction tree do not depend on the row count M.
+//      walk, block fold and reduction tree do not depend on the row count M (and the
+//      *_batch calls carry that to 32 rows).
 //
 // gfx950 mapping (the pages' sm_120 design is prior art; this is the CDNA4 one):
 //   * wave64. A wave covers 4 weight rows x 16 "chunk lanes". A chunk is 16 bytes of codes:
 //     64 ternary weights (half a block) or 128 sign weights (one block). In each step the
 //     16 lanes of a row read 256 contiguous bytes: coalesced 16-byte non-temporal loads.
 //   * Streaming (gemv_ring_kernel): one workgroup of 16 waves per CU stages the int8
-//     activation once; each CU owns an equal share of the row tiles, and its waves take
-//     (tile, step) items from an LDS counter, loads running two or three items ahead in a
-//     register ring. Each step's partial sums meet in LDS and are added in step order.
+//     activation once (or rotates the fp32 input itself, for a few rows); each CU owns an
+//     equal share of the row tiles, and its waves take (tile, step) items from an LDS
+//     counter, loads running one (gate/up) or two (one matrix) items ahead in a register
+//     ring. Each step's partial sums meet in LDS and are added in step order.
 //   * 2-bit decode with v_perm_b32 (9 VALU ops per 16 weights, shared by all M rows),
 //     v_dot4c_i32_i8 against the LDS-staged transposed activation, one DPP add to join the
 //     two half-block sums, an fp32 term per block, a fixed DPP tree per row and step, and
 //     the step partials summed in step order (tb_device.h).
-//   * With M <= 8 rows this is not a dense contraction: the roof is HBM. From M = 5 on
-//     gate/up (both formats), and from M = 6 (ternary) or 7 (sign) on the single GEMV,
-//     hand their integer dot products to v_mfma_i32_16x16x64_i8 (gemv_mfma_kernel), where
-//     M dot products per 4 weights would bind the VALU. The block-sum export follows the
-//     gate/up threshold, so it runs the matrix-core integer core at every M where
-//     production does.
+//   * With M <= 32 rows this is not a dense contraction: the roof is HBM. From M = 5 on
+//     gate/up (both formats), and from M = 6 (ternary) or 7 (sign) on the single GEMV, the
+//     integer dot products go to v_mfma_i32_16x16x64_i8, where that measures faster:
+//     gemv_mfma_pack_kernel (two blocks per MFMA) up to 8 rows, gemv_mfma_kernel (16-row
+//     tiles) for batches of 9 to 16 rows. The block-sum export follows the gate/up
+//     threshold, so it runs the matrix-core integer core at every M where production does.
+//   * 1-bit weights in the row-interleaved layout take a lookup-table GEMV (tb_lut.h).
 //   * No floating-point atomics.
 #include <hip/hip_runtime.h>
 
