@@ -254,6 +254,44 @@ def read_probe(torch, nbytes: int, reps: int = 5):
     return best
 
 
+def shader_clock(torch, replay, rounds: int = 4):
+    """The shader clock while the M=1 stream runs, measured on the GPU: the clock probe (one
+    wave per CU, 50 us of real time) is launched on a second stream, at the default priority,
+    while about 20 graph replays are queued on the current one, so its waves share the CUs
+    with the stream's kernels; per workgroup, shader-clock ticks over 100 MHz real-time
+    ticks. The same probe on the idle GPU is reported beside it. MHz: median, min, max."""
+    import ctypes
+    from ternary_weight_int8_tb_amd import build as tb_build
+    path = os.path.join(ROOT, "ternary_weight_int8_tb_amd", "libtb_probe.so")
+    if not os.path.exists(path):
+        tb_build.build()
+    P = ctypes.CDLL(path)
+    P.tbp_clock.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    grid = 256
+    out = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+
+    def run(busy: bool):
+        mhz = []
+        for _ in range(rounds):
+            torch.cuda.synchronize()
+            if busy:
+                for _ in range(20):
+                    replay()
+            rc = P.tbp_clock(5000, out.data_ptr(), grid, side.cuda_stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                return None
+            o = out.view(grid, 2).cpu().numpy().astype(np.float64)
+            mhz += list(o[:, 0] / np.maximum(o[:, 1], 1.0) * 100.0)
+        mhz = np.sort(np.array(mhz))
+        return {"median": round(float(np.median(mhz)), 1), "min": round(float(mhz[0]), 1),
+                "max": round(float(mhz[-1]), 1), "samples": int(mhz.size)}
+    return {"while_m1_stream_runs": run(True), "idle": run(False),
+            "method": "s_memtime ticks over s_memrealtime (100 MHz) ticks in a 50 us probe "
+                      "wave per CU, launched beside the replayed M=1 graph"}
+
+
 def gateup_event_timing(torch, s: Stream64, reps: int):
     """Mean duration (s) of the gate/up launch of the separate-call path at M=1 (the
     rotation of x inside it): HIP events around back-to-back launches over every layer's
@@ -679,6 +717,10 @@ def main():
     log("M=1 calls (graph, us): " + ", ".join(f"{k[:-3]} {v}" for k, v in breakdown.items()
                                                if k.endswith("_us")))
     clocks = gpu_clocks(torch, graph1.replay) if graph1 is not None else None
+    sclk = shader_clock(torch, graph1.replay) if graph1 is not None else None
+    if sclk:
+        log(f"shader clock (probe beside the M=1 stream): {sclk['while_m1_stream_runs']} MHz; "
+            f"idle: {sclk['idle']} MHz")
     log("clocks (while the M=1 graph replays): "
         + (" | ".join(clocks["lines"]) if clocks else "amd-smi unavailable"))
     del f1, s1, graph1
@@ -892,6 +934,7 @@ def main():
         "parity_checked": parity,
         "m1_call_breakdown": breakdown,
         "gpu_clocks_amd_smi": clocks,
+        "gpu_shader_clock_mhz": sclk,
     }
     print(json.dumps(out), flush=True)
     if not parity_ok:

@@ -3,6 +3,9 @@
 //   tbp_stream_read: reads a device buffer once with 16-byte non-temporal loads (the same
 //                    load the GEMV kernels use) and folds it into one word per workgroup,
 //                    to measure the achievable HBM read bandwidth.
+//   tbp_clock:       per workgroup, shader-clock ticks (s_memtime) over a span of real-time
+//                    ticks (s_memrealtime, 100 MHz): launched beside running kernels, the
+//                    ratio is the shader clock they run at.
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -46,9 +49,39 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4 *__re
     }
 }
 
+// One wave per workgroup; its first lane records the shader ticks that pass while the real-time
+// counter advances by `ticks` (a bounded wait: it ends after ticks / 100 MHz).
+__global__ __launch_bounds__(64) void clock_kernel(uint32_t ticks, unsigned long long *out)
+{
+    const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    unsigned long long r1 = r0;
+    while (r1 - r0 < ticks) {
+        __builtin_amdgcn_s_sleep(2);
+        r1 = __builtin_amdgcn_s_memrealtime();
+    }
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = t1 - t0;
+        out[2 * blockIdx.x + 1] = r1 - r0;
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+// out: device uint64 array of 2 * grid entries (shader ticks, real-time ticks per workgroup);
+// 1 <= ticks <= 10^7 (at most 0.1 s). Returns 0 or a HIP error code.
+int tbp_clock(uint32_t ticks, unsigned long long *out, int grid, void *stream)
+{
+    if (!out || grid < 1 || ticks < 1 || ticks > 10000000u)
+        return -1;
+    hipLaunchKernelGGL(clock_kernel, dim3(grid), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       ticks, out);
+    return (int)hipGetLastError();
+}
+
 
 // buf: device buffer of `bytes` bytes (16-byte aligned, bytes % 16 == 0);
 // sink: device uint32 array of at least `grid` entries. Returns 0 or a HIP error code.
