@@ -86,6 +86,16 @@ constexpr int kRingDepthOne = TB_RING_DEPTH_ONE;   // one matrix
 // at depth 1 against 19.7 at depth 2, one matrix 18.9 against 20.2; sign gate/up, which
 // fits 12 waves only at depth 1, 17.3-17.8 there against 19.8-20.8 at depth 2 on 8 waves)
 constexpr int kMfmaDepth = TB_MFMA_DEPTH;
+// Activation units staged per thread and round by the matrix-core kernels (16 bytes per
+// ternary unit, 32 per sign unit): one round covers M=8 at k = 17408, so every staging load
+// is in flight at once. 64-layer stream at M=8, µs/layer with 4 / 6 / 9 / 12 ternary units:
+// 36.81-36.88 / 36.89 / 36.45 / 36.08 (no spills at 12: 96 registers).
+#ifndef TB_MFMA_STAGE_TERN
+#define TB_MFMA_STAGE_TERN 12
+#endif
+#ifndef TB_MFMA_STAGE_SIGN
+#define TB_MFMA_STAGE_SIGN 6
+#endif
 #ifndef TB_STAGE_FIRST
 #define TB_STAGE_FIRST 0
 #endif
@@ -184,7 +194,8 @@ __device__ __forceinline__ void stage_activation(const GemvArgs &a, uint8_t *act
                                                  int *qsum_s, Prologue &&prologue)
 {
     constexpr int kBlocksPerStep = kChunkLanes / Fmt<FMT>::kChunksPerBlock;
-    constexpr int kStageRound = 4, kTermRound = 2;
+    constexpr int kStageRound = MFMA_LAYOUT ? (FMT == TB_FMT_TERNARY2 ? TB_MFMA_STAGE_TERN : TB_MFMA_STAGE_SIGN) : 4;
+    constexpr int kTermRound = 2;
     const int tid = threadIdx.x, k = a.k, nb = k / kBlock;
     const int per_row = (k / Fmt<FMT>::kWeightsPerChunk) * 4, units = M * per_row;
     const int nterm = (nb + kBlocksPerStep) * M;
