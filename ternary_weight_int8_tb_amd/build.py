@@ -20,6 +20,9 @@ FLAGS = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     # no packed fp32 instructions (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive preloaded in SGPRs (no kernel-argument fetch
+    # before the first loads); the code object keeps a fallback for firmware without it
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

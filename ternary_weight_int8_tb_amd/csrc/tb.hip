@@ -368,9 +368,36 @@ __device__ __forceinline__ void stage_rotate(const GemvArgs &a, uint8_t *act, fl
 // ROTX: the activation arrives as fp32 x and each workgroup rotates and quantises it
 // itself (stage_rotate), which saves a launch on the decode path.
 // ------------------------------------------------------------------------------------
+//
+// Launch: the leading arguments (the matrices, the activation, n, k, the grid) are
+// separate scalars, which the command processor preloads into SGPRs (built with
+// -amdgpu-kernarg-preload-count), so the first loads wait for no kernel-argument fetch;
+// the rest comes in GemvArgs. With ROTX every wave issues its first weight items (static:
+// wave w takes w + 16 d) right behind its x loads, before any barrier; the item counter
+// starts after the staging barrier. (Without ROTX the counter hands out every item but the
+// first: measured faster there.)
 template <int M, int FMT, int MODE, bool ROTX = false>
-__global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
+__global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(const void *p0, const void *p1,
+                                                                 const void *p2, const void *p3,
+                                                                 const void *p4, int pn, int pk,
+                                                                 int pg, GemvArgs a_in)
 {
+    constexpr bool kTwoArgs = MODE == kModeGateUp;
+    GemvArgs a = a_in;
+    a.codes0 = static_cast<const uint8_t *>(p0);
+    a.scales0 = static_cast<const uint16_t *>(p1);
+    if (kTwoArgs) {
+        a.codes1 = static_cast<const uint8_t *>(p2);
+        a.scales1 = static_cast<const uint16_t *>(p3);
+    }
+    a.q = static_cast<const int8_t *>(kTwoArgs ? p4 : p2);   // the activation: q, or x (ROTX)
+    a.x = static_cast<const float *>(kTwoArgs ? p4 : p2);
+    if (!kTwoArgs)
+        a.dq = static_cast<const float *>(p3);
+    a.n = pn;
+    a.k = pk;
+    a.codes_bytes = (uint32_t)((size_t)pn * (size_t)pk / (FMT == TB_FMT_TERNARY2 ? 4u : 8u));
+    a.scales_bytes = (uint32_t)(((size_t)pn * (size_t)(pk / kBlock) * 2u + 3u) & ~(size_t)3);
     static_assert(!ROTX || MODE != kModeIsum, "the block-sum export takes int8 input");
     extern __shared__ __align__(16) uint8_t lds[];
     using L = StepLayout<M, FMT>;
@@ -386,7 +413,7 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     const int C = k / kWpc;                 // chunks per row
     const int I = (C + kChunkLanes - 1) / kChunkLanes;   // steps per tile
     const int tid = threadIdx.x, lane = tid & 63, cl = lane & 15, rl = lane >> 4;
-    const int G = gridDim.x, c = blockIdx.x;
+    const int G = pg, c = blockIdx.x;
     const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
     const int tA = part_lo(T, G, c), tB = part_lo(T, G, c + 1);
     const int J = (tB - tA) * I;            // this workgroup's items
@@ -409,12 +436,14 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     const __amdgpu_buffer_rsrc_t rc1 = buffer_rsrc(kTwo ? a.codes1 : a.codes0, a.codes_bytes);
     const __amdgpu_buffer_rsrc_t rsc1 = buffer_rsrc(kTwo ? a.scales1 : a.scales0, a.scales_bytes);
 
-    if (tid == 0)
-        *ctr_s = kRingWaves;   // wave w starts with item w
-    if (FMT == TB_FMT_SIGN1)
-        for (int i = tid; i < (nb + kBlocksPerStep) * M; i += kRingThreads)
-            qsum_s[i] = 0;
-    __syncthreads();
+    if (!ROTX) {
+        if (tid == 0)
+            *ctr_s = kRingWaves;   // wave w starts with item w
+        if (FMT == TB_FMT_SIGN1)   // the staging adds code sums into qsum_s
+            for (int i = tid; i < (nb + kBlocksPerStep) * M; i += kRingThreads)
+                qsum_s[i] = 0;
+        __syncthreads();
+    }
 
     // ---- issue side ------------------------------------------------------------------
     // The wave's items increase, so (tile, step) follow by carrying the step over.
@@ -441,7 +470,7 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     // 4-byte word gives the word of (row, block).
     const uint32_t lane_off = (uint32_t)rl * row_bytes + (uint32_t)cl * 16u;
     const uint32_t lane_soff = (((uint32_t)rl * (uint32_t)nb + (uint32_t)(cl / kCpb)) * 2u) & ~3u;
-    auto issue = [&](uint4 &w0, uint4 &w1, uint32_t &s0, uint32_t &s1, int &it) {
+    auto issue = [&](uint4 &w0, uint4 &w1, uint32_t &s0, uint32_t &s1, int &it, bool take) {
         const int idx = __builtin_amdgcn_readfirstlane(pending);
         uint32_t off = kOutOfRange, soff = kOutOfRange;
         int so = 0, sso = 0;
@@ -460,10 +489,12 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
                 soff = kOutOfRange;
             }
             // take the next item now; the add completes while this one streams
-            int v = 0;
-            if (lane == 0)
-                v = atomicAdd(ctr_s, 1);
-            pending = v;
+            if (take) {
+                int v = 0;
+                if (lane == 0)
+                    v = atomicAdd(ctr_s, 1);
+                pending = v;
+            }
         }
         w0 = buffer_load16_nt(rc0, off, so);
         s0 = buffer_load_u32(rsc0, soff, sso);
@@ -479,14 +510,25 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
     // ---- staging (q and the block terms; the ring prologue between loads and stores)
     auto prologue = [&]() {
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d)
-            issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
+        for (int d = 0; d < kDepth; ++d) {
+            if (ROTX)   // static first items: no counter before the barrier
+                pending = (tid >> 6) + kRingWaves * d;
+            issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d], !ROTX);
+        }
     };
     if constexpr (ROTX)
         stage_rotate<M, FMT, kRingThreads>(a, act, dq_s, qsum_s, prologue);
     else
         stage_activation<M, FMT, MODE, kRingThreads, false>(a, act, dq_s, qsum_s, prologue);
+    if (ROTX && tid == 0)
+        *ctr_s = kRingWaves * kDepth;   // the prologue took items w + 16 d
     __syncthreads();
+    if (ROTX) {
+        int v = 0;
+        if (lane == 0)
+            v = atomicAdd(ctr_s, 1);
+        pending = v;
+    }
 
     // ---- compute side -----------------------------------------------------------------
     const uint8_t *lds_lane = act + cl * 16;
@@ -549,7 +591,7 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(GemvArgs a)
                 consume(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
                 any = true;
             }
-            issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d]);
+            issue(rb0[d], rb1[d], rs0[d], rs1[d], rit[d], true);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (!any)
@@ -1333,7 +1375,46 @@ using GemvFn = void (*)(GemvArgs);
         return NAME##_pick_m<TB_FMT_SIGN1, kModeIsum>(m);                                      \
     }
 
-TB_KERNEL_TABLE(gemv_ring_kernel)
+using RingFn = void (*)(const void *, const void *, const void *, const void *, const void *, int,
+                       int, int, GemvArgs);
+template <int FMT, int MODE>
+RingFn gemv_ring_kernel_pick_m(int m)
+{
+    switch (m) {
+    case 1: return gemv_ring_kernel<1, FMT, MODE>;
+    case 2: return gemv_ring_kernel<2, FMT, MODE>;
+    case 3: return gemv_ring_kernel<3, FMT, MODE>;
+    case 4: return gemv_ring_kernel<4, FMT, MODE>;
+    case 5: return gemv_ring_kernel<5, FMT, MODE>;
+    case 6: return gemv_ring_kernel<6, FMT, MODE>;
+    case 7: return gemv_ring_kernel<7, FMT, MODE>;
+    case 8: return gemv_ring_kernel<8, FMT, MODE>;
+    default: return nullptr;
+    }
+}
+RingFn gemv_ring_kernel_pick(int fmt, int mode, int m)
+{
+    if (fmt == TB_FMT_TERNARY2) {
+        if (mode == kModeY) return gemv_ring_kernel_pick_m<TB_FMT_TERNARY2, kModeY>(m);
+        if (mode == kModeGateUp) return gemv_ring_kernel_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m);
+        return gemv_ring_kernel_pick_m<TB_FMT_TERNARY2, kModeIsum>(m);
+    }
+    if (mode == kModeY) return gemv_ring_kernel_pick_m<TB_FMT_SIGN1, kModeY>(m);
+    if (mode == kModeGateUp) return gemv_ring_kernel_pick_m<TB_FMT_SIGN1, kModeGateUp>(m);
+    return gemv_ring_kernel_pick_m<TB_FMT_SIGN1, kModeIsum>(m);
+}
+// Launches gemv_ring_kernel: its leading scalar arguments are the matrices, the activation
+// act (q, or x with ROTX), n, k and the grid (see the kernel).
+void launch_ring(RingFn fn, int grid, size_t lds, hipStream_t stream, const GemvArgs &a,
+                 const void *act)
+{
+    const bool two = a.codes1 != nullptr;
+    const void *p2 = two ? static_cast<const void *>(a.codes1) : act;
+    const void *p3 = two ? static_cast<const void *>(a.scales1) : static_cast<const void *>(a.dq);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kRingThreads), lds, stream,
+                       static_cast<const void *>(a.codes0), static_cast<const void *>(a.scales0),
+                       p2, p3, two ? act : nullptr, a.n, a.k, grid, a);
+}
 TB_KERNEL_TABLE(gemv_sliced_kernel)
 
 template <int FMT, int MODE>
@@ -1638,14 +1719,14 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
     const size_t ring_lds = ring_lds_bytes(w0, mode, m, ring_grid);
     // (both kernels fold every row in the same order, so the choice never changes a result)
     if (ring_lds <= (size_t)info.lds_limit) {
-        GemvFn fn = gemv_ring_kernel_pick(w0->fmt, mode, m);
+        RingFn fn = gemv_ring_kernel_pick(w0->fmt, mode, m);
         if (!fn)
             return TB_EINVAL;
-        if ((rc = set_lds(fn, ring_lds)))
+        if ((rc = raise_lds(reinterpret_cast<const void *>(fn), ring_lds)))
             return rc;
         // one workgroup per CU (fewer only if there are fewer row tiles than CUs)
         a.slice_chunks = C;
-        hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(kRingThreads), ring_lds, stream, a);
+        launch_ring(fn, ring_grid, ring_lds, stream, a, q);
         return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
     }
     // otherwise stage the activation in slices of S chunks (S a multiple of 16)
@@ -1682,7 +1763,7 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
 #define TB_ROTX_MAX_ROWS 4
 #endif
 template <int FMT, int MODE>
-GemvFn gemv_ring_rotx_pick_m(int m)
+RingFn gemv_ring_rotx_pick_m(int m)
 {
     static_assert(TB_ROTX_MAX_ROWS >= 1 && TB_ROTX_MAX_ROWS <= 4, "built for 1..4 rows");
     switch (m) {
@@ -1715,13 +1796,13 @@ int launch_gemv_rotx(int mode, const tb_matrix *w0, const tb_matrix *w1, const f
     const size_t lds = ring_lds_bytes(w0, mode, m, grid);
     if (lds > (size_t)info.lds_limit)
         return TB_EUNSUPPORTED;
-    GemvFn fn = tern ? (mode == kModeGateUp ? gemv_ring_rotx_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
+    RingFn fn = tern ? (mode == kModeGateUp ? gemv_ring_rotx_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
                                             : gemv_ring_rotx_pick_m<TB_FMT_TERNARY2, kModeY>(m))
                      : (mode == kModeGateUp ? gemv_ring_rotx_pick_m<TB_FMT_SIGN1, kModeGateUp>(m)
                                             : gemv_ring_rotx_pick_m<TB_FMT_SIGN1, kModeY>(m));
     if (!fn)
         return TB_EUNSUPPORTED;
-    if ((rc = set_lds(fn, lds)))
+    if ((rc = raise_lds(reinterpret_cast<const void *>(fn), lds)))
         return rc;
     GemvArgs a = {};
     a.codes0 = static_cast<const uint8_t *>(w0->codes);
@@ -1738,7 +1819,7 @@ int launch_gemv_rotx(int mode, const tb_matrix *w0, const tb_matrix *w1, const f
     a.qx = qx;
     a.dqx = dqx;
     a.unit = dq_unit();
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kRingThreads), lds, stream, a);
+    launch_ring(fn, grid, lds, stream, a, x);
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
