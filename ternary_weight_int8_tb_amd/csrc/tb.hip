@@ -171,6 +171,33 @@ struct GemvArgs {
     float unit;              // fp32(1 / (127 sqrt(128)))
 };
 
+// The arguments of a streaming kernel from its leading scalar arguments (preloaded into
+// SGPRs) and the rest in GemvArgs: p0, p1 the (first) matrix; gate/up: p2, p3 the up matrix
+// and p4 the activation; one matrix: p2 the activation and p3 its block terms. The
+// activation is q, or x for a kernel that rotates it. Buffer sizes follow from n and k.
+template <int FMT, bool TWO>
+__device__ __forceinline__ GemvArgs with_leading_args(const GemvArgs &in, const void *p0,
+                                                      const void *p1, const void *p2,
+                                                      const void *p3, const void *p4, int pn, int pk)
+{
+    GemvArgs a = in;
+    a.codes0 = static_cast<const uint8_t *>(p0);
+    a.scales0 = static_cast<const uint16_t *>(p1);
+    if (TWO) {
+        a.codes1 = static_cast<const uint8_t *>(p2);
+        a.scales1 = static_cast<const uint16_t *>(p3);
+    }
+    a.q = static_cast<const int8_t *>(TWO ? p4 : p2);
+    a.x = static_cast<const float *>(TWO ? p4 : p2);
+    if (!TWO)
+        a.dq = static_cast<const float *>(p3);
+    a.n = pn;
+    a.k = pk;
+    a.codes_bytes = (uint32_t)((size_t)pn * (size_t)pk / (FMT == TB_FMT_TERNARY2 ? 4u : 8u));
+    a.scales_bytes = (uint32_t)(((size_t)pn * (size_t)(pk / kBlock) * 2u + 3u) & ~(size_t)3);
+    return a;
+}
+
 // Writes the results of one finished row (lane 0 of the row's 16 lanes).
 template <int M, int MODE>
 __device__ __forceinline__ void store_row(const GemvArgs &a, int row, const float (&acc0)[M],
@@ -382,22 +409,7 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(const void *p0,
                                                                  const void *p4, int pn, int pk,
                                                                  int pg, GemvArgs a_in)
 {
-    constexpr bool kTwoArgs = MODE == kModeGateUp;
-    GemvArgs a = a_in;
-    a.codes0 = static_cast<const uint8_t *>(p0);
-    a.scales0 = static_cast<const uint16_t *>(p1);
-    if (kTwoArgs) {
-        a.codes1 = static_cast<const uint8_t *>(p2);
-        a.scales1 = static_cast<const uint16_t *>(p3);
-    }
-    a.q = static_cast<const int8_t *>(kTwoArgs ? p4 : p2);   // the activation: q, or x (ROTX)
-    a.x = static_cast<const float *>(kTwoArgs ? p4 : p2);
-    if (!kTwoArgs)
-        a.dq = static_cast<const float *>(p3);
-    a.n = pn;
-    a.k = pk;
-    a.codes_bytes = (uint32_t)((size_t)pn * (size_t)pk / (FMT == TB_FMT_TERNARY2 ? 4u : 8u));
-    a.scales_bytes = (uint32_t)(((size_t)pn * (size_t)(pk / kBlock) * 2u + 3u) & ~(size_t)3);
+    GemvArgs a = with_leading_args<FMT, MODE == kModeGateUp>(a_in, p0, p1, p2, p3, p4, pn, pk);
     static_assert(!ROTX || MODE != kModeIsum, "the block-sum export takes int8 input");
     extern __shared__ __align__(16) uint8_t lds[];
     using L = StepLayout<M, FMT>;
@@ -969,8 +981,13 @@ __host__ __device__ inline PackLds pack_lds(int M, int fmt, int k, int waves)
 }
 
 template <int M, int FMT, int MODE>
-__global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(GemvArgs a)
+__global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const void *p0, const void *p1,
+                                                                           const void *p2, const void *p3,
+                                                                           const void *p4, int pn, int pk,
+                                                                           int pg, GemvArgs a_in)
 {
+    // leading arguments preloaded into SGPRs, as for gemv_ring_kernel
+    const GemvArgs a = with_leading_args<FMT, MODE == kModeGateUp>(a_in, p0, p1, p2, p3, p4, pn, pk);
     static_assert(M >= 1 && M <= 8, "two blocks per MFMA: at most 8 activation rows");
     extern __shared__ __align__(16) uint8_t lds[];
     using L = StepLayout<M, FMT>;
@@ -989,7 +1006,7 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(GemvA
     const int C = k / Fmt<FMT>::kWeightsPerChunk, I = (C + kChunkLanes - 1) / kChunkLanes;
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = gridDim.x, c = blockIdx.x;
+    const int G = pg, c = blockIdx.x;
     const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
     const int R0 = part_lo(T, G, c) * kRowsPerWave;
     const int R1 = min(part_lo(T, G, c + 1) * kRowsPerWave, n);
@@ -1346,6 +1363,9 @@ __global__ __launch_bounds__(kSlicedThreads) void gemv_sliced_kernel(GemvArgs a)
 // Host side
 // ------------------------------------------------------------------------------------
 using GemvFn = void (*)(GemvArgs);
+// gemv_ring_kernel and gemv_mfma_pack_kernel: leading scalar arguments, then GemvArgs
+using RingFn = void (*)(const void *, const void *, const void *, const void *, const void *, int,
+                       int, int, GemvArgs);
 
 #define TB_KERNEL_TABLE(NAME)                                                                  \
     template <int FMT, int MODE>                                                               \
@@ -1375,8 +1395,6 @@ using GemvFn = void (*)(GemvArgs);
         return NAME##_pick_m<TB_FMT_SIGN1, kModeIsum>(m);                                      \
     }
 
-using RingFn = void (*)(const void *, const void *, const void *, const void *, const void *, int,
-                       int, int, GemvArgs);
 template <int FMT, int MODE>
 RingFn gemv_ring_kernel_pick_m(int m)
 {
@@ -1403,15 +1421,15 @@ RingFn gemv_ring_kernel_pick(int fmt, int mode, int m)
     if (mode == kModeGateUp) return gemv_ring_kernel_pick_m<TB_FMT_SIGN1, kModeGateUp>(m);
     return gemv_ring_kernel_pick_m<TB_FMT_SIGN1, kModeIsum>(m);
 }
-// Launches gemv_ring_kernel: its leading scalar arguments are the matrices, the activation
-// act (q, or x with ROTX), n, k and the grid (see the kernel).
+// Launches gemv_ring_kernel or gemv_mfma_pack_kernel: the leading scalar arguments are the
+// matrices, the activation act (q, or x with ROTX), n, k and the grid (see the kernel).
 void launch_ring(RingFn fn, int grid, size_t lds, hipStream_t stream, const GemvArgs &a,
-                 const void *act)
+                 const void *act, int threads = kRingThreads)
 {
     const bool two = a.codes1 != nullptr;
     const void *p2 = two ? static_cast<const void *>(a.codes1) : act;
     const void *p3 = two ? static_cast<const void *>(a.scales1) : static_cast<const void *>(a.dq);
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kRingThreads), lds, stream,
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), lds, stream,
                        static_cast<const void *>(a.codes0), static_cast<const void *>(a.scales0),
                        p2, p3, two ? act : nullptr, a.n, a.k, grid, a);
 }
@@ -1438,7 +1456,7 @@ GemvFn gemv_mfma_pick_m(int m)
     }
 }
 template <int FMT, int MODE>
-GemvFn gemv_mfma_pack_pick_m(int m)
+RingFn gemv_mfma_pack_pick_m(int m)
 {
     switch (m) {
     case 2: return gemv_mfma_pack_kernel<2, FMT, MODE>;
@@ -1680,7 +1698,7 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
         const size_t pack_lds_bytes = m > 8 ? ~(size_t)0 :
             pack_lds(m, w0->fmt, w0->k, pack_threads(w0->fmt) / 64).part + parts;
         if (m <= 8 && pack_lds_bytes <= (size_t)info.lds_limit) {
-            GemvFn fn = tern ? (mode == kModeGateUp ? gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
+            RingFn fn = tern ? (mode == kModeGateUp ? gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeGateUp>(m)
                                 : mode == kModeY  ? gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeY>(m)
                                                   : gemv_mfma_pack_pick_m<TB_FMT_TERNARY2, kModeIsum>(m))
                              : (mode == kModeGateUp ? gemv_mfma_pack_pick_m<TB_FMT_SIGN1, kModeGateUp>(m)
@@ -1688,9 +1706,9 @@ int launch_gemv(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t
                                                   : gemv_mfma_pack_pick_m<TB_FMT_SIGN1, kModeIsum>(m));
             if (!fn)
                 return TB_EINVAL;
-            if ((rc = set_lds(fn, pack_lds_bytes)))
+            if ((rc = raise_lds(reinterpret_cast<const void *>(fn), pack_lds_bytes)))
                 return rc;
-            hipLaunchKernelGGL(fn, dim3(ring_grid), dim3(pack_threads(w0->fmt)), pack_lds_bytes, stream, a);
+            launch_ring(fn, ring_grid, pack_lds_bytes, stream, a, q, pack_threads(w0->fmt));
             return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
         }
 #endif
