@@ -12,10 +12,11 @@ quantise h, down. Nothing is hoisted out of a step.
 Two complete paths are timed at M=1, both with strict layer order (layer l+1
 starts after every output of layer l is written; no layer is overlapped with
 another and no work is hoisted out of a step): the fused entry point
-tb_ffn_layers (one persistent launch per 32 layers), and the three separate
-calls per layer (tb_rotate_quant_i8, tb_ffn_gateup_silu, tb_ffn_down) replayed
-from a HIP graph (and eagerly). The value is the faster of the two; the JSON
-names it. Also printed: the same at M=8; the 1-bit sign stream; the roofline
+tb_ffn_layers (one persistent launch per 32 layers), and the separate calls per
+layer (tb_ffn_gateup_silu_x, which rotates x inside its launch where that
+applies, and tb_ffn_down_split, which at M=1 runs tb_ffn_down's kernels and
+from 4 rows splits the down stage over k) replayed from a HIP graph (and
+eagerly). The value is the faster of the two; the JSON names it. Also printed: the same at M=8; the 1-bit sign stream; the roofline
 of the headline path's dominant kernel, timed with HIP events on the stream it
 runs on; a 4 GiB streaming-read probe; and the scalar CPU oracle timed on this
 host's cores.
@@ -97,6 +98,8 @@ class Stream64:
         self.qh = torch.empty(L, m, n, dtype=torch.int8, device=dev)
         self.dqh = torch.empty(L, m, n // 128, dtype=torch.float32, device=dev)
         self.y = torch.empty(L, m, k, dtype=torch.float32, device=dev)
+        # the step partials of tb_ffn_down_split (one workspace: the calls are in order)
+        self.ws = None if batch else tb.tb_ffn_down_split_workspace(layers_dev[0][2], m)
 
     def step(self):
         tb = self.tb
@@ -108,7 +111,7 @@ class Stream64:
             return
         for l, (wg, wu, wd) in enumerate(self.layers):
             tb.tb_ffn_gateup_silu_x(wg, wu, self.x[l], self.q[l], self.dq[l], self.h[l])
-            tb.tb_ffn_down(wd, self.h[l], self.qh[l], self.dqh[l], self.y[l])
+            tb.tb_ffn_down_split(wd, self.h[l], self.qh[l], self.dqh[l], self.y[l], self.ws)
 
     def outputs(self):
         """Every intermediate and output of the last step, on the host."""
@@ -913,7 +916,7 @@ def main():
                    "rows": 1, "format": "ternary 2-bit, 128-weight blocks, fp16 scales",
                    "bytes_per_step": step_bytes,
                    "entry_point": {"fused": "tb_ffn_layers (one persistent launch per 32 layers)",
-                                   "separate": "tb_ffn_gateup_silu_x + tb_ffn_down per layer, "
+                                   "separate": "tb_ffn_gateup_silu_x + tb_ffn_down_split per layer, "
                                                + ("hip graph replay" if use_graph else "eager")}[head],
                    "layer_order": "strict: layer l+1 starts after layer l's outputs are written"},
         "us_per_layer": round(t1 / args.layers * 1e6, 3),

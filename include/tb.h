@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TB_ABI_VERSION 4
+#define TB_ABI_VERSION 5
 #define TB_BLOCK 128
 #define TB_MAX_ROWS 8
 #define TB_MAX_BATCH_ROWS 32
@@ -233,6 +233,37 @@ int tb_ffn_down_batch(const tb_matrix *wd, const float *h, int m, int8_t *qh_ws,
                       float *y, void *stream);
 int tb_gemv_block_sums_batch(const tb_matrix *w, const int8_t *q, int m, int32_t *isum,
                              void *stream);
+
+/* ---- Down stage split over k -------------------------------------------
+ * tb_ffn_down with a caller workspace that lets the down stage run split over k
+ * as well as over rows (PR #1154, Summary and commit message: h is rotated and
+ * quantised to int8, then the down matrix's blocks are multiplied against that
+ * copy). From 4 rows on, on the matrix cores: each workgroup of the first
+ * launch takes one step (8 ternary or 16 sign blocks) of one row group. It
+ * rotates and quantises those blocks of h itself (the rotate-quantise
+ * arithmetic, bit for bit) and streams the group's weights at that step, and
+ * each row's step partial goes to ws. A second, small launch adds every row's
+ * partials in step order. That is the fold of tb_ffn_down, so y, qh and dqh are
+ * bit-identical to tb_ffn_down on the same inputs. What it saves is the
+ * separate rotation launch and the staging of all of rotquant(h) in every CU.
+ * For 1 to 3 rows (where the split measured slower), or where its plan does
+ * not apply (k/128 not a multiple of 2 (ternary) or 4 (sign)), the call runs
+ * tb_ffn_down and leaves ws untouched.
+ *   h    float [m][wd->k]     input
+ *   qh   int8  [m][wd->k]     output: rotquant(h) codes
+ *   dqh  float [m][wd->k/128] output: their block scales
+ *   y    float [m][wd->n]     output
+ *   ws   device workspace of at least tb_ffn_down_split_workspace_bytes(wd, m)
+ *        bytes, 16-byte aligned: the step partials, float [steps][m][wd->n],
+ *        steps = ceil(k / 1024) for ternary and ceil(k / 2048) for sign. It needs
+ *        no initialisation; calls that share one must not overlap in time.
+ * 1 <= m <= 8; the format must not be TB_FMT_SIGN1_RI4. Outputs and workspace
+ * may not overlap one another or the inputs. Returns TB_EINVAL for a
+ * workspace that is too small. */
+int tb_ffn_down_split(const tb_matrix *wd, const float *h, int m, int8_t *qh, float *dqh,
+                      float *y, void *ws, size_t ws_bytes, void *stream);
+/* Workspace bytes of tb_ffn_down_split for m rows; 0 for invalid arguments. */
+size_t tb_ffn_down_split_workspace_bytes(const tb_matrix *wd, int m);
 
 /* ---- No allocation -------------------------------------------------------
  * For callers that cannot allocate device memory (code under HIP graph

@@ -130,6 +130,13 @@ constexpr int kPackDepth = TB_PACK_DEPTH;
 #ifndef TB_MFMA_MIN_ROWS_SIGN_ONE
 #define TB_MFMA_MIN_ROWS_SIGN_ONE 7
 #endif
+// Rows from which tb_ffn_down_split takes the split over k (below: tb_ffn_down's route).
+// Down stage of the 64-layer stream (5120 x 17408, ternary), µs per call, tb_ffn_down
+// against the split: M=2 10.66 / 12.64, M=4 13.88 / 12.94, M=6 16.36 / 13.83, M=8 17.33 /
+// 14.52 (sign M=8 18.49 / 15.88).
+#ifndef TB_SPLIT_MIN_ROWS
+#define TB_SPLIT_MIN_ROWS 4
+#endif
 constexpr int mfma_min_rows(bool ternary, bool gateup)
 {
     return ternary ? (gateup ? TB_MFMA_MIN_ROWS_TERN : TB_MFMA_MIN_ROWS_TERN_ONE)
@@ -169,6 +176,10 @@ struct GemvArgs {
     int8_t *qx;
     float *dqx;
     float unit;              // fp32(1 / (127 sqrt(128)))
+    // down stage split over k (gemv_mfma_pack_kernel with KS): row groups, and the step
+    // partials [I][M][n] it writes (x holds h; qx, dqx receive rotquant(h))
+    int groups;
+    float *part;
 };
 
 // The arguments of a streaming kernel from its leading scalar arguments (preloaded into
@@ -980,7 +991,7 @@ __host__ __device__ inline PackLds pack_lds(int M, int fmt, int k, int waves)
     return p;
 }
 
-template <int M, int FMT, int MODE>
+template <int M, int FMT, int MODE, bool KS = false>
 __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const void *p0, const void *p1,
                                                                            const void *p2, const void *p3,
                                                                            const void *p4, int pn, int pk,
@@ -1002,18 +1013,24 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const
     constexpr int kThreads = pack_threads(FMT), kWaves = kThreads / 64;
     constexpr int kScratch = pack_scratch_bytes(FMT);   // per wave: scales [block][row], uint16
 
+    static_assert(!KS || MODE == kModeY, "the split over k is the down stage");
     const int k = a.k, n = a.n, nb = k / kBlock;
-    const int C = k / Fmt<FMT>::kWeightsPerChunk, I = (C + kChunkLanes - 1) / kChunkLanes;
+    const int C = k / Fmt<FMT>::kWeightsPerChunk, Ik = (C + kChunkLanes - 1) / kChunkLanes;
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = pg, c = blockIdx.x;
+    // KS: workgroup (g, s) of a.groups row groups x Ik steps covers step s of group g;
+    // otherwise workgroup c covers all steps of share c of the grid
+    const int G = KS ? a.groups : pg;
+    const int c = KS ? (int)blockIdx.x / Ik : (int)blockIdx.x;
+    const int s0 = KS ? (int)blockIdx.x - c * Ik : 0;   // the step of KS items
+    const int I = KS ? 1 : Ik;                          // steps per tile in this workgroup
     const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
     const int R0 = part_lo(T, G, c) * kRowsPerWave;
     const int R1 = min(part_lo(T, G, c + 1) * kRowsPerWave, n);
     const int J = (((R1 - R0 + 15) / 16) * I) << kMatShift;   // this workgroup's items
     const uint32_t row_bytes = (uint32_t)C * 16u;
 
-    const PackLds pl = pack_lds(M, FMT, k, kWaves);
+    const PackLds pl = pack_lds(M, FMT, KS ? kBps * kBlock : k, kWaves);
     uint8_t *act = lds;
     float *dq_s = reinterpret_cast<float *>(lds + pl.dq);
     int *qsum_s = reinterpret_cast<int *>(lds + pl.qsum);
@@ -1028,7 +1045,7 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const
         *ctr_s = kWaves;   // wave w starts with item w
     for (int i = tid; i < kPackZeroBytes / 4; i += kThreads)
         reinterpret_cast<uint32_t *>(lds + pl.zero)[i] = 0u;
-    if (!kTern)
+    if (!kTern && !KS)
         for (int i = tid; i < (nb + kBps) * M; i += kThreads)
             qsum_s[i] = 0;
     __syncthreads();
@@ -1068,12 +1085,13 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const
             mat = idx & (kTwo ? 1 : 0);
             rit[d] = mat << 30 | gtile << 16 | gstep;
             const int row0 = R0 + gtile * 16;
-            so = row0 * (int)row_bytes + gstep * 256;
-            sso = (row0 * nb + gstep * kBps) * 2;
-            nbk = min(kBps, nb - gstep * kBps);   // blocks of this step inside the row
+            const int wstep = s0 + gstep;            // the step in the weight rows
+            so = row0 * (int)row_bytes + wstep * 256;
+            sso = (row0 * nb + wstep * kBps) * 2;
+            nbk = min(kBps, nb - wstep * kBps);   // blocks of this step inside the row
             if (row0 + li < R1) {
                 off = lane_off;
-                soff = (!kIsum && gstep * kBps + lg * kBpl < nb) ? lane_soff : kOutOfRange;
+                soff = (!kIsum && wstep * kBps + lg * kBpl < nb) ? lane_soff : kOutOfRange;
             }
             int v = 0;
             if (lane == 0)
@@ -1105,11 +1123,65 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const
         }
     };
 
-    stage_activation<M, FMT, MODE, kThreads, true>(a, act, dq_s, qsum_s, [&]() {
+    if constexpr (KS) {
+        // h loads of step s0's blocks first, then the weight prologue, then the rotation
+        constexpr int kGroups16 = kThreads / 16;
+        constexpr int kRounds = (M * kBps + kGroups16 - 1) / kGroups16;
+        const int l16 = tid & 15, grp = tid >> 4;
+        const int b0 = s0 * kBps, nbs = min(kBps, nb - b0), Z = M * nbs;
+        float hv[kRounds][8];
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int z = grp + r * kGroups16;
+            if (z < Z) {
+                const int m = z / nbs, bl = z - m * nbs;
+                const float *src = a.x + (size_t)m * k + (size_t)(b0 + bl) * kBlock + l16 * 8;
+                const float4 lo = *reinterpret_cast<const float4 *>(src);
+                const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+                hv[r][0] = lo.x; hv[r][1] = lo.y; hv[r][2] = lo.z; hv[r][3] = lo.w;
+                hv[r][4] = hi.x; hv[r][5] = hi.y; hv[r][6] = hi.z; hv[r][7] = hi.w;
+            }
+        }
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
             issue(d);
-    });
+        for (int i = Z + tid; i < 2 * kBps * M; i += kThreads) {   // [block][m] past the step
+            dq_s[i] = 0.0f;
+            if (!kTern)
+                qsum_s[i] = 0;
+        }
+        // (the zero slots of blocks past nbs: chunks past C read zero weights; their
+        // activation slots are never multiplied by a nonzero code)
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int z = grp + r * kGroups16;
+            if (z < Z) {   // (a 16-lane group takes or skips a block as a whole)
+                const int m = z / nbs, bl = z - m * nbs;
+                uint32_t pk[2];
+                float dq;
+                int qsum;
+                rotquant_regs(hv[r], l16, a.unit, pk, dq, qsum);
+                store_block_mfma<M, FMT>(act, m, bl, l16, pk);
+                if (l16 == 0) {
+                    dq_s[bl * M + m] = dq;
+                    if (!kTern)
+                        qsum_s[bl * M + m] = qsum;
+                }
+                if (c == 0) {   // row group 0 writes rotquant(h)
+                    *reinterpret_cast<uint2 *>(a.qx + (size_t)m * k + (size_t)(b0 + bl) * kBlock + l16 * 8) =
+                        make_uint2(pk[0], pk[1]);
+                    if (l16 == 0)
+                        a.dqx[(size_t)m * nb + b0 + bl] = dq;
+                }
+            }
+        }
+    } else {
+        stage_activation<M, FMT, MODE, kThreads, true>(a, act, dq_s, qsum_s, [&]() {
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d)
+                issue(d);
+        });
+    }
     __syncthreads();
 
     // ---- compute side
@@ -1253,8 +1325,15 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const
     }
     if (kIsum)
         return;
-    // ---- every row: its step partials in step order, from +0
     __syncthreads();
+    if constexpr (KS) {   // the step partials [s0][m][row], summed by the fold launch
+        for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
+            const int lrow = i / M, m = i % M;
+            a.part[((size_t)s0 * M + m) * n + R0 + lrow] = part_s[(size_t)lrow * M + m];
+        }
+        return;
+    }
+    // ---- every row: its step partials in step order, from +0
     for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
         const int lrow = i / M, m = i % M;
         const float *ps = part_s + ((size_t)lrow * I * M + m) * kParts;
@@ -1266,6 +1345,32 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const
         }
         a.out[(size_t)m * n + R0 + lrow] = kTwo ? silu_gate(g, u) : g;
     }
+}
+
+// The fold of the down stage split over k: y[m][row] = the row's step partials
+// part[s][m][row] summed in step order from +0. One thread per (m, row); its partials'
+// loads go out sixteen at a time (consecutive threads read consecutive rows).
+constexpr int kFoldThreads = 256;
+constexpr int kFoldLoads = 16;
+__global__ __launch_bounds__(kFoldThreads) void split_fold_kernel(const float *__restrict__ part,
+                                                                  int steps, int n, int mn,
+                                                                  float *__restrict__ y)
+{
+    const int i = blockIdx.x * kFoldThreads + threadIdx.x;   // = m * n + row
+    if (i >= mn)
+        return;
+    float acc = 0.0f;
+    for (int s0 = 0; s0 < steps; s0 += kFoldLoads) {
+        float v[kFoldLoads];
+#pragma unroll
+        for (int u = 0; u < kFoldLoads; ++u)
+            v[u] = s0 + u < steps ? part[(size_t)(s0 + u) * mn + i] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < kFoldLoads; ++u)
+            if (s0 + u < steps)
+                acc += v[u];
+    }
+    y[i] = acc;
 }
 
 // ------------------------------------------------------------------------------------
@@ -1841,6 +1946,71 @@ int launch_gemv_rotx(int mode, const tb_matrix *w0, const tb_matrix *w1, const f
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
+// The down stage split over k: gemv_mfma_pack_kernel<KS> on R row groups x I steps (R =
+// floor(CUs / I), at least 1, at most the row tiles), which rotates its step's blocks of h
+// and writes step partials to ws, then split_fold_kernel. TB_EUNSUPPORTED (nothing
+// launched) where the packed kernel's LDS plan does not fit.
+template <int FMT>
+RingFn split_pick_m(int m)
+{
+    static_assert(TB_SPLIT_MIN_ROWS >= 4, "built from 4 rows");
+    switch (m) {
+    case 4: return gemv_mfma_pack_kernel<4, FMT, kModeY, true>;
+    case 5: return gemv_mfma_pack_kernel<5, FMT, kModeY, true>;
+    case 6: return gemv_mfma_pack_kernel<6, FMT, kModeY, true>;
+    case 7: return gemv_mfma_pack_kernel<7, FMT, kModeY, true>;
+    case 8: return gemv_mfma_pack_kernel<8, FMT, kModeY, true>;
+    default: return nullptr;
+    }
+}
+int split_steps(const tb_matrix *w) { return (w->k / (w->fmt == TB_FMT_TERNARY2 ? 64 : 128) + 15) / 16; }
+size_t split_workspace_bytes(const tb_matrix *w, int m) { return (size_t)split_steps(w) * m * w->n * 4; }
+
+int launch_down_split(const tb_matrix *w, const float *h, int m, int8_t *qh, float *dqh, float *y,
+                      float *part, hipStream_t stream)
+{
+    DeviceInfo info;
+    int rc = device_info(&info);
+    if (rc)
+        return rc;
+    const bool tern = w->fmt == TB_FMT_TERNARY2;
+    const int I = split_steps(w), nb = w->k / kBlock;
+    const int T = (w->n + kRowsPerWave - 1) / kRowsPerWave;
+    const int R = std::max(1, std::min(info.cus / I, T));
+    if (nb % (tern ? 2 : 4) != 0)   // a lane's scale load holds whole block pairs / quads
+        return TB_EUNSUPPORTED;
+    const size_t rows_g = (size_t)((T + R - 1) / R) * kRowsPerWave + 16;   // + a 16-row tile's slack
+    const size_t lds = pack_lds(m, w->fmt, (tern ? 8 : 16) * kBlock, pack_threads(w->fmt) / 64).part +
+                       rows_g * m * 4;
+    if (lds > (size_t)info.lds_limit)
+        return TB_EUNSUPPORTED;
+    RingFn fn = tern ? split_pick_m<TB_FMT_TERNARY2>(m) : split_pick_m<TB_FMT_SIGN1>(m);
+    if (!fn)
+        return TB_EUNSUPPORTED;
+    if ((rc = raise_lds(reinterpret_cast<const void *>(fn), lds)))
+        return rc;
+    GemvArgs a = {};
+    a.codes0 = static_cast<const uint8_t *>(w->codes);
+    a.scales0 = w->scales;
+    a.n = w->n;
+    a.k = w->k;
+    a.x = h;
+    a.qx = qh;
+    a.dqx = dqh;
+    a.unit = dq_unit();
+    a.groups = R;
+    a.part = part;
+    a.codes_bytes = (uint32_t)codes_bytes(w);
+    a.scales_bytes = (uint32_t)((scales_bytes(w) + 3) & ~(size_t)3);
+    launch_ring(fn, I * R, lds, stream, a, h, pack_threads(w->fmt));
+    if (hipGetLastError() != hipSuccess)
+        return TB_EHIP;
+    const int mn = m * w->n;
+    hipLaunchKernelGGL(split_fold_kernel, dim3((mn + kFoldThreads - 1) / kFoldThreads),
+                       dim3(kFoldThreads), 0, stream, static_cast<const float *>(part), I, w->n, mn, y);
+    return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+}
+
 // The lookup-table GEMV (block sums when isum is given) over row-interleaved sign weights,
 // for 1 <= m <= 2 rows; one 16-wave workgroup per CU.
 int launch_lut(const tb_matrix *w, const int8_t *q, const float *dq, int m, float *y,
@@ -2215,6 +2385,53 @@ int tb_ffn_down_noalloc(const tb_matrix *wd, const float *h, int m, float *y, vo
     if ((rc = launch_rotquant(h, m, k, qh, dqh, s)))
         return rc;
     return launch_gemv(kModeY, wd, nullptr, qh, dqh, m, y, nullptr, s);
+}
+
+size_t tb_ffn_down_split_workspace_bytes(const tb_matrix *wd, int m)
+{
+    if (check_matrix(wd) || wd->fmt == TB_FMT_SIGN1_RI4 || check_rows(m))
+        return 0;
+    return split_workspace_bytes(wd, m);
+}
+
+int tb_ffn_down_split(const tb_matrix *wd, const float *h, int m, int8_t *qh, float *dqh, float *y,
+                      void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_matrix(wd);
+    if (rc)
+        return rc;
+    if (wd->fmt == TB_FMT_SIGN1_RI4)
+        return TB_EUNSUPPORTED;
+    if (check_rows(m) || !h || !qh || !dqh || !y || !ws)
+        return TB_EINVAL;
+    if (!aligned16(h) || !aligned16(qh) || !aligned16(dqh) || !aligned16(y) || !aligned16(ws))
+        return TB_EALIGN;
+    const size_t need = split_workspace_bytes(wd, m);
+    if (ws_bytes < need)
+        return TB_EINVAL;
+    const int k = wd->k;
+    const Range rh = range_of(h, (size_t)m * k * 4), rq = range_of(qh, (size_t)m * k),
+                rd = range_of(dqh, (size_t)m * (k / kBlock) * 4),
+                ry = range_of(y, (size_t)m * wd->n * 4), rw = range_of(ws, need),
+                rc_ = range_of(wd->codes, codes_bytes(wd)),
+                rs = range_of(wd->scales, scales_bytes(wd));
+    const Range outs[4] = {rq, rd, ry, rw};
+    const Range ins[3] = {rh, rc_, rs};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return TB_EINVAL;
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return TB_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (m >= TB_SPLIT_MIN_ROWS) {
+        rc = launch_down_split(wd, h, m, qh, dqh, y, static_cast<float *>(ws), s);
+        if (rc != TB_EUNSUPPORTED)
+            return rc;
+    }
+    return down_impl(wd, h, m, qh, dqh, y, stream, false);
 }
 
 static int block_sums_impl(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream,

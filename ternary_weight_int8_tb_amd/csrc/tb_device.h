@@ -520,6 +520,53 @@ __device__ __forceinline__ void store_block_step(uint8_t *act, int m, int b, int
                                L::offset(plane, m) + half * 8) = make_uint2(o[0], o[1]);
 }
 
+// One rotated-quantised block into the matrix-core layout of one step (the slots that
+// stage_unit_store_mfma writes from global memory): block b of the step, row m; the
+// 16-lane group holds the block as rotquant_regs returns it (lane L: codes 8L .. 8L+7).
+// The lanes exchange codes exactly as in store_block_step; only the slot differs.
+template <int M, int FMT>
+__device__ __forceinline__ void store_block_mfma(uint8_t *act, int m, int b, int lane16,
+                                                 const uint32_t (&pk)[2])
+{
+    uint32_t o[2];
+    size_t slot;
+    int half;
+    if (FMT == TB_FMT_TERNARY2) {
+        // unit u = lane16 / 2 of the block is unit g = 8 b + u of the step (chunk 2b + u / 4,
+        // part u % 4); its even lane writes words 0, 1 of the slot, the odd lane 2, 3
+        const uint32_t q0 = row_xor(pk[0], 1), q1 = row_xor(pk[1], 1);
+        const bool odd = lane16 & 1;
+        const uint32_t lo0 = odd ? q0 : pk[0], lo1 = odd ? q1 : pk[1];
+        const uint32_t hi0 = odd ? pk[0] : q0, hi1 = odd ? pk[1] : q1;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int e = (odd ? 2 : 0) + t;
+            o[t] = byte_at(lo0, e) | byte_at(lo1, e) << 8 | byte_at(hi0, e) << 16 | byte_at(hi1, e) << 24;
+        }
+        slot = (size_t)(8 * b + (lane16 >> 1)) * M + m;
+        half = lane16 & 1;
+    } else {
+        // unit u = lane16 / 4 is unit g = 4 b + u; lane i = lane16 % 4 writes words 2i, 2i+1
+        // of the unit's eight: slot 2g (words 0..3) or 2g + 1 (words 4..7)
+        const int i = lane16 & 3;
+        uint32_t src[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t w0 = quad_lane(pk[0], t), w1 = quad_lane(pk[1], t);
+            src[t] = (i >> 1) ? w1 : w0;
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int e = (2 * i + t) & 3;
+            o[t] = byte_at(src[0], e) | byte_at(src[1], e) << 8 | byte_at(src[2], e) << 16 |
+                   byte_at(src[3], e) << 24;
+        }
+        slot = (size_t)(2 * (4 * b + (lane16 >> 2)) + (i >> 1)) * M + m;
+        half = i & 1;
+    }
+    *reinterpret_cast<uint2 *>(act + slot * 16 + half * 8) = make_uint2(o[0], o[1]);
+}
+
 // Integer sums of one chunk against all M rows, step-major layout; `lds` is this lane's
 // slot address in the current step. Same arithmetic as chunk_sums.
 template <int M, int FMT, bool TWO>

@@ -55,9 +55,11 @@ ALGORITHMIC = {
     "gemv_ring_kernel<1, 0, 1, false>": 2 * MATRIX_BYTES + HIDDEN + NB_H * 4 + INTER * 4,
     "gemv_ring_kernel<1, 0, 0, false>": MATRIX_BYTES + INTER + NB_N * 4 + HIDDEN * 4,
     "ffn_layers_kernel<1, 0>": 32 * (3 * MATRIX_BYTES + 2 * HIDDEN * 4),
-    # M=8: matrix-core kernels with two blocks per MFMA
-    "gemv_mfma_pack_kernel<8, 0, 1>": 2 * MATRIX_BYTES + 8 * (HIDDEN + NB_H * 4 + INTER * 4),
-    "gemv_mfma_pack_kernel<8, 0, 0>": MATRIX_BYTES + 8 * (INTER + NB_N * 4 + HIDDEN * 4),
+    # M=8: matrix-core kernels with two blocks per MFMA; the down stage split over k reads
+    # h, writes rotquant(h) and its step partials (17 steps), which the fold reads
+    "gemv_mfma_pack_kernel<8, 0, 1, false>": 2 * MATRIX_BYTES + 8 * (HIDDEN + NB_H * 4 + INTER * 4),
+    "gemv_mfma_pack_kernel<8, 0, 0, true>": MATRIX_BYTES + 8 * (INTER * 4 + INTER + NB_N * 4)
+    + 17 * 8 * HIDDEN * 4,
     "ffn_layers_kernel<8, 0>": 32 * (3 * MATRIX_BYTES + 8 * 2 * HIDDEN * 4),
 }
 WHAT = {
@@ -66,8 +68,9 @@ WHAT = {
     "gemv_ring_kernel<1, 0, 1, false>": "tb_ffn_gateup_silu at M=1 (gate and up, 47,349,760 weight bytes)",
     "gemv_ring_kernel<1, 0, 0, false>": "the GEMV of tb_ffn_down at M=1 (23,674,880 weight bytes)",
     "ffn_layers_kernel<1, 0>": "one tb_ffn_layers launch of 32 layers at M=1",
-    "gemv_mfma_pack_kernel<8, 0, 1>": "tb_ffn_gateup_silu at M=8 (matrix cores)",
-    "gemv_mfma_pack_kernel<8, 0, 0>": "the GEMV of tb_ffn_down at M=8 (matrix cores)",
+    "gemv_mfma_pack_kernel<8, 0, 1, false>": "tb_ffn_gateup_silu at M=8 (matrix cores)",
+    "gemv_mfma_pack_kernel<8, 0, 0, true>": "the down GEMV of tb_ffn_down_split at M=8 (split over k, "
+                                            "rotation of h inside; matrix cores)",
     "ffn_layers_kernel<8, 0>": "one tb_ffn_layers launch of 32 layers at M=8",
 }
 
@@ -87,18 +90,19 @@ def read_stats(d: str):
 
 
 SIGN_MATRIX_BYTES = INTER * HIDDEN // 8 + INTER * NB_H * 2
-# the kernels of one layer of the separate-call stream (tb_ffn_gateup_silu_x, tb_ffn_down),
-# each with the weight bytes it streams: at M=1 the gate/up launch rotates x itself and the
-# down call is rotquant(h) + GEMV; at M=8 both calls are rotquant + GEMV
+# the kernels of one layer of the separate-call stream (tb_ffn_gateup_silu_x,
+# tb_ffn_down_split), each with the weight bytes it streams: at M=1 the gate/up launch
+# rotates x itself and the down call is rotquant(h) + GEMV; at M=8 gate/up is rotquant +
+# GEMV and the down call the split GEMV (rotation of h inside) + the fold
 STREAMS = {
     "ternary M=1": [("gemv_ring_kernel<1, 0, 1, true>", 2 * MATRIX_BYTES), ("rotquant_kernel", 0),
                     ("gemv_ring_kernel<1, 0, 0, false>", MATRIX_BYTES)],
-    "ternary M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 0, 1>", 2 * MATRIX_BYTES),
-                    ("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 0, 0>", MATRIX_BYTES)],
+    "ternary M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 0, 1, false>", 2 * MATRIX_BYTES),
+                    ("gemv_mfma_pack_kernel<8, 0, 0, true>", MATRIX_BYTES), ("split_fold_kernel", 0)],
     "sign M=1": [("gemv_ring_kernel<1, 1, 1, true>", 2 * SIGN_MATRIX_BYTES), ("rotquant_kernel", 0),
                  ("gemv_ring_kernel<1, 1, 0, false>", SIGN_MATRIX_BYTES)],
-    "sign M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 1, 1>", 2 * SIGN_MATRIX_BYTES),
-                 ("rotquant_kernel", 0), ("gemv_mfma_kernel<8, 1, 0>", SIGN_MATRIX_BYTES)],
+    "sign M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 1, 1, false>", 2 * SIGN_MATRIX_BYTES),
+                 ("gemv_mfma_pack_kernel<8, 1, 0, true>", SIGN_MATRIX_BYTES), ("split_fold_kernel", 0)],
 }
 
 
@@ -235,8 +239,8 @@ def write_sq(sq_dir: str, out: str):
             f"{100 * cb['SQ_ACTIVE_INST_VALU'] / wc:.0f} | {cb['SQ_LDS_BANK_CONFLICT'] / CUS:.0f} | "
             f"{cb['SQ_VALU_MFMA_BUSY_CYCLES'] / CUS:.0f} |")
     lines += ["", "Kernel names as in the kernel statistics: gemv_ring_kernel<M, FMT, MODE, ROTX> "
-              "(dot products), gemv_mfma_pack_kernel<M, FMT, MODE> (matrix cores), "
-              "ffn_layers_kernel<M, FMT> (32 layers per launch)."]
+              "(dot products), gemv_mfma_pack_kernel<M, FMT, MODE, KS> (matrix cores; KS true = "
+              "the down stage split over k), ffn_layers_kernel<M, FMT> (32 layers per launch)."]
     with open(os.path.join(out, "ffn64_stream_sq_counters.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {out}/ffn64_stream_sq_counters.md")
@@ -275,7 +279,9 @@ def main():
     lines += ["", "Template arguments: gemv_ring_kernel<M, FMT, MODE[, ROTX]>, FMT 0 = ternary, 1 = sign; "
               "MODE 0 = single GEMV (down), 1 = gate/up + SiLU, 2 = block-sum export; ROTX true = "
               "the fp32 input rotated and quantised inside the launch. "
-              "gemv_mfma_pack_kernel<M, FMT, MODE> (two blocks per MFMA, M <= 8) and "
+              "gemv_mfma_pack_kernel<M, FMT, MODE, KS> (two blocks per MFMA, M <= 8; KS true = the "
+              "down stage split over k, each workgroup one step of one row group, rotating its "
+              "blocks of h itself; split_fold_kernel adds its step partials) and "
               "gemv_mfma_kernel<M, FMT, MODE> (one block per MFMA, batches above 8 rows) run on the "
               "matrix cores (ternary: gate/up for M >= 5, a single GEMV for M >= 6; sign: gate/up "
               "for M >= 5, a single GEMV for M >= 7). "
@@ -291,8 +297,9 @@ def main():
     passes = stream_passes(a.stats)
     if passes:
         lines += ["", "Graph passes of the 64-layer separate-call stream in the same trace (per layer: "
-                  "tb_ffn_gateup_silu_x, then tb_ffn_down; at M=1 the gate/up launch rotates x "
-                  "itself, at M=8 each call is rotquant + GEMV). Durations and gaps are medians over "
+                  "tb_ffn_gateup_silu_x, then tb_ffn_down_split; at M=1 the gate/up launch rotates x "
+                  "itself and the down call is rotquant + GEMV, at M=8 gate/up is rotquant + GEMV and "
+                  "the down call the split GEMV + fold). Durations and gaps are medians over "
                   "every layer of every graph pass; a negative gap means the tracer stamped the next "
                   "start before the previous end. Kernel-only GB/s counts weight bytes over the "
                   "traced duration. The tracer's completion signal per dispatch lengthens passes, "

@@ -174,6 +174,37 @@ def test_down_validation(L):
     assert dn(wd, dqh=0x34000004) == tb.TB_EALIGN
 
 
+def test_down_split_validation(L):
+    wd = mat(n=5120, k=17408)
+    need = tb.tb_ffn_down_split_workspace_bytes(MatrixRef(wd), 8)
+    # float step partials [ceil(k/1024)][m][n] (ternary), [ceil(k/2048)][m][n] (sign)
+    assert need == 17 * 8 * 5120 * 4
+    assert tb.tb_ffn_down_split_workspace_bytes(MatrixRef(mat(n=5120, k=17408, fmt=1)), 3) == \
+        9 * 3 * 5120 * 4
+    assert tb.tb_ffn_down_split_workspace_bytes(MatrixRef(wd), 0) == 0
+    assert tb.tb_ffn_down_split_workspace_bytes(MatrixRef(wd), 9) == 0
+    assert tb.tb_ffn_down_split_workspace_bytes(MatrixRef(mat(fmt=2)), 1) == 0
+    WS = 0x40000000
+
+    def dn(w, h=0x20000000, qh=0x30000000, dqh=0x34000000, y=0x38000000, m=8, ws=WS, wsb=need):
+        return L.tb_ffn_down_split(ctypes.byref(w), h, m, qh, dqh, y, ws, wsb, None)
+    assert dn(wd, m=0) == tb.TB_EINVAL
+    assert dn(wd, m=9) == tb.TB_EINVAL
+    assert dn(wd, ws=0) == tb.TB_EINVAL
+    assert dn(wd, wsb=need - 4) == tb.TB_EINVAL                    # workspace too small
+    assert dn(wd, ws=WS + 4) == tb.TB_EALIGN
+    assert dn(wd, qh=0x20000000) == tb.TB_EINVAL                   # qh overlaps h
+    assert dn(wd, ws=0x38000000) == tb.TB_EINVAL                   # workspace overlaps y
+    assert dn(mat(n=5120, k=17408, fmt=2)) == tb.TB_EUNSUPPORTED
+
+
+class MatrixRef:
+    """A CMatrix in the shape the binding's workspace-size helper takes (.c)."""
+
+    def __init__(self, c):
+        self.c = c
+
+
 def test_block_sums_validation(L):
     assert L.tb_gemv_block_sums(ctypes.byref(mat()), ALIGNED3, 0, ALIGNED4, None) == tb.TB_EINVAL
     assert L.tb_gemv_block_sums(ctypes.byref(mat()), ALIGNED3, 1, 0, None) == tb.TB_EINVAL
@@ -260,6 +291,9 @@ def test_valid_calls_without_a_device_return_ehip(L):
                                   0x34000000, 0x38000000, None) == tb.TB_EHIP
     assert L.tb_gemv_ternary_x(ctypes.byref(w), 0x20000000, 1, 0x30000000, 0x34000000,
                                0x38000000, None) == tb.TB_EHIP
+    need = L.tb_ffn_down_split_workspace_bytes(ctypes.byref(w), 2)
+    assert L.tb_ffn_down_split(ctypes.byref(w), 0x20000000, 2, 0x30000000, 0x34000000, 0x38000000,
+                               0x40000000, need, None) == tb.TB_EHIP
 
 
 def test_batch_calls_validate_rows_and_arguments(L):

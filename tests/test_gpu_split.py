@@ -1,0 +1,146 @@
+"""tb_ffn_down_split on MI355X: the down stage split over k (matrix cores from 4 rows:
+a GEMV launch that rotates its own step of h, then a fold launch).
+
+qh and dqh must be bit-identical to the oracle's rotate-quantise of h. y must be
+bit-identical to tb_ffn_down on the same h: the rotation arithmetic, each row's step
+partial and the step-order fold are the same. y must also lie within 1e-4 * sum|terms|
+of the oracle's down GEMV.
+
+Cases:
+  * shapes: the FFN down shape (5120 x 17408); a partial last row tile (n = 1030); one
+    step (k = 512 ternary and sign, k = 128); twice the FFN k (34 steps of 7 row groups);
+    odd block counts (k = 2176, 640), which the split does not take (tb_ffn_down's route);
+  * both formats, 1..8 rows (1..3 rows: tb_ffn_down's route), zero and constant rows of h;
+  * two calls in a row on one workspace;
+  * a captured graph replayed three times, with eager work between the replays, every
+    replay checked.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ternary_weight_int8_tb_amd as tb
+from tests import bounds
+from tests import gpu_util as gu
+from ternary_weight_int8_tb_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TERN, SIGN = synth.FMT_TERNARY2, synth.FMT_SIGN1
+SHAPES = [(synth.HIDDEN, synth.INTER), (1028, 2176), (1030, 640), (1030, 1024), (96, 1280),
+          (64, 128), (256, 512), (260, 4096)]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.default()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert tb.tb_abi_version() == tb.ABI_VERSION
+    yield
+
+
+def hidden_rows(m, k, seed):
+    h = synth.normal_rows(m, k, seed, 0, synth.T_HIDDEN)
+    if m >= 3:
+        h[1] = 0.0       # dq = 0 blocks
+        h[2] = 0.75      # a constant row: one nonzero rotated element per block
+    if m >= 8:
+        h[7, :256] = 0.0  # zero blocks inside a row
+    return h
+
+
+def down_ref(wd, h):
+    m, k = h.shape
+    qh, dqh, y = gu.i8_out(m, k), gu.f32_out(m, k // 128), gu.f32_out(m, wd.n)
+    tb.tb_ffn_down(wd, h, qh, dqh, y)
+    return gu.host(qh).copy(), gu.host(dqh).copy(), gu.host(y).copy()
+
+
+def down_split(wd, h, ws):
+    m, k = h.shape
+    qh, dqh, y = gu.i8_out(m, k), gu.f32_out(m, k // 128), gu.f32_out(m, wd.n)
+    tb.tb_ffn_down_split(wd, h, qh, dqh, y, ws)
+    return gu.host(qh).copy(), gu.host(dqh).copy(), gu.host(y).copy()
+
+
+@pytest.mark.parametrize("fmt", [TERN, SIGN])
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_down_split_equals_down(fmt, n, k, m):
+    say(f"down split fmt={fmt} n={n} k={k} m={m}")
+    wd = tb.Matrix.upload(synth.matrix(fmt, n, k, 31, 0, synth.T_DOWN))
+    h = gu.dev(hidden_rows(m, k, 32 + m))
+    want = down_ref(wd, h)
+    ws = tb.tb_ffn_down_split_workspace(wd, m)
+    for rep in range(2):   # the second call reuses the workspace the first one wrote
+        got = down_split(wd, h, ws)
+        assert np.array_equal(got[0], want[0]), f"qh differs (call {rep})"
+        assert got[1].tobytes() == want[1].tobytes(), f"dqh differs (call {rep})"
+        bad = np.argwhere(got[2].view(np.uint32) != want[2].view(np.uint32))
+        assert bad.size == 0, f"y differs from tb_ffn_down at {bad[:5]} (call {rep})"
+
+
+@pytest.mark.parametrize("fmt", [TERN, SIGN])
+@pytest.mark.parametrize("n,k,m", [(synth.HIDDEN, synth.INTER, 8), (synth.HIDDEN, synth.INTER, 5),
+                                   (1030, 1024, 3)])
+def test_down_split_against_oracle(o, fmt, n, k, m):
+    say(f"down split vs oracle fmt={fmt} n={n} k={k} m={m}")
+    w = synth.matrix(fmt, n, k, 33, 0, synth.T_DOWN)
+    wd = tb.Matrix.upload(w)
+    h = hidden_rows(m, k, 34)
+    qh, dqh, y = down_split(wd, gu.dev(h), tb.tb_ffn_down_split_workspace(wd, m))
+    r = o.ffn_down(w, h)
+    assert np.array_equal(qh, r["qh"])
+    assert np.array_equal(dqh.view(np.uint32), r["dqh"].view(np.uint32))
+    ok, worst = bounds.gemv_ok(y, r["y"], r["sabs"])
+    say(f"  worst err / (1e-4 sum|tau|) = {worst:.3g}")
+    assert ok
+
+
+def test_down_split_many_steps():
+    # 34 steps: 7 row groups of 183 tiles (the largest group LDS plan), 238 workgroups
+    n, k = synth.HIDDEN, 2 * synth.INTER
+    wd = tb.Matrix.upload(synth.matrix(TERN, n, k, 35, 0, synth.T_DOWN))
+    h = gu.dev(hidden_rows(8, k, 36))
+    want = down_ref(wd, h)
+    got = down_split(wd, h, tb.tb_ffn_down_split_workspace(wd, 8))
+    assert np.array_equal(got[0], want[0])
+    assert got[2].tobytes() == want[2].tobytes()
+
+
+def test_down_split_graph_replays():
+    n, k, m = synth.HIDDEN, synth.INTER, 8
+    wd = tb.Matrix.upload(synth.matrix(TERN, n, k, 37, 0, synth.T_DOWN))
+    ws = tb.tb_ffn_down_split_workspace(wd, m)
+    h = gu.dev(hidden_rows(m, k, 38))
+    qh, dqh, y = gu.i8_out(m, k), gu.f32_out(m, k // 128), gu.f32_out(m, n)
+    tb.tb_ffn_down_split(wd, h, qh, dqh, y, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tb.tb_ffn_down_split(wd, h, qh, dqh, y, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        h.copy_(gu.dev(hidden_rows(m, k, 100 + rep)))   # eager work between the replays
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = down_ref(wd, h)
+        assert np.array_equal(gu.host(qh), want[0]), rep
+        assert gu.host(y).tobytes() == want[2].tobytes(), rep
