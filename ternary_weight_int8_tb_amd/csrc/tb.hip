@@ -1009,6 +1009,11 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const
     constexpr int kMatShift = kTwo ? 1 : 0;   // gate/up: item = ((tile, step), matrix)
     constexpr int kBps = kTern ? 8 : 16;      // blocks per step (256 code bytes per row)
     constexpr int kBpl = kBps / 4;            // blocks per scale load of one lane
+    // items in flight per wave: the split over k measured slower with 2 or 3 (the h loads
+    // queue behind the weight prologue of the whole chip, and more weight in flight delays
+    // them further: down stage at M = 4 / 6 / 8, µs per call, 13.12 / 13.77 / 14.28 at 1,
+    // 14.26 / 14.97 / 15.42 at 2, 15.48 / 16.26 / 16.68 at 3; rotating h before issuing the
+    // weight prologue: 13.95 / 14.98 / 14.75)
     constexpr int kDepth = kPackDepth;
     constexpr int kThreads = pack_threads(FMT), kWaves = kThreads / 64;
     constexpr int kScratch = pack_scratch_bytes(FMT);   // per wave: scales [block][row], uint16
