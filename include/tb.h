@@ -246,9 +246,12 @@ int tb_gemv_block_sums_batch(const tb_matrix *w, const int8_t *q, int m, int32_t
  * partials in step order. That is the fold of tb_ffn_down, so y, qh and dqh are
  * bit-identical to tb_ffn_down on the same inputs. What it saves is the
  * separate rotation launch and the staging of all of rotquant(h) in every CU.
- * For 1 to 3 rows (where the split measured slower), or where its plan does
- * not apply (k/128 not a multiple of 2 (ternary) or 4 (sign)), the call runs
- * tb_ffn_down and leaves ws untouched.
+ * It takes the split from 4 rows while tb_ffn_down's GEMV would run on the
+ * dot-product kernel (ternary up to 5 rows, sign up to 6), and for more rows only
+ * when k >= 8192, where the unsplit kernel stages m * k codes in every CU (the
+ * down stage of the FFN). Otherwise (where the split measured slower), or where
+ * its plan does not apply (k/128 not a multiple of 2 (ternary) or 4 (sign)), the
+ * call runs tb_ffn_down and leaves ws untouched.
  *   h    float [m][wd->k]     input
  *   qh   int8  [m][wd->k]     output: rotquant(h) codes
  *   dqh  float [m][wd->k/128] output: their block scales

@@ -130,12 +130,17 @@ constexpr int kPackDepth = TB_PACK_DEPTH;
 #ifndef TB_MFMA_MIN_ROWS_SIGN_ONE
 #define TB_MFMA_MIN_ROWS_SIGN_ONE 7
 #endif
-// Rows from which tb_ffn_down_split takes the split over k (below: tb_ffn_down's route).
-// Down stage of the 64-layer stream (5120 x 17408, ternary), µs per call, tb_ffn_down
-// against the split: M=2 10.66 / 12.64, M=4 13.88 / 12.94, M=6 16.36 / 13.83, M=8 17.33 /
-// 14.52 (sign M=8 18.49 / 15.88).
+// When tb_ffn_down_split takes the split over k (otherwise tb_ffn_down's route): from
+// TB_SPLIT_MIN_ROWS rows while the unsplit GEMV runs on the dot-product kernel, and on the
+// matrix cores only for k >= TB_SPLIT_MIN_K, where the unsplit kernel stages M * k codes in
+// every CU. µs per call, unsplit against split, ternary: 5120 x 17408 M=2 10.66 / 12.64, M=4
+// 13.88 / 12.94, M=6 16.36 / 13.83, M=8 17.33 / 14.52 (sign M=8 18.49 / 15.88); 9216 x 5120
+// M=4 11.09 / 10.28, M=8 10.82 / 11.43; 5120 x 4096 M=4 8.55 / 8.52, M=8 9.06 / 9.60.
 #ifndef TB_SPLIT_MIN_ROWS
 #define TB_SPLIT_MIN_ROWS 4
+#endif
+#ifndef TB_SPLIT_MIN_K
+#define TB_SPLIT_MIN_K 8192
 #endif
 constexpr int mfma_min_rows(bool ternary, bool gateup)
 {
@@ -2431,7 +2436,8 @@ int tb_ffn_down_split(const tb_matrix *wd, const float *h, int m, int8_t *qh, fl
             if (overlaps(outs[i], outs[j]))
                 return TB_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (m >= TB_SPLIT_MIN_ROWS) {
+    const bool tern = wd->fmt == TB_FMT_TERNARY2;
+    if (m >= TB_SPLIT_MIN_ROWS && (m < mfma_min_rows(tern, false) || k >= TB_SPLIT_MIN_K)) {
         rc = launch_down_split(wd, h, m, qh, dqh, y, static_cast<float *>(ws), s);
         if (rc != TB_EUNSUPPORTED)
             return rc;

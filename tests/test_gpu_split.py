@@ -1,5 +1,7 @@
-"""tb_ffn_down_split on MI355X: the down stage split over k (matrix cores from 4 rows:
-a GEMV launch that rotates its own step of h, then a fold launch).
+"""tb_ffn_down_split on MI355X: the down stage split over k (matrix cores: a GEMV launch
+whose workgroups rotate their own step of h, then a fold launch). It is taken from 4 rows
+while the unsplit GEMV would use the dot-product kernel, and on the matrix cores for
+k >= 8192; elsewhere the call runs tb_ffn_down.
 
 qh and dqh must be bit-identical to the oracle's rotate-quantise of h. y must be
 bit-identical to tb_ffn_down on the same h: the rotation arithmetic, each row's step
@@ -7,10 +9,11 @@ partial and the step-order fold are the same. y must also lie within 1e-4 * sum|
 of the oracle's down GEMV.
 
 Cases:
-  * shapes: the FFN down shape (5120 x 17408); a partial last row tile (n = 1030); one
-    step (k = 512 ternary and sign, k = 128); twice the FFN k (34 steps of 7 row groups);
-    odd block counts (k = 2176, 640), which the split does not take (tb_ffn_down's route);
-  * both formats, 1..8 rows (1..3 rows: tb_ffn_down's route), zero and constant rows of h;
+  * shapes: the FFN down shape (5120 x 17408); k >= 8192 with a partial 16-row tile
+    (n = 1030, 100); k below 8192 (taken up to 5 rows: n = 1030, k = 1024; one step,
+    k = 512); twice the FFN k (34 steps of 7 row groups); odd block counts (k = 2176,
+    640, 128), which the split does not take;
+  * both formats, 1..8 rows, zero and constant rows of h;
   * two calls in a row on one workspace;
   * a captured graph replayed three times, with eager work between the replays, every
     replay checked.
@@ -34,7 +37,7 @@ pytestmark = pytest.mark.gpu
 
 TERN, SIGN = synth.FMT_TERNARY2, synth.FMT_SIGN1
 SHAPES = [(synth.HIDDEN, synth.INTER), (1028, 2176), (1030, 640), (1030, 1024), (96, 1280),
-          (64, 128), (256, 512), (260, 4096)]
+          (64, 128), (256, 512), (260, 4096), (1030, 10240), (100, 8192)]
 
 
 def say(*a):
@@ -97,7 +100,7 @@ def test_down_split_equals_down(fmt, n, k, m):
 
 @pytest.mark.parametrize("fmt", [TERN, SIGN])
 @pytest.mark.parametrize("n,k,m", [(synth.HIDDEN, synth.INTER, 8), (synth.HIDDEN, synth.INTER, 5),
-                                   (1030, 1024, 3)])
+                                   (1030, 10240, 6), (1030, 1024, 4)])
 def test_down_split_against_oracle(o, fmt, n, k, m):
     say(f"down split vs oracle fmt={fmt} n={n} k={k} m={m}")
     w = synth.matrix(fmt, n, k, 33, 0, synth.T_DOWN)
