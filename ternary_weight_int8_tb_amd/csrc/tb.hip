@@ -30,6 +30,12 @@
 //     gemv_mfma_pack_kernel (two blocks per MFMA) up to 8 rows, gemv_mfma_kernel (16-row
 //     tiles) for batches of 9 to 16 rows. The block-sum export follows the gate/up
 //     threshold, so it runs the matrix-core integer core at every M where production does.
+//   * The down stage can also run split over k (tb_ffn_down_split, from 4 rows where it
+//     measures faster): each workgroup of gemv_mfma_pack_kernel<..., KS> takes one step of
+//     one row group, rotates its own blocks of h, and writes step partials that
+//     split_fold_kernel adds in step order, so the results are the same bits.
+//   * The streaming kernels take their leading arguments as scalars that the build
+//     preloads into SGPRs, so a launch's first loads wait for no argument fetch.
 //   * 1-bit weights in the row-interleaved layout take a lookup-table GEMV (tb_lut.h).
 //   * No floating-point atomics.
 #include <hip/hip_runtime.h>
