@@ -6,8 +6,8 @@
  * the FFN from a ternary copy through a dp4a GEMV" (sparkinfer PR #1154),
  * Summary and commit message:
  *   - decode reads each FFN's stored ternary weight blocks;
- *   - a Hadamard rotation emits one int8 copy of the activation, which gate
- *     and up share;
+ *   - the activation is rotated by a Hadamard transform and quantised to
+ *     int8 once; the gate and up matrices both read that one int8 vector;
  *   - an integer dot-product GEMV folds the per-block scales into each
  *     block's integer sum;
  *   - a packed step of up to 8 rows gives every row exactly the bytes it gets
