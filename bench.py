@@ -98,8 +98,8 @@ class Stream64:
         self.qh = torch.empty(L, m, n, dtype=torch.int8, device=dev)
         self.dqh = torch.empty(L, m, n // 128, dtype=torch.float32, device=dev)
         self.y = torch.empty(L, m, k, dtype=torch.float32, device=dev)
-        # the step partials of tb_ffn_down_split (one workspace: the calls are in order)
-        self.ws = None if batch else tb.tb_ffn_down_split_workspace(layers_dev[0][2], m)
+        # the step partials of tb_ffn_down_split(_batch) (one workspace: the calls are in order)
+        self.ws = tb.tb_ffn_down_split_workspace(layers_dev[0][2], m, batch=batch)
 
     def step(self):
         tb = self.tb
@@ -107,7 +107,7 @@ class Stream64:
             for l, (wg, wu, wd) in enumerate(self.layers):
                 tb.tb_rotate_quant_i8_batch(self.x[l], self.q[l], self.dq[l])
                 tb.tb_ffn_gateup_silu_batch(wg, wu, self.q[l], self.dq[l], self.h[l])
-                tb.tb_ffn_down_batch(wd, self.h[l], self.qh[l], self.dqh[l], self.y[l])
+                tb.tb_ffn_down_split_batch(wd, self.h[l], self.qh[l], self.dqh[l], self.y[l], self.ws)
             return
         for l, (wg, wu, wd) in enumerate(self.layers):
             tb.tb_ffn_gateup_silu_x(wg, wu, self.x[l], self.q[l], self.dq[l], self.h[l])
@@ -767,7 +767,8 @@ def main():
             if m == 16:
                 got16 = gotb
             del sb, gotb
-            res_big[f"m{m}"] = dict(summary(tb_s, pb), entry_point="tb_*_batch calls, hip graph replay")
+            res_big[f"m{m}"] = dict(summary(tb_s, pb), entry_point="tb_rotate_quant_i8_batch + tb_ffn_gateup_silu_batch + "
+                                "tb_ffn_down_split_batch per layer, hip graph replay")
             log(f"M={m} (batch calls): {tb_s / args.layers * 1e6:.2f} us/layer, "
                 f"{step_bytes / tb_s / 1e9:.1f} GB/s")
 

@@ -22,7 +22,7 @@ TB_FMT_TERNARY2, TB_FMT_SIGN1, TB_FMT_SIGN1_RI4 = 0, 1, 2
 BLOCK = 128
 MAX_ROWS = 8
 MAX_BATCH_ROWS = 32
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 # every symbol include/tb.h declares
 ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_gemv_ternary_x", "tb_ffn_gateup_silu",
@@ -32,6 +32,7 @@ ABI_SYMBOLS = ("tb_rotate_quant_i8", "tb_gemv_ternary", "tb_gemv_ternary_x", "tb
                "tb_ffn_gateup_silu_batch", "tb_ffn_down_batch", "tb_gemv_block_sums_batch",
                "tb_ffn_down_noalloc", "tb_sign_interleave",
                "tb_ffn_down_split", "tb_ffn_down_split_workspace_bytes",
+               "tb_ffn_down_split_batch", "tb_ffn_down_split_batch_workspace_bytes",
                "tb_ffn_workspace_bytes", "tb_ffn_workspace_init",
                "tb_ffn_layers", "tb_ffn_workspace_error", "tb_status_str", "tb_abi_version")
 TB_FFN_CHAIN = 1
@@ -72,6 +73,8 @@ _SIGS = {
     "tb_sign_interleave": ([_MP, _P, _P, _P], _I),
     "tb_ffn_down_split": ([_MP, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
     "tb_ffn_down_split_workspace_bytes": ([_MP, _I], ctypes.c_size_t),
+    "tb_ffn_down_split_batch": ([_MP, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "tb_ffn_down_split_batch_workspace_bytes": ([_MP, _I], ctypes.c_size_t),
     "tb_ffn_workspace_bytes": ([_I, _I, _I], ctypes.c_size_t),
     "tb_ffn_workspace_init": ([_P, ctypes.c_size_t, ctypes.c_uint32, _P], _I),
     "tb_ffn_layers": ([ctypes.POINTER(CFfnWeights), _I, _P, _I, ctypes.c_uint, _P, ctypes.c_size_t,
@@ -248,18 +251,32 @@ def tb_ffn_down_split_workspace_bytes(wd: Matrix, m: int) -> int:
     return int(lib().tb_ffn_down_split_workspace_bytes(ctypes.byref(wd.c), int(m)))
 
 
-def tb_ffn_down_split_workspace(wd: Matrix, m: int):
-    """A new tb_ffn_down_split workspace for m rows (uint8 device tensor; no initialisation)."""
+def tb_ffn_down_split_batch_workspace_bytes(wd: Matrix, m: int) -> int:
+    """Bytes of device workspace tb_ffn_down_split_batch needs for m rows (0 for bad arguments)."""
+    return int(lib().tb_ffn_down_split_batch_workspace_bytes(ctypes.byref(wd.c), int(m)))
+
+
+def tb_ffn_down_split_workspace(wd: Matrix, m: int, batch: bool = False):
+    """A new tb_ffn_down_split (batch: tb_ffn_down_split_batch) workspace for m rows
+    (uint8 device tensor; no initialisation)."""
     import torch
-    nbytes = tb_ffn_down_split_workspace_bytes(wd, m)
+    name = "tb_ffn_down_split_batch_workspace_bytes" if batch else "tb_ffn_down_split_workspace_bytes"
+    nbytes = int(getattr(lib(), name)(ctypes.byref(wd.c), int(m)))
     if nbytes == 0:
-        raise TbError("tb_ffn_down_split_workspace_bytes", TB_EINVAL)
+        raise TbError(name, TB_EINVAL)
     return torch.empty(nbytes, dtype=torch.uint8, device=wd.codes.device)
 
 
 def tb_ffn_down_split(wd: Matrix, h, qh, dqh, y, ws, stream=None) -> None:
     """tb_ffn_down with a workspace for the split over k; y, qh, dqh are bit-identical."""
     _call("tb_ffn_down_split", ctypes.byref(wd.c), h.data_ptr(), _rows(h), qh.data_ptr(),
+          dqh.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+          _stream(stream))
+
+
+def tb_ffn_down_split_batch(wd: Matrix, h, qh, dqh, y, ws, stream=None) -> None:
+    """tb_ffn_down_split for 1 ... 32 rows; each row bit-identical to tb_ffn_down alone."""
+    _call("tb_ffn_down_split_batch", ctypes.byref(wd.c), h.data_ptr(), _rows(h), qh.data_ptr(),
           dqh.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
           _stream(stream))
 

@@ -187,10 +187,12 @@ struct GemvArgs {
     int8_t *qx;
     float *dqx;
     float unit;              // fp32(1 / (127 sqrt(128)))
-    // down stage split over k (gemv_mfma_pack_kernel with KS): row groups, and the step
-    // partials [I][M][n] it writes (x holds h; qx, dqx receive rotquant(h))
+    // down stage split over k (gemv_mfma_pack_kernel and gemv_mfma_kernel with KS): row
+    // groups, and the step partials it writes, part[s][m][row] with part_rows rows m per
+    // step (x holds h; qx, dqx receive rotquant(h))
     int groups;
     float *part;
+    int part_rows;
 };
 
 // The arguments of a streaming kernel from its leading scalar arguments (preloaded into
@@ -699,9 +701,11 @@ __host__ __device__ constexpr int pack_threads(int fmt)
 //   * Sign runs 12 waves per CU: its 16-block steps need more than the 128 registers a
 //     wave has at 16.
 // ------------------------------------------------------------------------------------
-template <int M, int FMT, int MODE>
+template <int M, int FMT, int MODE, bool KS = false>
 __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a)
 {
+    static_assert(M >= 1 && M <= 16, "one 16-column B operand");
+    static_assert(!KS || MODE == kModeY, "the split over k is the down stage");
     extern __shared__ __align__(16) uint8_t lds[];
     using L = StepLayout<M, FMT>;
     constexpr bool kTern = FMT == TB_FMT_TERNARY2;
@@ -715,9 +719,15 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
     constexpr bool kIsum = MODE == kModeIsum;
 
     const int k = a.k, n = a.n, nb = k / kBlock;
-    const int C = k / Fmt<FMT>::kWeightsPerChunk, I = (C + kChunkLanes - 1) / kChunkLanes;
+    const int C = k / Fmt<FMT>::kWeightsPerChunk, Ik = (C + kChunkLanes - 1) / kChunkLanes;
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-    const int G = gridDim.x, c = blockIdx.x;
+    // KS: workgroup (g, s) of a.groups row groups x Ik steps covers step s of group g;
+    // otherwise workgroup c covers all steps of share c of the grid
+    const int G = KS ? a.groups : (int)gridDim.x;
+    const int c = KS ? (int)blockIdx.x / Ik : (int)blockIdx.x;
+    const int s0 = KS ? (int)blockIdx.x - c * Ik : 0;   // the step of KS items
+    const int I = KS ? 1 : Ik;                          // steps per tile in this workgroup
+    const int nbl = KS ? kBps : nb;                     // blocks of the staged activation
     const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
     const int R0 = part_lo(T, G, c) * kRowsPerWave;
     const int R1 = min(part_lo(T, G, c + 1) * kRowsPerWave, n);
@@ -726,15 +736,15 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
 
     uint8_t *act = lds;
     float *dq_s = reinterpret_cast<float *>(lds + (size_t)I * L::kStepBytes);
-    int *qsum_s = reinterpret_cast<int *>(dq_s + (size_t)(nb + kBps) * M);
-    int *ctr_s = qsum_s + (kTern ? 0 : (nb + kBps) * M);
+    int *qsum_s = reinterpret_cast<int *>(dq_s + (size_t)(nbl + kBps) * M);
+    int *ctr_s = qsum_s + (kTern ? 0 : (nbl + kBps) * M);
     float *part_s = reinterpret_cast<float *>(ctr_s + 4);   // [row - R0][step][m][part]
 
     const __amdgpu_buffer_rsrc_t rout =
         buffer_rsrc(a.isum, kIsum ? (uint32_t)((size_t)M * n * nb * 4) : 0u);
     if (tid == 0)
         *ctr_s = kWaves;   // wave w starts with item w
-    if (!kTern)
+    if (!kTern && !KS)
         for (int i = tid; i < (nb + kBps) * M; i += kThreads)
             qsum_s[i] = 0;
     __syncthreads();
@@ -768,12 +778,13 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
             mat = idx & (kTwo ? 1 : 0);
             rit[d] = mat << 30 | gtile << 16 | gstep;
             const int row0 = R0 + gtile * 16;
-            so = row0 * (int)row_bytes + gstep * 256;
-            sso = (row0 * nb + gstep * kBps) * 2;
-            nbk = min(kBps, nb - gstep * kBps);   // blocks of this step inside the row
+            const int wstep = s0 + gstep;            // the step in the weight rows
+            so = row0 * (int)row_bytes + wstep * 256;
+            sso = (row0 * nb + wstep * kBps) * 2;
+            nbk = min(kBps, nb - wstep * kBps);   // blocks of this step inside the row
             if (row0 + li < R1) {
                 off = lane_off;
-                soff = (!kIsum && gstep * kBps + lg * kBpl < nb) ? lane_soff : kOutOfRange;
+                soff = (!kIsum && wstep * kBps + lg * kBpl < nb) ? lane_soff : kOutOfRange;
             }
             int v = 0;
             if (lane == 0)
@@ -796,11 +807,64 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
         }
     };
 
-    stage_activation<M, FMT, MODE, kThreads, true>(a, act, dq_s, qsum_s, [&]() {
+    if constexpr (KS) {
+        // h loads of step s0's blocks first, then the weight prologue, then the rotation
+        // (as in gemv_mfma_pack_kernel: the two kernels share the LDS slot layout)
+        constexpr int kGroups16 = kThreads / 16;
+        constexpr int kRounds = (M * kBps + kGroups16 - 1) / kGroups16;
+        const int l16 = tid & 15, grp = tid >> 4;
+        const int b0 = s0 * kBps, nbs = min(kBps, nb - b0), Z = M * nbs;
+        float hv[kRounds][8];
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int z = grp + r * kGroups16;
+            if (z < Z) {
+                const int m = z / nbs, bl = z - m * nbs;
+                const float *src = a.x + (size_t)m * k + (size_t)(b0 + bl) * kBlock + l16 * 8;
+                const float4 lo = *reinterpret_cast<const float4 *>(src);
+                const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+                hv[r][0] = lo.x; hv[r][1] = lo.y; hv[r][2] = lo.z; hv[r][3] = lo.w;
+                hv[r][4] = hi.x; hv[r][5] = hi.y; hv[r][6] = hi.z; hv[r][7] = hi.w;
+            }
+        }
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
             issue(d);
-    });
+        for (int i = Z + tid; i < 2 * kBps * M; i += kThreads) {   // [block][m] past the step
+            dq_s[i] = 0.0f;
+            if (!kTern)
+                qsum_s[i] = 0;
+        }
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int z = grp + r * kGroups16;
+            if (z < Z) {   // (a 16-lane group takes or skips a block as a whole)
+                const int m = z / nbs, bl = z - m * nbs;
+                uint32_t pk[2];
+                float dq;
+                int qsum;
+                rotquant_regs(hv[r], l16, a.unit, pk, dq, qsum);
+                store_block_mfma<M, FMT>(act, m, bl, l16, pk);
+                if (l16 == 0) {
+                    dq_s[bl * M + m] = dq;
+                    if (!kTern)
+                        qsum_s[bl * M + m] = qsum;
+                }
+                if (c == 0) {   // row group 0 writes rotquant(h)
+                    *reinterpret_cast<uint2 *>(a.qx + (size_t)m * k + (size_t)(b0 + bl) * kBlock + l16 * 8) =
+                        make_uint2(pk[0], pk[1]);
+                    if (l16 == 0)
+                        a.dqx[(size_t)m * nb + b0 + bl] = dq;
+                }
+            }
+        }
+    } else {
+        stage_activation<M, FMT, MODE, kThreads, true>(a, act, dq_s, qsum_s, [&]() {
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d)
+                issue(d);
+        });
+    }
     __syncthreads();
 
     // ---- compute side
@@ -937,8 +1001,15 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
 
     if (kIsum)
         return;
-    // ---- every row: its step partials in step order, from +0
     __syncthreads();
+    if constexpr (KS) {   // the step partials [s0][m][row], summed by the fold launch
+        for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
+            const int lrow = i / M, m = i % M;
+            a.part[((size_t)s0 * a.part_rows + m) * n + R0 + lrow] = part_s[(size_t)lrow * M + m];
+        }
+        return;
+    }
+    // ---- every row: its step partials in step order, from +0
     for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
         const int lrow = i / M, m = i % M;
         const float *ps = part_s + ((size_t)lrow * I * M + m) * kParts;
@@ -1345,7 +1416,7 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const
     if constexpr (KS) {   // the step partials [s0][m][row], summed by the fold launch
         for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
             const int lrow = i / M, m = i % M;
-            a.part[((size_t)s0 * M + m) * n + R0 + lrow] = part_s[(size_t)lrow * M + m];
+            a.part[((size_t)s0 * a.part_rows + m) * n + R0 + lrow] = part_s[(size_t)lrow * M + m];
         }
         return;
     }
@@ -1962,6 +2033,15 @@ int launch_gemv_rotx(int mode, const tb_matrix *w0, const tb_matrix *w1, const f
     return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
 }
 
+// y[m][n] = the step partials part[I][m][n] summed in step order (split_fold_kernel).
+int launch_split_fold(const float *part, int I, int n, int m, float *y, hipStream_t stream)
+{
+    const int mn = m * n;
+    hipLaunchKernelGGL(split_fold_kernel, dim3((mn + kFoldThreads - 1) / kFoldThreads),
+                       dim3(kFoldThreads), 0, stream, part, I, n, mn, y);
+    return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+}
+
 // The down stage split over k: gemv_mfma_pack_kernel<KS> on R row groups x I steps (R =
 // floor(CUs / I), at least 1, at most the row tiles), which rotates its step's blocks of h
 // and writes step partials to ws, then split_fold_kernel. TB_EUNSUPPORTED (nothing
@@ -2016,15 +2096,93 @@ int launch_down_split(const tb_matrix *w, const float *h, int m, int8_t *qh, flo
     a.unit = dq_unit();
     a.groups = R;
     a.part = part;
+    a.part_rows = m;
     a.codes_bytes = (uint32_t)codes_bytes(w);
     a.scales_bytes = (uint32_t)((scales_bytes(w) + 3) & ~(size_t)3);
     launch_ring(fn, I * R, lds, stream, a, h, pack_threads(w->fmt));
     if (hipGetLastError() != hipSuccess)
         return TB_EHIP;
-    const int mn = m * w->n;
-    hipLaunchKernelGGL(split_fold_kernel, dim3((mn + kFoldThreads - 1) / kFoldThreads),
-                       dim3(kFoldThreads), 0, stream, static_cast<const float *>(part), I, w->n, mn, y);
-    return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+    return launch_split_fold(part, I, w->n, m, y, stream);
+}
+
+// The same split for batches of 9 ... 32 rows: balanced chunks of 8 ... 16 rows, each one
+// launch of gemv_mfma_kernel<KS> (one block per MFMA, all 16 B columns live) that writes
+// its rows' step partials into the batch's [I][m][n] workspace, then one fold launch for
+// the whole batch. Each chunk stages one step of its rows (16 KB of codes at 16 ternary
+// rows) where the unsplit 16-row kernel would stage all of k. TB_EUNSUPPORTED (nothing
+// launched) where a chunk's LDS does not fit.
+template <int FMT>
+GemvFn split_wide_pick_m(int m)
+{
+    switch (m) {
+    case 8: return gemv_mfma_kernel<8, FMT, kModeY, true>;   // (17 rows: 8 + 9)
+    case 9: return gemv_mfma_kernel<9, FMT, kModeY, true>;
+    case 10: return gemv_mfma_kernel<10, FMT, kModeY, true>;
+    case 11: return gemv_mfma_kernel<11, FMT, kModeY, true>;
+    case 12: return gemv_mfma_kernel<12, FMT, kModeY, true>;
+    case 13: return gemv_mfma_kernel<13, FMT, kModeY, true>;
+    case 14: return gemv_mfma_kernel<14, FMT, kModeY, true>;
+    case 15: return gemv_mfma_kernel<15, FMT, kModeY, true>;
+    case 16: return gemv_mfma_kernel<16, FMT, kModeY, true>;
+    default: return nullptr;
+    }
+}
+int launch_down_split_wide(const tb_matrix *w, const float *h, int m, int8_t *qh, float *dqh,
+                           float *y, float *part, hipStream_t stream)
+{
+    DeviceInfo info;
+    int rc = device_info(&info);
+    if (rc)
+        return rc;
+    if (m <= TB_MAX_ROWS || m > 2 * kMaxWideRows)
+        return TB_EUNSUPPORTED;
+    const bool tern = w->fmt == TB_FMT_TERNARY2;
+    const int I = split_steps(w), k = w->k, nb = k / kBlock, bps = tern ? 8 : 16;
+    const int T = (w->n + kRowsPerWave - 1) / kRowsPerWave;
+    const int R = std::max(1, std::min(info.cus / I, T));
+    if (nb % (tern ? 2 : 4) != 0)   // a lane's scale load holds whole block pairs / quads
+        return TB_EUNSUPPORTED;
+    const int chunks = (m + kMaxWideRows - 1) / kMaxWideRows;
+    const size_t rows_g = (size_t)((T + R - 1) / R) * kRowsPerWave;
+    // (the kernel's carve-up: one step of codes, the step's block terms [2 steps][m] (and
+    // code sums for sign), the item counter, the step partials of the group's rows)
+    auto lds_of = [&](int mc) {
+        return (size_t)(tern ? 1024 : 2048) * mc + (size_t)2 * bps * mc * 4 * (tern ? 1 : 2) + 16 +
+               rows_g * mc * 4;
+    };
+    GemvFn fns[2] = {nullptr, nullptr};
+    size_t ldss[2] = {0, 0};
+    for (int i = 0; i < chunks; ++i) {
+        const int mc = (m * (i + 1)) / chunks - (m * i) / chunks;
+        fns[i] = tern ? split_wide_pick_m<TB_FMT_TERNARY2>(mc) : split_wide_pick_m<TB_FMT_SIGN1>(mc);
+        ldss[i] = lds_of(mc);
+        if (!fns[i] || ldss[i] > (size_t)info.lds_limit)
+            return TB_EUNSUPPORTED;
+    }
+    for (int i = 0, r0 = 0; i < chunks; ++i) {
+        const int mc = (m * (i + 1)) / chunks - (m * i) / chunks;
+        if ((rc = raise_lds(reinterpret_cast<const void *>(fns[i]), ldss[i])))
+            return rc;
+        GemvArgs a = {};
+        a.codes0 = static_cast<const uint8_t *>(w->codes);
+        a.scales0 = w->scales;
+        a.n = w->n;
+        a.k = k;
+        a.x = h + (size_t)r0 * k;
+        a.qx = qh + (size_t)r0 * k;
+        a.dqx = dqh + (size_t)r0 * nb;
+        a.unit = dq_unit();
+        a.groups = R;
+        a.part = part + (size_t)r0 * w->n;
+        a.part_rows = m;
+        a.codes_bytes = (uint32_t)codes_bytes(w);
+        a.scales_bytes = (uint32_t)((scales_bytes(w) + 3) & ~(size_t)3);
+        hipLaunchKernelGGL(fns[i], dim3(I * R), dim3(mfma_threads(w->fmt)), ldss[i], stream, a);
+        if (hipGetLastError() != hipSuccess)
+            return TB_EHIP;
+        r0 += mc;
+    }
+    return launch_split_fold(part, I, w->n, m, y, stream);
 }
 
 // The lookup-table GEMV (block sums when isum is given) over row-interleaved sign weights,
@@ -2403,22 +2561,33 @@ int tb_ffn_down_noalloc(const tb_matrix *wd, const float *h, int m, float *y, vo
     return launch_gemv(kModeY, wd, nullptr, qh, dqh, m, y, nullptr, s);
 }
 
-size_t tb_ffn_down_split_workspace_bytes(const tb_matrix *wd, int m)
+static size_t down_split_workspace(const tb_matrix *wd, int m, bool batch)
 {
-    if (check_matrix(wd) || wd->fmt == TB_FMT_SIGN1_RI4 || check_rows(m))
+    if (check_matrix(wd) || wd->fmt == TB_FMT_SIGN1_RI4 ||
+        check_rows(m, batch ? TB_MAX_BATCH_ROWS : TB_MAX_ROWS))
         return 0;
     return split_workspace_bytes(wd, m);
 }
 
-int tb_ffn_down_split(const tb_matrix *wd, const float *h, int m, int8_t *qh, float *dqh, float *y,
-                      void *ws, size_t ws_bytes, void *stream)
+size_t tb_ffn_down_split_workspace_bytes(const tb_matrix *wd, int m)
+{
+    return down_split_workspace(wd, m, false);
+}
+
+size_t tb_ffn_down_split_batch_workspace_bytes(const tb_matrix *wd, int m)
+{
+    return down_split_workspace(wd, m, true);
+}
+
+static int down_split_impl(const tb_matrix *wd, const float *h, int m, int8_t *qh, float *dqh,
+                           float *y, void *ws, size_t ws_bytes, void *stream, bool batch)
 {
     int rc = check_matrix(wd);
     if (rc)
         return rc;
     if (wd->fmt == TB_FMT_SIGN1_RI4)
         return TB_EUNSUPPORTED;
-    if (check_rows(m) || !h || !qh || !dqh || !y || !ws)
+    if (check_rows(m, batch ? TB_MAX_BATCH_ROWS : TB_MAX_ROWS) || !h || !qh || !dqh || !y || !ws)
         return TB_EINVAL;
     if (!aligned16(h) || !aligned16(qh) || !aligned16(dqh) || !aligned16(y) || !aligned16(ws))
         return TB_EALIGN;
@@ -2443,12 +2612,32 @@ int tb_ffn_down_split(const tb_matrix *wd, const float *h, int m, int8_t *qh, fl
                 return TB_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool tern = wd->fmt == TB_FMT_TERNARY2;
+    if (m > TB_MAX_ROWS) {
+        if (k >= TB_SPLIT_MIN_K) {
+            rc = launch_down_split_wide(wd, h, m, qh, dqh, y, static_cast<float *>(ws), s);
+            if (rc != TB_EUNSUPPORTED)
+                return rc;
+        }
+        return down_impl(wd, h, m, qh, dqh, y, stream, true);
+    }
     if (m >= TB_SPLIT_MIN_ROWS && (m < mfma_min_rows(tern, false) || k >= TB_SPLIT_MIN_K)) {
         rc = launch_down_split(wd, h, m, qh, dqh, y, static_cast<float *>(ws), s);
         if (rc != TB_EUNSUPPORTED)
             return rc;
     }
     return down_impl(wd, h, m, qh, dqh, y, stream, false);
+}
+
+int tb_ffn_down_split(const tb_matrix *wd, const float *h, int m, int8_t *qh, float *dqh, float *y,
+                      void *ws, size_t ws_bytes, void *stream)
+{
+    return down_split_impl(wd, h, m, qh, dqh, y, ws, ws_bytes, stream, false);
+}
+
+int tb_ffn_down_split_batch(const tb_matrix *wd, const float *h, int m, int8_t *qh, float *dqh,
+                            float *y, void *ws, size_t ws_bytes, void *stream)
+{
+    return down_split_impl(wd, h, m, qh, dqh, y, ws, ws_bytes, stream, true);
 }
 
 static int block_sums_impl(const tb_matrix *w, const int8_t *q, int m, int32_t *isum, void *stream,

@@ -198,6 +198,29 @@ def test_down_split_validation(L):
     assert dn(mat(n=5120, k=17408, fmt=2)) == tb.TB_EUNSUPPORTED
 
 
+def test_down_split_batch_validation(L):
+    wd = mat(n=5120, k=17408)
+    need = tb.tb_ffn_down_split_batch_workspace_bytes(MatrixRef(wd), 32)
+    assert need == 17 * 32 * 5120 * 4
+    assert tb.tb_ffn_down_split_batch_workspace_bytes(MatrixRef(wd), 8) == \
+        tb.tb_ffn_down_split_workspace_bytes(MatrixRef(wd), 8)
+    assert tb.tb_ffn_down_split_batch_workspace_bytes(MatrixRef(wd), 0) == 0
+    assert tb.tb_ffn_down_split_batch_workspace_bytes(MatrixRef(wd), 33) == 0
+    assert tb.tb_ffn_down_split_batch_workspace_bytes(MatrixRef(mat(fmt=2)), 16) == 0
+    WS = 0x40000000
+
+    def dn(w, h=0x20000000, qh=0x30000000, dqh=0x34000000, y=0x38000000, m=32, ws=WS, wsb=need):
+        return L.tb_ffn_down_split_batch(ctypes.byref(w), h, m, qh, dqh, y, ws, wsb, None)
+    assert dn(wd, m=0) == tb.TB_EINVAL
+    assert dn(wd, m=33) == tb.TB_EINVAL
+    assert dn(wd, ws=0) == tb.TB_EINVAL
+    assert dn(wd, wsb=need - 4) == tb.TB_EINVAL                    # workspace too small
+    assert dn(wd, ws=WS + 4) == tb.TB_EALIGN
+    assert dn(wd, qh=0x20000000) == tb.TB_EINVAL                   # qh overlaps h
+    assert dn(wd, ws=0x38000000) == tb.TB_EINVAL                   # workspace overlaps y
+    assert dn(mat(n=5120, k=17408, fmt=2)) == tb.TB_EUNSUPPORTED
+
+
 class MatrixRef:
     """A CMatrix in the shape the binding's workspace-size helper takes (.c)."""
 

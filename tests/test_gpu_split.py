@@ -17,6 +17,13 @@ Cases:
   * two calls in a row on one workspace;
   * a captured graph replayed three times, with eager work between the replays, every
     replay checked.
+
+tb_ffn_down_split_batch (1 ... 32 rows): from 9 rows and k >= 8192 the batch runs as
+chunks of 8 ... 16 rows on the 16-column matrix-core kernel split over k, with one fold
+launch. Every row's y, qh and dqh must be bit-identical to tb_ffn_down_batch (whose rows
+are bit-identical to each row run alone, tests/test_gpu_batch.py) and, for sampled rows,
+to tb_ffn_down on the row alone; y within the oracle's bound at the FFN shape for 16
+and 32 rows. Shapes below k = 8192 and odd block counts take tb_ffn_down_batch.
 """
 
 from __future__ import annotations
@@ -145,5 +152,96 @@ def test_down_split_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         want = down_ref(wd, h)
+        assert np.array_equal(gu.host(qh), want[0]), rep
+        assert gu.host(y).tobytes() == want[2].tobytes(), rep
+
+
+def down_batch_ref(wd, h):
+    m, k = h.shape
+    qh, dqh, y = gu.i8_out(m, k), gu.f32_out(m, k // 128), gu.f32_out(m, wd.n)
+    tb.tb_ffn_down_batch(wd, h, qh, dqh, y)
+    return gu.host(qh).copy(), gu.host(dqh).copy(), gu.host(y).copy()
+
+
+def down_split_batch(wd, h, ws):
+    m, k = h.shape
+    qh, dqh, y = gu.i8_out(m, k), gu.f32_out(m, k // 128), gu.f32_out(m, wd.n)
+    tb.tb_ffn_down_split_batch(wd, h, qh, dqh, y, ws)
+    return gu.host(qh).copy(), gu.host(dqh).copy(), gu.host(y).copy()
+
+
+BATCH_SHAPES = [(synth.HIDDEN, synth.INTER), (1030, 10240), (100, 8192), (1030, 1024),
+                (260, 4096), (1028, 2176)]
+
+
+@pytest.mark.parametrize("fmt", [TERN, SIGN])
+@pytest.mark.parametrize("n,k", BATCH_SHAPES)
+@pytest.mark.parametrize("m", [1, 8, 9, 12, 16, 17, 24, 32])
+def test_down_split_batch_equals_batch(fmt, n, k, m):
+    say(f"down split batch fmt={fmt} n={n} k={k} m={m}")
+    wd = tb.Matrix.upload(synth.matrix(fmt, n, k, 41, 0, synth.T_DOWN))
+    hh = hidden_rows(m, k, 42 + m)
+    h = gu.dev(hh)
+    want = down_batch_ref(wd, h)
+    ws = tb.tb_ffn_down_split_workspace(wd, m, batch=True)
+    assert ws.numel() == tb.tb_ffn_down_split_batch_workspace_bytes(wd, m)
+    for rep in range(2):   # the second call reuses the workspace the first one wrote
+        got = down_split_batch(wd, h, ws)
+        assert np.array_equal(got[0], want[0]), f"qh differs (call {rep})"
+        assert got[1].tobytes() == want[1].tobytes(), f"dqh differs (call {rep})"
+        bad = np.argwhere(got[2].view(np.uint32) != want[2].view(np.uint32))
+        assert bad.size == 0, f"y differs from tb_ffn_down_batch at {bad[:5]} (call {rep})"
+    for r in sorted({0, m // 2, m - 1}):   # rows alone through the 1 ... 8-row call
+        alone = down_ref(wd, gu.dev(hh[r:r + 1]))
+        assert np.array_equal(got[0][r], alone[0][0]), f"qh row {r} differs from the row alone"
+        assert got[2][r].tobytes() == alone[2][0].tobytes(), f"y row {r} differs from the row alone"
+
+
+@pytest.mark.parametrize("fmt,m", [(TERN, 16), (TERN, 32), (SIGN, 16), (SIGN, 32)])
+def test_down_split_batch_against_oracle(o, fmt, m):
+    n, k = synth.HIDDEN, synth.INTER
+    say(f"down split batch vs oracle fmt={fmt} m={m}")
+    w = synth.matrix(fmt, n, k, 43, 0, synth.T_DOWN)
+    wd = tb.Matrix.upload(w)
+    h = hidden_rows(m, k, 44)
+    qh, dqh, y = down_split_batch(wd, gu.dev(h), tb.tb_ffn_down_split_workspace(wd, m, batch=True))
+    r = o.ffn_down(w, h)
+    assert np.array_equal(qh, r["qh"])
+    assert np.array_equal(dqh.view(np.uint32), r["dqh"].view(np.uint32))
+    ok, worst = bounds.gemv_ok(y, r["y"], r["sabs"])
+    say(f"  worst err / (1e-4 sum|tau|) = {worst:.3g}")
+    assert ok
+
+
+def test_down_split_batch_many_steps():
+    # 34 steps: 7 row groups, 238 workgroups per chunk, two chunks of 10 rows
+    n, k, m = synth.HIDDEN, 2 * synth.INTER, 20
+    wd = tb.Matrix.upload(synth.matrix(TERN, n, k, 45, 0, synth.T_DOWN))
+    h = gu.dev(hidden_rows(m, k, 46))
+    want = down_batch_ref(wd, h)
+    got = down_split_batch(wd, h, tb.tb_ffn_down_split_workspace(wd, m, batch=True))
+    assert np.array_equal(got[0], want[0])
+    assert got[2].tobytes() == want[2].tobytes()
+
+
+def test_down_split_batch_graph_replays():
+    n, k, m = synth.HIDDEN, synth.INTER, 32
+    wd = tb.Matrix.upload(synth.matrix(TERN, n, k, 47, 0, synth.T_DOWN))
+    ws = tb.tb_ffn_down_split_workspace(wd, m, batch=True)
+    h = gu.dev(hidden_rows(m, k, 48))
+    qh, dqh, y = gu.i8_out(m, k), gu.f32_out(m, k // 128), gu.f32_out(m, n)
+    tb.tb_ffn_down_split_batch(wd, h, qh, dqh, y, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tb.tb_ffn_down_split_batch(wd, h, qh, dqh, y, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        h.copy_(gu.dev(hidden_rows(m, k, 200 + rep)))   # eager work between the replays
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = down_batch_ref(wd, h)
         assert np.array_equal(gu.host(qh), want[0]), rep
         assert gu.host(y).tobytes() == want[2].tobytes(), rep
