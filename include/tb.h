@@ -270,18 +270,18 @@ size_t tb_ffn_down_split_workspace_bytes(const tb_matrix *wd, int m);
 
 /* tb_ffn_down_split for 1 <= m <= TB_MAX_BATCH_ROWS (32) rows, the down stage
  * of the batches above 8 rows (see tb_ffn_down_batch for the pages' passages).
- * Up to 8 rows it is tb_ffn_down_split. From 9 rows, when k >= 8192, the
- * batch runs as balanced chunks of 8 to 16 rows on the matrix-core kernel with
- * all 16 B columns live, each chunk one launch split over k as above (one step
- * of one row group per workgroup, h rotated and quantised inside), all chunks
- * writing the batch's step partials, then one fold launch for the batch. So
- * the down weights are read once per 16 rows, where tb_ffn_down_batch, whose
- * 16-row kernel cannot stage k = 17408 codes per row in a CU, reads them once
- * per 8 rows. Otherwise (k < 8192, or the plan does not fit the device) the
- * call runs tb_ffn_down_batch and leaves ws untouched. Arguments, layouts,
- * outputs, workspace and errors are those of tb_ffn_down_split with m up to
- * 32; each row's y, qh and dqh are bit-identical to tb_ffn_down on that row
- * alone. */
+ * Up to 8 rows it is tb_ffn_down_split. From 9 rows, when k >= 8192, it runs on
+ * the matrix-core kernel with all 16 B columns live, split over k as above (one
+ * step of one row group per workgroup, h rotated and quantised inside), then one
+ * fold launch for the batch. Ternary: one launch for the whole batch, whose B
+ * operands hold 16 rows, or 32 in two column groups sharing each decoded weight
+ * operand, so the down weights are read once. Sign: balanced chunks of up to 16
+ * rows, one launch each. tb_ffn_down_batch, whose 16-row kernel cannot stage
+ * k = 17408 codes per row in a CU, reads them once per 8 rows. Otherwise (k < 8192,
+ * or the plan does not fit the device) the call runs tb_ffn_down_batch and leaves
+ * ws untouched. Arguments, layouts, outputs, workspace and errors are those of
+ * tb_ffn_down_split with m up to 32; each row's y, qh and dqh are bit-identical
+ * to tb_ffn_down on that row alone. */
 int tb_ffn_down_split_batch(const tb_matrix *wd, const float *h, int m, int8_t *qh, float *dqh,
                             float *y, void *ws, size_t ws_bytes, void *stream);
 /* Workspace bytes of tb_ffn_down_split_batch for m rows (1 ... 32); 0 for

@@ -33,7 +33,10 @@
 //   * The down stage can also run split over k (tb_ffn_down_split, from 4 rows where it
 //     measures faster): each workgroup of gemv_mfma_pack_kernel<..., KS> takes one step of
 //     one row group, rotates its own blocks of h, and writes step partials that
-//     split_fold_kernel adds in step order, so the results are the same bits.
+//     split_fold_kernel adds in step order, so the results are the same bits. Batches of
+//     9 to 32 rows (tb_ffn_down_split_batch) split the same way on gemv_mfma_kernel<..., KS>,
+//     whose B operands hold 16 rows, or 32 in two column groups sharing each decoded weight
+//     operand (ternary), so the down weights are read once per batch.
 //   * The streaming kernels take their leading arguments as scalars that the build
 //     preloads into SGPRs, so a launch's first loads wait for no argument fetch.
 //   * 1-bit weights in the row-interleaved layout take a lookup-table GEMV (tb_lut.h).
@@ -193,6 +196,7 @@ struct GemvArgs {
     int groups;
     float *part;
     int part_rows;
+    int act_rows;            // rows of h (gemv_mfma_kernel with KS: 1 <= act_rows <= M)
 };
 
 // The arguments of a streaming kernel from its leading scalar arguments (preloaded into
@@ -657,8 +661,12 @@ __global__ __launch_bounds__(kRingThreads) void gemv_ring_kernel(const void *p0,
 
 // Threads per workgroup of gemv_mfma_kernel: 16 waves for ternary; 12 for sign, whose
 // 16-block steps need 156-160 registers, more than the 128 a wave has at 16 waves per CU
-// (sign down at M=8: 17.7-17.8 µs at 12 waves against 18.9-19.1 at 8).
-__host__ __device__ constexpr int mfma_threads(int fmt) { return fmt == TB_FMT_TERNARY2 ? 1024 : 768; }
+// (sign down at M=8: 17.7-17.8 µs at 12 waves against 18.9-19.1 at 8). With two 16-column
+// groups (M > 16) each wave holds twice the sums and trees: 12 and 8 waves.
+__host__ __device__ constexpr int mfma_threads(int fmt, int m = 16)
+{
+    return fmt == TB_FMT_TERNARY2 ? (m > 16 ? 768 : 1024) : (m > 16 ? 512 : 768);
+}
 // Threads per workgroup of gemv_mfma_pack_kernel.
 #ifndef TB_PACK_TERN_WAVES
 #define TB_PACK_TERN_WAVES 16
@@ -702,9 +710,10 @@ __host__ __device__ constexpr int pack_threads(int fmt)
 //     wave has at 16.
 // ------------------------------------------------------------------------------------
 template <int M, int FMT, int MODE, bool KS = false>
-__global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a)
+__global__ __launch_bounds__(mfma_threads(FMT, M)) void gemv_mfma_kernel(GemvArgs a)
 {
-    static_assert(M >= 1 && M <= 16, "one 16-column B operand");
+    static_assert(M >= 1 && M <= 32, "one or two 16-column B operands");
+    static_assert(M <= 16 || KS, "two column groups only split over k (one step staged)");
     static_assert(!KS || MODE == kModeY, "the split over k is the down stage");
     extern __shared__ __align__(16) uint8_t lds[];
     using L = StepLayout<M, FMT>;
@@ -715,8 +724,9 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
     constexpr int kBps = kTern ? 8 : 16;      // blocks per step (256 code bytes per row)
     constexpr int kBpl = kBps / 4;            // blocks per 16-byte load of the 4 lanes of a row
     constexpr int kDepth = kMfmaDepth;
-    constexpr int kThreads = mfma_threads(FMT), kWaves = kThreads / 64;
+    constexpr int kThreads = mfma_threads(FMT, M), kWaves = kThreads / 64;
     constexpr bool kIsum = MODE == kModeIsum;
+    constexpr int kCG = (M + 15) / 16;   // 16-column groups of D (activation rows 16 cg + i)
 
     const int k = a.k, n = a.n, nb = k / kBlock;
     const int C = k / Fmt<FMT>::kWeightsPerChunk, Ik = (C + kChunkLanes - 1) / kChunkLanes;
@@ -728,6 +738,7 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
     const int s0 = KS ? (int)blockIdx.x - c * Ik : 0;   // the step of KS items
     const int I = KS ? 1 : Ik;                          // steps per tile in this workgroup
     const int nbl = KS ? kBps : nb;                     // blocks of the staged activation
+    const int rows = KS ? a.act_rows : M;               // live activation rows (<= M)
     const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
     const int R0 = part_lo(T, G, c) * kRowsPerWave;
     const int R1 = min(part_lo(T, G, c + 1) * kRowsPerWave, n);
@@ -808,55 +819,64 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
     };
 
     if constexpr (KS) {
-        // h loads of step s0's blocks first, then the weight prologue, then the rotation
-        // (as in gemv_mfma_pack_kernel: the two kernels share the LDS slot layout)
+        // h loads of step s0's blocks first (up to kPre rounds), then the weight prologue,
+        // then the rotation (as in gemv_mfma_pack_kernel: the two kernels share the LDS slot
+        // layout); later rounds load after the prologue
         constexpr int kGroups16 = kThreads / 16;
         constexpr int kRounds = (M * kBps + kGroups16 - 1) / kGroups16;
+        constexpr int kPre = kRounds < 6 ? kRounds : 6;
         const int l16 = tid & 15, grp = tid >> 4;
-        const int b0 = s0 * kBps, nbs = min(kBps, nb - b0), Z = M * nbs;
-        float hv[kRounds][8];
-#pragma unroll
-        for (int r = 0; r < kRounds; ++r) {
-            const int z = grp + r * kGroups16;
-            if (z < Z) {
-                const int m = z / nbs, bl = z - m * nbs;
-                const float *src = a.x + (size_t)m * k + (size_t)(b0 + bl) * kBlock + l16 * 8;
-                const float4 lo = *reinterpret_cast<const float4 *>(src);
-                const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
-                hv[r][0] = lo.x; hv[r][1] = lo.y; hv[r][2] = lo.z; hv[r][3] = lo.w;
-                hv[r][4] = hi.x; hv[r][5] = hi.y; hv[r][6] = hi.z; hv[r][7] = hi.w;
+        const int b0 = s0 * kBps, nbs = min(kBps, nb - b0), Z = rows * nbs;
+        auto hload = [&](float (&v)[8], int z) {
+            const int m = z / nbs, bl = z - m * nbs;
+            const float *src = a.x + (size_t)m * k + (size_t)(b0 + bl) * kBlock + l16 * 8;
+            const float4 lo = *reinterpret_cast<const float4 *>(src);
+            const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        };
+        auto hblock = [&](float (&v)[8], int z) {   // (a 16-lane group takes a block whole)
+            const int m = z / nbs, bl = z - m * nbs;
+            uint32_t pk[2];
+            float dq;
+            int qsum;
+            rotquant_regs(v, l16, a.unit, pk, dq, qsum);
+            store_block_mfma<M, FMT>(act, m, bl, l16, pk);
+            if (l16 == 0) {
+                dq_s[bl * M + m] = dq;
+                if (!kTern)
+                    qsum_s[bl * M + m] = qsum;
             }
-        }
+            if (c == 0) {   // row group 0 writes rotquant(h)
+                *reinterpret_cast<uint2 *>(a.qx + (size_t)m * k + (size_t)(b0 + bl) * kBlock + l16 * 8) =
+                    make_uint2(pk[0], pk[1]);
+                if (l16 == 0)
+                    a.dqx[(size_t)m * nb + b0 + bl] = dq;
+            }
+        };
+        float hv[kPre][8];
+#pragma unroll
+        for (int r = 0; r < kPre; ++r)
+            if (grp + r * kGroups16 < Z)
+                hload(hv[r], grp + r * kGroups16);
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
             issue(d);
-        for (int i = Z + tid; i < 2 * kBps * M; i += kThreads) {   // [block][m] past the step
+        // block terms [block][m] of the blocks past the step's end read zero (their codes
+        // are zero too); rows past act_rows feed only D columns that are never stored
+        for (int i = nbs * M + tid; i < 2 * kBps * M; i += kThreads) {
             dq_s[i] = 0.0f;
             if (!kTern)
                 qsum_s[i] = 0;
         }
 #pragma unroll
-        for (int r = 0; r < kRounds; ++r) {
-            const int z = grp + r * kGroups16;
-            if (z < Z) {   // (a 16-lane group takes or skips a block as a whole)
-                const int m = z / nbs, bl = z - m * nbs;
-                uint32_t pk[2];
-                float dq;
-                int qsum;
-                rotquant_regs(hv[r], l16, a.unit, pk, dq, qsum);
-                store_block_mfma<M, FMT>(act, m, bl, l16, pk);
-                if (l16 == 0) {
-                    dq_s[bl * M + m] = dq;
-                    if (!kTern)
-                        qsum_s[bl * M + m] = qsum;
-                }
-                if (c == 0) {   // row group 0 writes rotquant(h)
-                    *reinterpret_cast<uint2 *>(a.qx + (size_t)m * k + (size_t)(b0 + bl) * kBlock + l16 * 8) =
-                        make_uint2(pk[0], pk[1]);
-                    if (l16 == 0)
-                        a.dqx[(size_t)m * nb + b0 + bl] = dq;
-                }
-            }
+        for (int r = 0; r < kPre; ++r)
+            if (grp + r * kGroups16 < Z)
+                hblock(hv[r], grp + r * kGroups16);
+        for (int z = grp + kPre * kGroups16; z < Z; z += kGroups16) {
+            float v[8];
+            hload(v, z);
+            hblock(v, z);
         }
     } else {
         stage_activation<M, FMT, MODE, kThreads, true>(a, act, dq_s, qsum_s, [&]() {
@@ -868,7 +888,11 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
     __syncthreads();
 
     // ---- compute side
-    const int mB = li < M ? li : M - 1;   // activation row of this lane's B and D column
+    // activation row of this lane's B and D column in column group cg: 16 cg + li
+    int mB[kCG];
+#pragma unroll
+    for (int cg = 0; cg < kCG; ++cg)
+        mB[cg] = 16 * cg + li < M ? 16 * cg + li : M - 1;
     auto consume = [&](int d) {
         const int mat = rit[d] >> 30, tile = (rit[d] >> 16) & 0x3fff, step = rit[d] & 0xffff;
         // The lane groups exchange code words so that each MFMA sees one block.
@@ -892,14 +916,13 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
                 rc[d][q] = make_uint4(t0.x, t0.y, t1.x, t1.y);
             }
         }
-        const uint8_t *sact = act + (size_t)step * L::kStepBytes +
-                              (kTern ? (((lg & 1) * 4 + 2 * (lg >> 1)) * M + mB) * 16
-                                     : ((2 * lg) * M + mB) * 16);
+        const uint8_t *sbase = act + (size_t)step * L::kStepBytes +
+                               (kTern ? (((lg & 1) * 4 + 2 * (lg >> 1)) * M) * 16 : ((2 * lg) * M) * 16);
         // The step tree in the order row_tree produces (each level adds lane L - off), taken
         // as a balanced tree over the blocks in the order 0, kBps - 1, .., 1:
         // ((t0 + t7) + (t6 + t5)) + ((t4 + t3) + (t2 + t1)) for ternary, the same over 16
         // blocks for sign. lv holds the pending left subtrees per level.
-        float lv[4][4], tot[4];
+        float lv[kCG][4][4], tot[kCG][4];
         // byte address of this lane's row group for ds_bpermute, made opaque here so the
         // compiler forms the per-block addresses in the loop instead of keeping all of them
         // live across it (which spills)
@@ -909,10 +932,6 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
         for (int o = 0; o < kBps; ++o) {
             const int kb = o == 0 ? 0 : kBps - o;
             const int blk = step * kBps + kb;
-            const uint8_t *bp = sact + kb * (kTern ? 2 * 4 : 8) * M * 16;
-            const v4i b0 = *reinterpret_cast<const v4i *>(bp);
-            const v4i b1 = *reinterpret_cast<const v4i *>(bp + M * 16);
-            const float dqv = dq_s[blk * M + mB];
             uint32_t w[8];
             if (kTern) {
                 const uint4 cw = rc[d][kb >> 1];
@@ -927,20 +946,34 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
             }
             const v4i a0 = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
             const v4i a1 = {(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-            v4i acc = {0, 0, 0, 0};
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
-            const int qs = kTern ? 0 : qsum_s[blk * M + mB];
+            // both formats: a block's B groups are 8 slots of M rows apart
+            v4i acc[kCG];
+            float dqv[kCG];
+            int qs[kCG];
+#pragma unroll
+            for (int cg = 0; cg < kCG; ++cg) {
+                const uint8_t *bp = sbase + (size_t)mB[cg] * 16 + (size_t)kb * 8 * M * 16;
+                const v4i b0 = *reinterpret_cast<const v4i *>(bp);
+                const v4i b1 = *reinterpret_cast<const v4i *>(bp + M * 16);
+                acc[cg] = v4i{0, 0, 0, 0};
+                acc[cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc[cg], 0, 0, 0);
+                acc[cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc[cg], 0, 0, 0);
+                dqv[cg] = dq_s[blk * M + mB[cg]];
+                qs[cg] = kTern ? 0 : qsum_s[blk * M + mB[cg]];
+            }
             if constexpr (kIsum) {
                 // the block-sum export: D's exact sums, before any scale, for the live
-                // activation rows (lanes li < M) of rows inside this workgroup's range
+                // activation rows of rows inside this workgroup's range
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = R0 + tile * 16 + 4 * lg + r;
-                    const bool wr = li < M && row < R1 && blk < nb;
-                    const int v = kTern ? acc[r] : 2 * acc[r] - qs;
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        (uint32_t)v, rout, wr ? (uint32_t)(((li * n + row) * nb + blk) * 4) : kOutOfRange, 0, 0);
+                for (int cg = 0; cg < kCG; ++cg) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = R0 + tile * 16 + 4 * lg + r, mr = 16 * cg + li;
+                        const bool wr = mr < M && row < R1 && blk < nb;
+                        const int v = kTern ? acc[cg][r] : 2 * acc[cg][r] - qs[cg];
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            (uint32_t)v, rout, wr ? (uint32_t)(((mr * n + row) * nb + blk) * 4) : kOutOfRange, 0, 0);
+                    }
                 }
                 if (!kTern)
                     __builtin_amdgcn_sched_barrier(0);
@@ -953,34 +986,43 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
                 const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(
                     pbase + (16 * (kb / kBpl) + r) * 4, (int)word);
                 const float sv = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(sw, (kb & 1) * 16, 16));
-                const int isum = kTern ? acc[r] : 2 * acc[r] - qs;
-                float v = (sv * dqv) * (float)isum;
-                bool done = false;
 #pragma unroll
-                for (int l = 0; l < 4; ++l) {
-                    if (!done) {
-                        if ((o >> l) & 1) {
-                            v = lv[r][l] + v;
-                        } else {
-                            lv[r][l] = v;
-                            done = true;
+                for (int cg = 0; cg < kCG; ++cg) {
+                    const int isum = kTern ? acc[cg][r] : 2 * acc[cg][r] - qs[cg];
+                    float v = (sv * dqv[cg]) * (float)isum;
+                    bool done = false;
+#pragma unroll
+                    for (int l = 0; l < 4; ++l) {
+                        if (!done) {
+                            if ((o >> l) & 1) {
+                                v = lv[cg][r][l] + v;
+                            } else {
+                                lv[cg][r][l] = v;
+                                done = true;
+                            }
                         }
                     }
+                    if (o == kBps - 1)
+                        tot[cg][r] = v;
                 }
-                if (o == kBps - 1)
-                    tot[r] = v;
             }
             // sign: one block at a time (hoisting the LDS reads of the 16 blocks of a step
             // spills)
             if (!kTern)
                 __builtin_amdgcn_sched_barrier(0);
         }
-        if (!kIsum && li < M) {
+        if (!kIsum) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int lrow = tile * 16 + 4 * lg + r;   // row - R0
-                if (R0 + lrow < R1)
-                    part_s[((size_t)(lrow * I + step) * M + li) * kParts + mat] = tot[r];
+            for (int cg = 0; cg < kCG; ++cg) {
+                const int mr = 16 * cg + li;
+                if (mr < rows) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int lrow = tile * 16 + 4 * lg + r;   // row - R0
+                        if (R0 + lrow < R1)
+                            part_s[((size_t)(lrow * I + step) * M + mr) * kParts + mat] = tot[cg][r];
+                    }
+                }
             }
         }
     };
@@ -1003,8 +1045,8 @@ __global__ __launch_bounds__(mfma_threads(FMT)) void gemv_mfma_kernel(GemvArgs a
         return;
     __syncthreads();
     if constexpr (KS) {   // the step partials [s0][m][row], summed by the fold launch
-        for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
-            const int lrow = i / M, m = i % M;
+        for (int i = tid; i < (R1 - R0) * rows; i += kThreads) {
+            const int lrow = i / rows, m = i - lrow * rows;
             a.part[((size_t)s0 * a.part_rows + m) * n + R0 + lrow] = part_s[(size_t)lrow * M + m];
         }
         return;
@@ -2105,27 +2147,23 @@ int launch_down_split(const tb_matrix *w, const float *h, int m, int8_t *qh, flo
     return launch_split_fold(part, I, w->n, m, y, stream);
 }
 
-// The same split for batches of 9 ... 32 rows: balanced chunks of 8 ... 16 rows, each one
-// launch of gemv_mfma_kernel<KS> (one block per MFMA, all 16 B columns live) that writes
-// its rows' step partials into the batch's [I][m][n] workspace, then one fold launch for
-// the whole batch. Each chunk stages one step of its rows (16 KB of codes at 16 ternary
-// rows) where the unsplit 16-row kernel would stage all of k. TB_EUNSUPPORTED (nothing
-// launched) where a chunk's LDS does not fit.
+// The same split for batches of 9 ... 32 rows on gemv_mfma_kernel<KS> (one block per
+// MFMA, all 16 B columns live). Ternary: one launch whose B operands hold up to 16 rows
+// (one column group) or up to 32 (two, sharing each decoded A operand), so the down
+// weights are read once per batch. Sign: balanced chunks of up to 16 rows (two column
+// groups over its 16-block steps need more registers than 8 waves have: 120 bytes of
+// spills per lane), each chunk one launch. Each workgroup stages one step of its rows
+// (16 KB of codes at 16 ternary rows) where the unsplit 16-row kernel would stage all of
+// k; the kernel is built for 16 or 32 rows and takes the row count at run time. Every
+// launch writes its rows' step partials into the batch's [I][m][n] workspace; then one
+// fold launch. TB_EUNSUPPORTED (nothing launched) where the LDS plan does not fit.
 template <int FMT>
-GemvFn split_wide_pick_m(int m)
+GemvFn split_wide_pick(int mcap)
 {
-    switch (m) {
-    case 8: return gemv_mfma_kernel<8, FMT, kModeY, true>;   // (17 rows: 8 + 9)
-    case 9: return gemv_mfma_kernel<9, FMT, kModeY, true>;
-    case 10: return gemv_mfma_kernel<10, FMT, kModeY, true>;
-    case 11: return gemv_mfma_kernel<11, FMT, kModeY, true>;
-    case 12: return gemv_mfma_kernel<12, FMT, kModeY, true>;
-    case 13: return gemv_mfma_kernel<13, FMT, kModeY, true>;
-    case 14: return gemv_mfma_kernel<14, FMT, kModeY, true>;
-    case 15: return gemv_mfma_kernel<15, FMT, kModeY, true>;
-    case 16: return gemv_mfma_kernel<16, FMT, kModeY, true>;
-    default: return nullptr;
-    }
+    if constexpr (FMT == TB_FMT_TERNARY2)
+        if (mcap > 16)
+            return gemv_mfma_kernel<32, FMT, kModeY, true>;
+    return mcap <= 16 ? gemv_mfma_kernel<16, FMT, kModeY, true> : nullptr;
 }
 int launch_down_split_wide(const tb_matrix *w, const float *h, int m, int8_t *qh, float *dqh,
                            float *y, float *part, hipStream_t stream)
@@ -2134,7 +2172,7 @@ int launch_down_split_wide(const tb_matrix *w, const float *h, int m, int8_t *qh
     int rc = device_info(&info);
     if (rc)
         return rc;
-    if (m <= TB_MAX_ROWS || m > 2 * kMaxWideRows)
+    if (m <= TB_MAX_ROWS || m > TB_MAX_BATCH_ROWS)
         return TB_EUNSUPPORTED;
     const bool tern = w->fmt == TB_FMT_TERNARY2;
     const int I = split_steps(w), k = w->k, nb = k / kBlock, bps = tern ? 8 : 16;
@@ -2142,27 +2180,22 @@ int launch_down_split_wide(const tb_matrix *w, const float *h, int m, int8_t *qh
     const int R = std::max(1, std::min(info.cus / I, T));
     if (nb % (tern ? 2 : 4) != 0)   // a lane's scale load holds whole block pairs / quads
         return TB_EUNSUPPORTED;
-    const int chunks = (m + kMaxWideRows - 1) / kMaxWideRows;
+    const int mcap = (m <= 16 || !tern) ? 16 : 32;   // the kernel's rows (B columns)
+    const int chunks = (m + mcap - 1) / mcap;
     const size_t rows_g = (size_t)((T + R - 1) / R) * kRowsPerWave;
-    // (the kernel's carve-up: one step of codes, the step's block terms [2 steps][m] (and
+    // (the kernel's carve-up: one step of codes, the step's block terms [2 steps][rows] (and
     // code sums for sign), the item counter, the step partials of the group's rows)
-    auto lds_of = [&](int mc) {
-        return (size_t)(tern ? 1024 : 2048) * mc + (size_t)2 * bps * mc * 4 * (tern ? 1 : 2) + 16 +
-               rows_g * mc * 4;
-    };
-    GemvFn fns[2] = {nullptr, nullptr};
-    size_t ldss[2] = {0, 0};
-    for (int i = 0; i < chunks; ++i) {
-        const int mc = (m * (i + 1)) / chunks - (m * i) / chunks;
-        fns[i] = tern ? split_wide_pick_m<TB_FMT_TERNARY2>(mc) : split_wide_pick_m<TB_FMT_SIGN1>(mc);
-        ldss[i] = lds_of(mc);
-        if (!fns[i] || ldss[i] > (size_t)info.lds_limit)
-            return TB_EUNSUPPORTED;
-    }
+    const size_t lds = (size_t)(tern ? 1024 : 2048) * mcap + (size_t)2 * bps * mcap * 4 * (tern ? 1 : 2) +
+                       16 + rows_g * mcap * 4;
+    if (lds > (size_t)info.lds_limit)
+        return TB_EUNSUPPORTED;
+    GemvFn fn = tern ? split_wide_pick<TB_FMT_TERNARY2>(mcap) : split_wide_pick<TB_FMT_SIGN1>(mcap);
+    if (!fn)
+        return TB_EUNSUPPORTED;
+    if ((rc = raise_lds(reinterpret_cast<const void *>(fn), lds)))
+        return rc;
     for (int i = 0, r0 = 0; i < chunks; ++i) {
         const int mc = (m * (i + 1)) / chunks - (m * i) / chunks;
-        if ((rc = raise_lds(reinterpret_cast<const void *>(fns[i]), ldss[i])))
-            return rc;
         GemvArgs a = {};
         a.codes0 = static_cast<const uint8_t *>(w->codes);
         a.scales0 = w->scales;
@@ -2175,9 +2208,10 @@ int launch_down_split_wide(const tb_matrix *w, const float *h, int m, int8_t *qh
         a.groups = R;
         a.part = part + (size_t)r0 * w->n;
         a.part_rows = m;
+        a.act_rows = mc;
         a.codes_bytes = (uint32_t)codes_bytes(w);
         a.scales_bytes = (uint32_t)((scales_bytes(w) + 3) & ~(size_t)3);
-        hipLaunchKernelGGL(fns[i], dim3(I * R), dim3(mfma_threads(w->fmt)), ldss[i], stream, a);
+        hipLaunchKernelGGL(fn, dim3(I * R), dim3(mfma_threads(w->fmt, mcap)), lds, stream, a);
         if (hipGetLastError() != hipSuccess)
             return TB_EHIP;
         r0 += mc;

@@ -18,9 +18,9 @@ Cases:
   * a captured graph replayed three times, with eager work between the replays, every
     replay checked.
 
-tb_ffn_down_split_batch (1 ... 32 rows): from 9 rows and k >= 8192 the batch runs as
-chunks of 8 ... 16 rows on the 16-column matrix-core kernel split over k, with one fold
-launch. Every row's y, qh and dqh must be bit-identical to tb_ffn_down_batch (whose rows
+tb_ffn_down_split_batch (1 ... 32 rows): from 9 rows and k >= 8192 the batch runs on the
+matrix-core kernel split over k (ternary: one launch, 16 or 32 B columns; sign: chunks of
+up to 16 rows), with one fold launch. Every row's y, qh and dqh must be bit-identical to tb_ffn_down_batch (whose rows
 are bit-identical to each row run alone, tests/test_gpu_batch.py) and, for sampled rows,
 to tb_ffn_down on the row alone; y within the oracle's bound at the FFN shape for 16
 and 32 rows. Shapes below k = 8192 and odd block counts take tb_ffn_down_batch.
