@@ -1463,6 +1463,11 @@ __global__ __launch_bounds__(pack_threads(FMT)) void gemv_mfma_pack_kernel(const
                         P[p] = t[p][r] + row_down(t[p][r], 8);
                     tot[r] = ((P[0] + P[7]) + (P[6] + P[5])) + ((P[4] + P[3]) + (P[2] + P[1]));
                 }
+                // computed here, with every lane active: left free, the adds sink into the
+                // store's branch below while the row rotations (DPP, which read other lanes)
+                // stay out, so each rotation costs a move of its own instead of riding on
+                // its add
+                asm volatile("" : "+v"(tot[r]));
             }
             if (hsel == 0 && mcol < M) {
 #pragma unroll
