@@ -72,8 +72,9 @@ def parse():
                    help="no all-cores oracle pass (and oracle parity check) at M=8")
     p.add_argument("--profile-only", action="store_true",
                    help="one eager pass of each path and exit (for rocprofv3 counter runs)")
-    p.add_argument("--profile-m", default="1,8",
-                   help="rows of the --profile-only passes, comma-separated (each 1..8)")
+    p.add_argument("--profile-m", default="1,8,32",
+                   help="rows of the --profile-only passes, comma-separated (1..8: the fused "
+                        "and the separate paths; 9..32: the *_batch calls)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -647,6 +648,13 @@ def main():
 
     if args.profile_only:
         for pm in (int(v) for v in args.profile_m.split(",")):
+            if pm > 8:
+                sp = Stream64(tb, dev_layers, xs, pm, torch, batch=True)
+                sp.step()
+                torch.cuda.synchronize()
+                del sp
+                log(f"profile pass done at M={pm} (one pass of the *_batch calls)")
+                continue
             fp = Fused64(tb, dev_layers, xs, pm, torch)
             sp = Stream64(tb, dev_layers, xs, pm, torch)
             fp.step()

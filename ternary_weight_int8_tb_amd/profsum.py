@@ -5,7 +5,8 @@
 
 --stats: the directory of a `rocprofv3 --kernel-trace --stats --output-format csv -o bench`
 run of bench.py; --pmc: the parent directory of the four counter runs pmc_FETCH_SIZE,
-pmc_WRITE_SIZE (bench.py --profile-only: one pass of each path at M=1 and at M=8) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE
+pmc_WRITE_SIZE (bench.py --profile-only: one pass of each path at M=1 and at M=8, and of the
+batch calls at M=32) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE
 (bench.py --copy-probe-mib 1024); --bench: the JSON line of an untraced bench.py run of
 the same code. Writes ffn64_stream_kernel_stats.md, ffn64_stream_traffic.md and
 ffn64_stream_traffic.json. --sq: the parent directory of two SQ counter runs (pmc_sq_a,
@@ -61,6 +62,11 @@ ALGORITHMIC = {
     "gemv_mfma_pack_kernel<8, 0, 0, true>": MATRIX_BYTES + 8 * (INTER * 4 + INTER + NB_N * 4)
     + 17 * 8 * HIDDEN * 4,
     "ffn_layers_kernel<8, 0>": 32 * (3 * MATRIX_BYTES + 8 * 2 * HIDDEN * 4),
+    # M=32 (batch calls): gate/up as two 16-row passes, the down stage split over k in one
+    # launch of two 16-column groups
+    "gemv_mfma_kernel<16, 0, 1>": 2 * MATRIX_BYTES + 16 * (HIDDEN + NB_H * 4 + INTER * 4),
+    "gemv_mfma_kernel<32, 0, 0, true>": MATRIX_BYTES + 32 * (INTER * 4 + INTER + NB_N * 4)
+    + 17 * 32 * HIDDEN * 4,
 }
 WHAT = {
     "gemv_ring_kernel<1, 0, 1, true>": "tb_ffn_gateup_silu_x at M=1 (gate and up, 47,349,760 weight "
@@ -72,6 +78,10 @@ WHAT = {
     "gemv_mfma_pack_kernel<8, 0, 0, true>": "the down GEMV of tb_ffn_down_split at M=8 (split over k, "
                                             "rotation of h inside; matrix cores)",
     "ffn_layers_kernel<8, 0>": "one tb_ffn_layers launch of 32 layers at M=8",
+    "gemv_mfma_kernel<16, 0, 1>": "one 16-row pass of tb_ffn_gateup_silu_batch (matrix cores; two per "
+                                  "call at M=32)",
+    "gemv_mfma_kernel<32, 0, 0, true>": "the down GEMV of tb_ffn_down_split_batch at M=32 (split over k, "
+                                        "rotation of h inside, two 16-column groups; matrix cores)",
 }
 
 
@@ -103,6 +113,12 @@ STREAMS = {
                  ("gemv_ring_kernel<1, 1, 0, false>", SIGN_MATRIX_BYTES)],
     "sign M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 1, 1, false>", 2 * SIGN_MATRIX_BYTES),
                  ("gemv_mfma_pack_kernel<8, 1, 0, true>", SIGN_MATRIX_BYTES), ("split_fold_kernel", 0)],
+    # batch calls: rotquant, gate/up (one or two 16-row passes), the down split, the fold
+    "ternary M=16": [("rotquant_kernel", 0), ("gemv_mfma_kernel<16, 0, 1>", 2 * MATRIX_BYTES),
+                     ("gemv_mfma_kernel<16, 0, 0, true>", MATRIX_BYTES), ("split_fold_kernel", 0)],
+    "ternary M=32": [("rotquant_kernel", 0), ("gemv_mfma_kernel<16, 0, 1>", 2 * MATRIX_BYTES),
+                     ("gemv_mfma_kernel<16, 0, 1>", 2 * MATRIX_BYTES),
+                     ("gemv_mfma_kernel<32, 0, 0, true>", MATRIX_BYTES), ("split_fold_kernel", 0)],
 }
 
 
@@ -203,19 +219,20 @@ def read_all_counters(d: str):
 
 
 def write_sq(sq_dir: str, out: str):
-    """SQ counters of the M=1 and M=8 kernels: instruction mix per wave and where wave time
-    goes (waiting on memory counters, waiting to issue, issuing VALU)."""
+    """SQ counters of the M=1, M=8 and M=32 kernels: instruction mix per wave and where wave
+    time goes (waiting on memory counters, waiting to issue, issuing VALU)."""
     a = read_all_counters(os.path.join(sq_dir, "pmc_sq_a"))
     b = read_all_counters(os.path.join(sq_dir, "pmc_sq_b"))
     keep = [k for k in a if k in b and ("gemv" in k or "ffn_layers" in k)]
-    lines = ["# FFN 64-layer stream: SQ counters of the M=1 and M=8 kernels", "",
+    lines = ["# FFN 64-layer stream: SQ counters of the M=1, M=8 and M=32 kernels", "",
              "Commands (on the GPU box, from /tmp with TMPDIR=/tmp; one counter set per run):", "", "```"]
     for name, cs in SQ_SETS.items():
         lines.append(f"rocprofv3 --pmc {cs} --output-format csv -d <out>/pmc_sq_{name} -o run -- "
                      "python3 /root/repo/bench.py --profile-only")
     lines += ["```", "",
               "Means per dispatch over every dispatch of the kernel in one pass of each path at M=1 "
-              "and M=8 (bench.py --profile-only). Instruction counts are wave instructions per wave. "
+              "and M=8, and of the batch calls at M=32 (bench.py --profile-only). Instruction counts "
+              "are wave instructions per wave. "
               "SQ_WAVE_CYCLES, SQ_WAIT_ANY (waiting on s_waitcnt: memory and LDS counters), "
               "SQ_WAIT_INST_ANY (waiting to issue the next instruction) and SQ_ACTIVE_INST_VALU "
               "share one unit (quad-cycles), so their ratios are fractions of resident wave time. "
@@ -239,8 +256,9 @@ def write_sq(sq_dir: str, out: str):
             f"{100 * cb['SQ_ACTIVE_INST_VALU'] / wc:.0f} | {cb['SQ_LDS_BANK_CONFLICT'] / CUS:.0f} | "
             f"{cb['SQ_VALU_MFMA_BUSY_CYCLES'] / CUS:.0f} |")
     lines += ["", "Kernel names as in the kernel statistics: gemv_ring_kernel<M, FMT, MODE, ROTX> "
-              "(dot products), gemv_mfma_pack_kernel<M, FMT, MODE, KS> (matrix cores; KS true = "
-              "the down stage split over k), ffn_layers_kernel<M, FMT> (32 layers per launch)."]
+              "(dot products), gemv_mfma_pack_kernel<M, FMT, MODE, KS> and gemv_mfma_kernel<M, FMT, "
+              "MODE, KS> (matrix cores; KS true = the down stage split over k), "
+              "ffn_layers_kernel<M, FMT> (32 layers per launch)."]
     with open(os.path.join(out, "ffn64_stream_sq_counters.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {out}/ffn64_stream_sq_counters.md")
@@ -282,7 +300,8 @@ def main():
               "gemv_mfma_pack_kernel<M, FMT, MODE, KS> (two blocks per MFMA, M <= 8; KS true = the "
               "down stage split over k, each workgroup one step of one row group, rotating its "
               "blocks of h itself; split_fold_kernel adds its step partials) and "
-              "gemv_mfma_kernel<M, FMT, MODE> (one block per MFMA, batches above 8 rows) run on the "
+              "gemv_mfma_kernel<M, FMT, MODE[, KS]> (one block per MFMA, batches above 8 rows; KS "
+              "true = the batch's down stage split over k, 16 or 32 rows) run on the "
               "matrix cores (ternary: gate/up for M >= 5, a single GEMV for M >= 6; sign: gate/up "
               "for M >= 5, a single GEMV for M >= 7). "
               "ffn_layers_kernel<M, FMT> is one tb_ffn_layers launch of up to 32 whole layers. "
