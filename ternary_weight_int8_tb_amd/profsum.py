@@ -64,7 +64,7 @@ ALGORITHMIC = {
     "ffn_layers_kernel<8, 0>": 32 * (3 * MATRIX_BYTES + 8 * 2 * HIDDEN * 4),
     # M=32 (batch calls): gate/up as two 16-row passes, the down stage split over k in one
     # launch of two 16-column groups
-    "gemv_mfma_kernel<16, 0, 1>": 2 * MATRIX_BYTES + 16 * (HIDDEN + NB_H * 4 + INTER * 4),
+    "gemv_mfma_kernel<16, 0, 1, false>": 2 * MATRIX_BYTES + 16 * (HIDDEN + NB_H * 4 + INTER * 4),
     "gemv_mfma_kernel<32, 0, 0, true>": MATRIX_BYTES + 32 * (INTER * 4 + INTER + NB_N * 4)
     + 17 * 32 * HIDDEN * 4,
 }
@@ -78,7 +78,7 @@ WHAT = {
     "gemv_mfma_pack_kernel<8, 0, 0, true>": "the down GEMV of tb_ffn_down_split at M=8 (split over k, "
                                             "rotation of h inside; matrix cores)",
     "ffn_layers_kernel<8, 0>": "one tb_ffn_layers launch of 32 layers at M=8",
-    "gemv_mfma_kernel<16, 0, 1>": "one 16-row pass of tb_ffn_gateup_silu_batch (matrix cores; two per "
+    "gemv_mfma_kernel<16, 0, 1, false>": "one 16-row pass of tb_ffn_gateup_silu_batch (matrix cores; two per "
                                   "call at M=32)",
     "gemv_mfma_kernel<32, 0, 0, true>": "the down GEMV of tb_ffn_down_split_batch at M=32 (split over k, "
                                         "rotation of h inside, two 16-column groups; matrix cores)",
@@ -114,10 +114,10 @@ STREAMS = {
     "sign M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 1, 1, false>", 2 * SIGN_MATRIX_BYTES),
                  ("gemv_mfma_pack_kernel<8, 1, 0, true>", SIGN_MATRIX_BYTES), ("split_fold_kernel", 0)],
     # batch calls: rotquant, gate/up (one or two 16-row passes), the down split, the fold
-    "ternary M=16": [("rotquant_kernel", 0), ("gemv_mfma_kernel<16, 0, 1>", 2 * MATRIX_BYTES),
+    "ternary M=16": [("rotquant_kernel", 0), ("gemv_mfma_kernel<16, 0, 1, false>", 2 * MATRIX_BYTES),
                      ("gemv_mfma_kernel<16, 0, 0, true>", MATRIX_BYTES), ("split_fold_kernel", 0)],
-    "ternary M=32": [("rotquant_kernel", 0), ("gemv_mfma_kernel<16, 0, 1>", 2 * MATRIX_BYTES),
-                     ("gemv_mfma_kernel<16, 0, 1>", 2 * MATRIX_BYTES),
+    "ternary M=32": [("rotquant_kernel", 0), ("gemv_mfma_kernel<16, 0, 1, false>", 2 * MATRIX_BYTES),
+                     ("gemv_mfma_kernel<16, 0, 1, false>", 2 * MATRIX_BYTES),
                      ("gemv_mfma_kernel<32, 0, 0, true>", MATRIX_BYTES), ("split_fold_kernel", 0)],
 }
 
