@@ -2889,7 +2889,7 @@ int tb_ffn_layers(const tb_ffn_weights *layers, int num_layers, const float *x, 
         a.chain = chain ? 1 : 0;
         a.x = chain ? (start == 0 ? x : y + (size_t)(start - 1) * m * H) : x + (size_t)start * m * H;
         a.y = y + (size_t)start * m * H;
-        hipLaunchKernelGGL(fn, dim3(G), dim3(tbl::kThreads), plan.total, s, a);
+        hipLaunchKernelGGL(fn, dim3(G), dim3(tbl::layers_threads(F, m)), plan.total, s, a);
         if (hipGetLastError() != hipSuccess)
             return TB_EHIP;
     }

@@ -573,8 +573,10 @@ __device__ __forceinline__ void store_block_mfma(uint8_t *act, int m, int b, int
 }
 
 // Integer sums of one chunk against all M rows, step-major layout; `lds` is this lane's
-// slot address in the current step. Same arithmetic as chunk_sums.
-template <int M, int FMT, bool TWO>
+// slot address in the current step. Same arithmetic as chunk_sums. MASK: sign weights at
+// one row take the masked bit planes below (more registers: the fused kernel, which holds
+// a whole ring across phases, spilled 76 bytes per lane with them).
+template <int M, int FMT, bool TWO, bool MASK = true>
 __device__ __forceinline__ void chunk_sums_step(const uint4 &w0, const uint4 &w1, const uint8_t *lds,
                                                 int (&is0)[M], int (&is1)[M])
 {
@@ -614,7 +616,7 @@ __device__ __forceinline__ void chunk_sums_step(const uint4 &w0, const uint4 &w1
             if (TWO)
                 is1[m] = pair_add(is1[m]);
         }
-    } else if (TB_SIGN_MASK && M == 1) {
+    } else if (TB_SIGN_MASK && MASK && M == 1) {
         // Bit k of every byte masked in place: the bytes are 0 or 2^k (k = 7: 0x80, i.e.
         // -128 as a signed byte), so the dot product of plane bit k is 2^k D_k (k = 7:
         // -128 D_7) with D_k the exact sum over that bit's weights. One AND per dot product

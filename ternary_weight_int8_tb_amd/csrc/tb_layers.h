@@ -10,7 +10,7 @@
 //
 // Why one launch: a dependent kernel launch costs a ramp of 2-4 us before its weight
 // stream reaches full rate, against about 10 us for the whole layer's 71 MB at the
-// measured 7 TB/s. Here one workgroup of 16 waves per CU stays resident for all layers:
+// measured 7 TB/s. Here one workgroup per CU (16 waves; 12 or 8 for sign batches) stays resident for all layers:
 //   * Work. Each CU owns an equal share of the gate/up row tiles and of the down row tiles
 //     (4 rows each), the same shares every layer. An item is one step of a gate/up tile
 //     (gate and up, 2 KB per wave) or two steps of a down tile (2 KB). The CU's items of
@@ -39,8 +39,15 @@ namespace tbl {
 
 using namespace tbk;
 
-constexpr int kWaves = 16;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup: 16 for ternary and for sign at one row; for sign, whose decode holds
+// more registers, 12 for 2 to 5 rows and 8 from 6 (at 16 waves, 128 VGPRs each, its kernels
+// spilled from 2 rows on, 328 bytes per lane at 8; at 12 waves, from 6 rows on). Sign
+// layers, us per layer: M=8 96.7 -> 69.3; M=1 on 12 waves 25.0 against 23.6 on 16.
+__host__ __device__ constexpr int layers_waves(int fmt, int m)
+{
+    return (fmt == TB_FMT_SIGN1 && m > 1) ? (m >= 6 ? 8 : 12) : 16;
+}
+__host__ __device__ constexpr int layers_threads(int fmt, int m) { return 64 * layers_waves(fmt, m); }
 #ifndef TBL_DEPTH_TERN
 #define TBL_DEPTH_TERN 2
 #endif
@@ -144,8 +151,9 @@ __device__ __forceinline__ int div_small(int a, int b, float rb)
 }
 
 template <int M, int FMT>
-__global__ __launch_bounds__(kThreads, 1) void ffn_layers_kernel(LArgs a)
+__global__ __launch_bounds__(layers_threads(FMT, M), 1) void ffn_layers_kernel(LArgs a)
 {
+    constexpr int kWaves = layers_waves(FMT, M), kThreads = layers_threads(FMT, M);
     extern __shared__ __align__(16) uint8_t lds[];
     using SL = StepLayout<M, FMT>;
     constexpr int kWpc = Fmt<FMT>::kWeightsPerChunk;
@@ -558,9 +566,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_layers_kernel(LArgs a)
                           uint32_t row, int nb, float *dst, bool two) {
         int is0[M], is1[M];
         if (two)
-            chunk_sums_step<M, FMT, true>(w0, w1, lds_lane + (size_t)step * SL::kStepBytes, is0, is1);
+            chunk_sums_step<M, FMT, true, false>(w0, w1, lds_lane + (size_t)step * SL::kStepBytes, is0, is1);
         else
-            chunk_sums_step<M, FMT, false>(w0, w0, lds_lane + (size_t)step * SL::kStepBytes, is0, is1);
+            chunk_sums_step<M, FMT, false, false>(w0, w0, lds_lane + (size_t)step * SL::kStepBytes, is0, is1);
         const int blk = step * kBps + blk_lane;
         const uint32_t cshift = ((row * (uint32_t)nb + (uint32_t)blk_lane) & 1u) * 16u;
         const float s0 = half_bits_to_float((uint16_t)__builtin_amdgcn_ubfe(sw0, cshift, 16));
