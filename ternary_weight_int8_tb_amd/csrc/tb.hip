@@ -743,12 +743,14 @@ __host__ __device__ constexpr int pack_threads(int fmt)
 //   * Sign runs 12 waves per CU: its 16-block steps need more than the 128 registers a
 //     wave has at 16.
 // ------------------------------------------------------------------------------------
-template <int M, int FMT, int MODE, bool KS = false>
+template <int M, int FMT, int MODE, bool KS = false, bool KP = false>
 __global__ __launch_bounds__(mfma_threads(FMT, M)) void gemv_mfma_kernel(GemvArgs a)
 {
     static_assert(M >= 1 && M <= 32, "one or two 16-column B operands");
-    static_assert(M <= 16 || KS, "two column groups only split over k (one step staged)");
+    static_assert(M <= 16 || KS || KP, "two column groups stage one step, or k in two phases");
     static_assert(!KS || MODE == kModeY, "the split over k is the down stage");
+    static_assert(!KP || (!KS && MODE == kModeGateUp && FMT == TB_FMT_TERNARY2),
+                  "k in two phases: ternary gate/up");
     extern __shared__ __align__(16) uint8_t lds[];
     using L = StepLayout<M, FMT>;
     constexpr bool kTern = FMT == TB_FMT_TERNARY2;
@@ -771,13 +773,20 @@ __global__ __launch_bounds__(mfma_threads(FMT, M)) void gemv_mfma_kernel(GemvArg
     int c = (int)blockIdx.x, s0 = 0;   // s0: the step of KS items
     if (KS && !split_index<FMT>(G, Ik, c, s0))
         return;
-    const int I = KS ? 1 : Ik;                          // steps per tile in this workgroup
+    // KP: the steps in two phases, [0, Sp) then [Sp, Ik), each staged in turn; a row's step
+    // partials of phase 0 are summed (in step order, from +0) into its first slot before
+    // phase 1 writes the next slots, so the row's sum keeps the order of the other kernels
+    const int Sp = KP ? (Ik + 1) / 2 : Ik;
+    int I = KS ? 1 : Sp;                                // steps per tile in this phase
+    const int NS = KP ? max(Sp, 1 + Ik - Sp) : I;       // partial slots per row
+    int slot0 = 0;                                      // the phase's first slot
     const int nbl = KS ? kBps : nb;                     // blocks of the staged activation
-    const int rows = KS ? a.act_rows : M;               // live activation rows (<= M)
+    const int rows = (KS || KP) ? a.act_rows : M;       // live activation rows (<= M)
     const int T = (n + kRowsPerWave - 1) / kRowsPerWave;
     const int R0 = part_lo(T, G, c) * kRowsPerWave;
     const int R1 = min(part_lo(T, G, c + 1) * kRowsPerWave, n);
-    const int J = (((R1 - R0 + 15) / 16) * I) << kMatShift;   // this workgroup's items
+    const int tiles16 = (R1 - R0 + 15) / 16;
+    int J = (tiles16 * I) << kMatShift;                 // this workgroup's items (this phase)
     const uint32_t row_bytes = (uint32_t)C * 16u;
 
     uint8_t *act = lds;
@@ -853,6 +862,38 @@ __global__ __launch_bounds__(mfma_threads(FMT, M)) void gemv_mfma_kernel(GemvArg
         }
     };
 
+    // KP: the int8 codes of steps [ps0, ps0 + pI) of rows < act_rows into the matrix-core
+    // layout (unit (g, m), g = 4 c + j over the phase's chunks, slot g M + m), the first
+    // round's loads before the weight prologue
+    auto stage_phase = [&](int ps0, int pI) {
+        constexpr int kR = 4;
+        const int units = 64 * pI * M;
+        auto uload = [&](StageUnit<FMT> &su, int u) {   // (chunks past C: zeros, not read)
+            const int m = u % M, g = u / M;
+            su.lo = (m < rows && ps0 * 16 + g / 4 < C)
+                        ? *reinterpret_cast<const uint4 *>(a.q + (size_t)m * k + (size_t)(ps0 * 64 + g) * 16)
+                        : make_uint4(0u, 0u, 0u, 0u);
+        };
+        StageUnit<FMT> su[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+            if (tid + r * kThreads < units)
+                uload(su[r], tid + r * kThreads);
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+            issue(d);
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int u = tid + r * kThreads;
+            if (u < units)
+                stage_unit_store_mfma<M, FMT>(su[r], act, u % M, u / M);
+        }
+        for (int u = tid + kR * kThreads; u < units; u += kThreads) {
+            StageUnit<FMT> t;
+            uload(t, u);
+            stage_unit_store_mfma<M, FMT>(t, act, u % M, u / M);
+        }
+    };
     if constexpr (KS) {
         // h loads of step s0's blocks first (up to kPre rounds), then the weight prologue,
         // then the rotation (as in gemv_mfma_pack_kernel: the two kernels share the LDS slot
@@ -913,6 +954,14 @@ __global__ __launch_bounds__(mfma_threads(FMT, M)) void gemv_mfma_kernel(GemvArg
             hload(v, z);
             hblock(v, z);
         }
+    } else if constexpr (KP) {
+        // the block terms of all steps once (zero for rows past act_rows and blocks past
+        // k), then phase 0's codes
+        for (int i = tid; i < (nb + kBps) * M; i += kThreads) {
+            const int b = i / M, m = i - b * M;
+            dq_s[i] = (b < nb && m < rows) ? a.dq[(size_t)m * nb + b] : 0.0f;
+        }
+        stage_phase(0, Sp);
     } else {
         stage_activation<M, FMT, MODE, kThreads, true>(a, act, dq_s, qsum_s, [&]() {
 #pragma unroll
@@ -966,7 +1015,7 @@ __global__ __launch_bounds__(mfma_threads(FMT, M)) void gemv_mfma_kernel(GemvArg
 #pragma unroll
         for (int o = 0; o < kBps; ++o) {
             const int kb = o == 0 ? 0 : kBps - o;
-            const int blk = step * kBps + kb;
+            const int blk = ((KS ? 0 : s0) + step) * kBps + kb;   // its block terms in dq_s
             uint32_t w[8];
             if (kTern) {
                 const uint4 cw = rc[d][kb >> 1];
@@ -1055,25 +1104,55 @@ __global__ __launch_bounds__(mfma_threads(FMT, M)) void gemv_mfma_kernel(GemvArg
                     for (int r = 0; r < 4; ++r) {
                         const int lrow = tile * 16 + 4 * lg + r;   // row - R0
                         if (R0 + lrow < R1)
-                            part_s[((size_t)(lrow * I + step) * M + mr) * kParts + mat] = tot[cg][r];
+                            part_s[((size_t)(lrow * NS + slot0 + step) * M + mr) * kParts + mat] = tot[cg][r];
                     }
                 }
             }
         }
     };
-    for (;;) {
-        bool any = false;
+    auto run_ring = [&]() {
+        for (;;) {
+            bool any = false;
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-            if (rit[d] >= 0) {
-                consume(d);
-                any = true;
+            for (int d = 0; d < kDepth; ++d) {
+                if (rit[d] >= 0) {
+                    consume(d);
+                    any = true;
+                }
+                issue(d);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            issue(d);
-            __builtin_amdgcn_sched_barrier(0);
+            if (!any)
+                break;
         }
-        if (!any)
-            break;
+    };
+    run_ring();
+    if constexpr (KP) {
+        __syncthreads();
+        // phase 0's partials of each row, in step order from +0, into its first slot
+        for (int i = tid; i < (R1 - R0) * rows * kParts; i += kThreads) {
+            const int lrow = i / (rows * kParts), rem = i - lrow * rows * kParts;
+            float *ps = part_s + ((size_t)lrow * NS * M + rem / kParts) * kParts + rem % kParts;
+            float v = 0.0f;
+            for (int st = 0; st < Sp; ++st)
+                v += ps[(size_t)st * M * kParts];
+            ps[0] = v;
+        }
+        // phase 1: the next steps, the item counter and the issue state from the start
+        s0 = Sp;
+        I = Ik - Sp;
+        J = (tiles16 * I) << kMatShift;
+        slot0 = 1;
+        gidx = 0;
+        gtile = 0;
+        gstep = 0;
+        pending = tid >> 6;
+        if (tid == 0)
+            *ctr_s = kWaves;
+        __syncthreads();
+        stage_phase(Sp, I);
+        __syncthreads();
+        run_ring();
     }
 
     if (kIsum)
@@ -1086,12 +1165,14 @@ __global__ __launch_bounds__(mfma_threads(FMT, M)) void gemv_mfma_kernel(GemvArg
         }
         return;
     }
-    // ---- every row: its step partials in step order, from +0
-    for (int i = tid; i < (R1 - R0) * M; i += kThreads) {
-        const int lrow = i / M, m = i % M;
-        const float *ps = part_s + ((size_t)lrow * I * M + m) * kParts;
+    // ---- every row: its step partials in step order, from +0 (KP: phase 0's sum, then
+    // phase 1's steps)
+    const int NF = KP ? 1 + Ik - Sp : I;
+    for (int i = tid; i < (R1 - R0) * rows; i += kThreads) {
+        const int lrow = i / rows, m = i - lrow * rows;
+        const float *ps = part_s + ((size_t)lrow * NS * M + m) * kParts;
         float g = 0.0f, u = 0.0f;
-        for (int st = 0; st < I; ++st) {
+        for (int st = 0; st < NF; ++st) {
             g += ps[(size_t)st * M * kParts];
             if (kTwo)
                 u += ps[(size_t)st * M * kParts + 1];
@@ -1749,6 +1830,9 @@ static_assert(mfma_min_rows(true, true) >= 2 && mfma_min_rows(true, false) >= 2 
               "gemv_mfma_pack_kernel is instantiated for M = 2 .. 8");
 
 constexpr int kMaxWideRows = 16;   // rows of one gemv_mfma_kernel launch in the batch calls
+#ifndef TB_GATEUP_PHASED
+#define TB_GATEUP_PHASED 1
+#endif
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
     int lds_limit = 0;   // 0 = not queried yet
@@ -2301,6 +2385,52 @@ int launch_lut(const tb_matrix *w, const int8_t *q, const float *dq, int m, floa
 // gemv_mfma_kernel (all 16 B columns live) where they fit the device's LDS, else of up to 8
 // rows on the kernels of the 1..8-row calls. Every kernel folds a row the same way, so a
 // row's outputs do not depend on the chunk it lands in.
+// Ternary gate/up of 17 ... 32 rows in one launch: gemv_mfma_kernel<32, ..., KP>, two
+// 16-column groups sharing each decoded weight operand, k staged in two phases (32 rows of
+// the whole activation would not fit the LDS), so the weights are read once instead of once
+// per 16-row chunk. TB_EUNSUPPORTED (nothing launched) where the LDS plan does not fit.
+int launch_gateup_phased(const tb_matrix *wg, const tb_matrix *wu, const int8_t *q, const float *dq,
+                         int m, float *h, hipStream_t stream)
+{
+    DeviceInfo info;
+    int rc = device_info(&info);
+    if (rc)
+        return rc;
+    if (wg->fmt != TB_FMT_TERNARY2 || m <= kMaxWideRows || m > TB_MAX_BATCH_ROWS)
+        return TB_EUNSUPPORTED;
+    const int k = wg->k, nb = k / kBlock;
+    if (nb % 2 != 0)   // a lane's scale load holds whole block pairs
+        return TB_EUNSUPPORTED;
+    const int Ik = (k / 64 + kChunkLanes - 1) / kChunkLanes, Sp = (Ik + 1) / 2;
+    const int NS = std::max(Sp, 1 + Ik - Sp);
+    const long tiles = (wg->n + kRowsPerWave - 1) / kRowsPerWave;
+    const int grid = (int)(tiles < info.cus ? tiles : info.cus);
+    const size_t rows_cu = (size_t)((tiles + grid - 1) / grid) * kRowsPerWave;
+    // (the kernel's carve-up: phase 0's codes, the block terms of all steps, the item
+    // counter, the step partials [row][slot][32][gate, up])
+    const size_t lds = (size_t)Sp * 1024 * 32 + (size_t)(nb + 8) * 32 * 4 + 16 + rows_cu * NS * 32 * 2 * 4;
+    if (lds > (size_t)info.lds_limit)
+        return TB_EUNSUPPORTED;
+    GemvFn fn = gemv_mfma_kernel<32, TB_FMT_TERNARY2, kModeGateUp, false, true>;
+    if ((rc = raise_lds(reinterpret_cast<const void *>(fn), lds)))
+        return rc;
+    GemvArgs a = {};
+    a.codes0 = static_cast<const uint8_t *>(wg->codes);
+    a.scales0 = wg->scales;
+    a.codes1 = static_cast<const uint8_t *>(wu->codes);
+    a.scales1 = wu->scales;
+    a.n = wg->n;
+    a.k = k;
+    a.q = q;
+    a.dq = dq;
+    a.out = h;
+    a.act_rows = m;
+    a.codes_bytes = (uint32_t)codes_bytes(wg);
+    a.scales_bytes = (uint32_t)((scales_bytes(wg) + 3) & ~(size_t)3);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(mfma_threads(TB_FMT_TERNARY2, 32)), lds, stream, a);
+    return hipGetLastError() == hipSuccess ? TB_OK : TB_EHIP;
+}
+
 int launch_gemv_batch(int mode, const tb_matrix *w0, const tb_matrix *w1, const int8_t *q,
                       const float *dq, int m, float *out, int32_t *isum, hipStream_t stream)
 {
@@ -2308,6 +2438,13 @@ int launch_gemv_batch(int mode, const tb_matrix *w0, const tb_matrix *w1, const 
     int rc = device_info(&info);
     if (rc)
         return rc;
+#if TB_GATEUP_PHASED
+    if (mode == kModeGateUp && m > kMaxWideRows) {
+        rc = launch_gateup_phased(w0, w1, q, dq, m, out, stream);
+        if (rc != TB_EUNSUPPORTED)
+            return rc;
+    }
+#endif
     int cmax = 8;
     for (int c = m < kMaxWideRows ? m : kMaxWideRows; c > 8; --c)
         if (wide_fits(info, mode, w0, c)) {

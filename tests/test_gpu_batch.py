@@ -4,8 +4,9 @@ Bars, as for the 1..8-row calls: block sums bit-exact; y within 1e-4 * sum|terms
 h within the propagated bound; rotquant codes and scales bit-exact; and every row
 of a batch bit-identical to the same row run alone through the 1..8-row calls.
 The shapes are the FFN's (gate/up 17408 x 5120, down 5120 x 17408), where gate/up
-runs 16 rows per matrix-core launch and the down GEMV chunks of 8, plus ragged
-shapes whose block count takes the chunks-of-8 route.
+runs 16 rows per matrix-core launch (ternary from 17 rows: one launch, k staged in two
+phases) and the down GEMV chunks of 8, plus ragged shapes whose block count takes the
+chunks-of-8 route.
 """
 
 from __future__ import annotations
@@ -146,3 +147,33 @@ def test_batch_small_m_equals_the_1_to_8_calls(o):
     q, dq = o.rotate_quant(synth.normal_rows(8, 5120, 34, 0))
     for m in (1, 5, 8):
         assert gemv_batch(wd, q[:m], dq[:m]).tobytes() == gu.gemv(wd, q[:m], dq[:m]).tobytes()
+
+
+def gateup_batch(wg, wu, q, dq):
+    h = gu.f32_out(q.shape[0], wg.n)
+    tb.tb_ffn_gateup_silu_batch(wg, wu, gu.dev(q), gu.dev(dq), h)
+    return gu.host(h)
+
+
+# k = 5120, 4096, 2304, 1280, 1024: 5, 4, 3, 2, 1 steps (the phases split them 3 + 2,
+# 2 + 2, 2 + 1, 1 + 1 and 1 + 0); n with a partial 16-row tile in a workgroup
+@pytest.mark.parametrize("n,k", [(synth.INTER, synth.HIDDEN), (1030, 4096), (100, 2304), (1030, 1280),
+                                 (260, 1024)])
+@pytest.mark.parametrize("m", [17, 24, 32])
+def test_batch_gateup_one_launch_equals_chunks(o, n, k, m):
+    # ternary gate/up of 17..32 rows runs as one launch with k staged in two phases; every
+    # row must equal the same row through calls of at most 16 rows (and the oracle's bound)
+    say(f"batch gate/up one launch n={n} k={k} m={m}")
+    wg = synth.matrix(TERN, n, k, 35, 0, synth.T_GATE)
+    wu = synth.matrix(TERN, n, k, 35, 0, synth.T_UP)
+    g, u = tb.Matrix.upload(wg), tb.Matrix.upload(wu)
+    q, dq = o.rotate_quant(synth.normal_rows(m, k, 36 + m, 0))
+    h = gateup_batch(g, u, q, dq)
+    for a in range(0, m, 16):
+        b = min(a + 16, m)
+        part = gateup_batch(g, u, q[a:b], dq[a:b])
+        bad = np.argwhere(part.view(np.uint32) != h[a:b].view(np.uint32))
+        assert bad.size == 0, f"rows {a}..{b - 1} differ from the one-launch batch at {bad[:5]}"
+    r = o.gateup_silu(wg, wu, q, dq)
+    tol = bounds.h_tolerance(r["g"], r["u"], r["sg"], r["su"])
+    assert np.all(np.abs(h.astype(np.float64) - r["h"]) <= tol)
