@@ -220,8 +220,11 @@ int tb_sign_interleave(const tb_matrix *w, void *codes_ri, uint16_t *scales_ri, 
  * kernel with all 16 B columns live (one read of the weights per chunk) where
  * the shape's activation and step partials fit the device's LDS and k/128 is a
  * multiple of 2 (ternary) or 4 (sign); otherwise chunks of up to 8 rows on the
- * kernels of the calls above. At hidden 5120, intermediate 17408: gate/up
- * takes 16 rows per chunk, the down GEMV 8.
+ * kernels of the calls above. Ternary gate/up of 17 to 32 rows runs in one
+ * launch (two 16-column groups, k staged in two phases) where its LDS plan
+ * fits. At hidden 5120, intermediate 17408: gate/up takes the whole batch
+ * (ternary) or 16 rows per chunk (sign), the down GEMV 8 (see
+ * tb_ffn_down_split_batch for a down stage that reads its weights once).
  * tb_gemv_block_sums_batch: (chunk rows) * n * (k/128) * 4 must be below
  * 2 GiB. */
 int tb_rotate_quant_i8_batch(const float *x, int m, int k, int8_t *q, float *dq, void *stream);

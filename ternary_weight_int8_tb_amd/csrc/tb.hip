@@ -28,7 +28,8 @@
 //     gate/up (both formats), and from M = 6 (ternary) or 7 (sign) on the single GEMV, the
 //     integer dot products go to v_mfma_i32_16x16x64_i8, where that measures faster:
 //     gemv_mfma_pack_kernel (two blocks per MFMA) up to 8 rows, gemv_mfma_kernel (16-row
-//     tiles) for batches of 9 to 16 rows. The block-sum export follows the gate/up
+//     tiles) for batches of 9 to 16 rows, and for ternary gate/up of 17 to 32 rows in one
+//     launch (two 16-column groups, k staged in two phases). The block-sum export follows the gate/up
 //     threshold, so it runs the matrix-core integer core at every M where production does.
 //   * The down stage can also run split over k (tb_ffn_down_split, from 4 rows where it
 //     measures faster): each workgroup of gemv_mfma_pack_kernel<..., KS> takes one step of
