@@ -62,10 +62,10 @@ ALGORITHMIC = {
     "gemv_mfma_pack_kernel<8, 0, 0, true>": MATRIX_BYTES + 8 * (INTER * 4 + INTER + NB_N * 4)
     + 17 * 8 * HIDDEN * 4,
     "ffn_layers_kernel<8, 0>": 32 * (3 * MATRIX_BYTES + 8 * 2 * HIDDEN * 4),
-    # M=32 (batch calls): gate/up as two 16-row passes, the down stage split over k in one
-    # launch of two 16-column groups
-    "gemv_mfma_kernel<16, 0, 1, false>": 2 * MATRIX_BYTES + 16 * (HIDDEN + NB_H * 4 + INTER * 4),
-    "gemv_mfma_kernel<32, 0, 0, true>": MATRIX_BYTES + 32 * (INTER * 4 + INTER + NB_N * 4)
+    # M=32 (batch calls): gate/up in one launch (k staged in two phases) and the down stage
+    # split over k in one launch, both with two 16-column groups
+    "gemv_mfma_kernel<32, 0, 1, false, true>": 2 * MATRIX_BYTES + 32 * (HIDDEN + NB_H * 4 + INTER * 4),
+    "gemv_mfma_kernel<32, 0, 0, true, false>": MATRIX_BYTES + 32 * (INTER * 4 + INTER + NB_N * 4)
     + 17 * 32 * HIDDEN * 4,
 }
 WHAT = {
@@ -78,9 +78,9 @@ WHAT = {
     "gemv_mfma_pack_kernel<8, 0, 0, true>": "the down GEMV of tb_ffn_down_split at M=8 (split over k, "
                                             "rotation of h inside; matrix cores)",
     "ffn_layers_kernel<8, 0>": "one tb_ffn_layers launch of 32 layers at M=8",
-    "gemv_mfma_kernel<16, 0, 1, false>": "one 16-row pass of tb_ffn_gateup_silu_batch (matrix cores; two per "
-                                  "call at M=32)",
-    "gemv_mfma_kernel<32, 0, 0, true>": "the down GEMV of tb_ffn_down_split_batch at M=32 (split over k, "
+    "gemv_mfma_kernel<32, 0, 1, false, true>": "tb_ffn_gateup_silu_batch at M=32 (matrix cores, two 16-column "
+                                               "groups, k staged in two phases)",
+    "gemv_mfma_kernel<32, 0, 0, true, false>": "the down GEMV of tb_ffn_down_split_batch at M=32 (split over k, "
                                         "rotation of h inside, two 16-column groups; matrix cores)",
 }
 
@@ -114,11 +114,10 @@ STREAMS = {
     "sign M=8": [("rotquant_kernel", 0), ("gemv_mfma_pack_kernel<8, 1, 1, false>", 2 * SIGN_MATRIX_BYTES),
                  ("gemv_mfma_pack_kernel<8, 1, 0, true>", SIGN_MATRIX_BYTES), ("split_fold_kernel", 0)],
     # batch calls: rotquant, gate/up (one or two 16-row passes), the down split, the fold
-    "ternary M=16": [("rotquant_kernel", 0), ("gemv_mfma_kernel<16, 0, 1, false>", 2 * MATRIX_BYTES),
-                     ("gemv_mfma_kernel<16, 0, 0, true>", MATRIX_BYTES), ("split_fold_kernel", 0)],
-    "ternary M=32": [("rotquant_kernel", 0), ("gemv_mfma_kernel<16, 0, 1, false>", 2 * MATRIX_BYTES),
-                     ("gemv_mfma_kernel<16, 0, 1, false>", 2 * MATRIX_BYTES),
-                     ("gemv_mfma_kernel<32, 0, 0, true>", MATRIX_BYTES), ("split_fold_kernel", 0)],
+    "ternary M=16": [("rotquant_kernel", 0), ("gemv_mfma_kernel<16, 0, 1, false, false>", 2 * MATRIX_BYTES),
+                     ("gemv_mfma_kernel<16, 0, 0, true, false>", MATRIX_BYTES), ("split_fold_kernel", 0)],
+    "ternary M=32": [("rotquant_kernel", 0), ("gemv_mfma_kernel<32, 0, 1, false, true>", 2 * MATRIX_BYTES),
+                     ("gemv_mfma_kernel<32, 0, 0, true, false>", MATRIX_BYTES), ("split_fold_kernel", 0)],
 }
 
 
@@ -257,7 +256,8 @@ def write_sq(sq_dir: str, out: str):
             f"{cb['SQ_VALU_MFMA_BUSY_CYCLES'] / CUS:.0f} |")
     lines += ["", "Kernel names as in the kernel statistics: gemv_ring_kernel<M, FMT, MODE, ROTX> "
               "(dot products), gemv_mfma_pack_kernel<M, FMT, MODE, KS> and gemv_mfma_kernel<M, FMT, "
-              "MODE, KS> (matrix cores; KS true = the down stage split over k), "
+              "MODE, KS, KP> (matrix cores; KS true = the down stage split over k, KP true = k "
+              "staged in two phases), "
               "ffn_layers_kernel<M, FMT> (32 layers per launch)."]
     with open(os.path.join(out, "ffn64_stream_sq_counters.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -300,8 +300,9 @@ def main():
               "gemv_mfma_pack_kernel<M, FMT, MODE, KS> (two blocks per MFMA, M <= 8; KS true = the "
               "down stage split over k, each workgroup one step of one row group, rotating its "
               "blocks of h itself; split_fold_kernel adds its step partials) and "
-              "gemv_mfma_kernel<M, FMT, MODE[, KS]> (one block per MFMA, batches above 8 rows; KS "
-              "true = the batch's down stage split over k, 16 or 32 rows) run on the "
+              "gemv_mfma_kernel<M, FMT, MODE, KS, KP> (one block per MFMA, batches above 8 rows; KS "
+              "true = the batch's down stage split over k, KP true = gate/up with k staged in two "
+              "phases; 32 rows in two 16-column groups) run on the "
               "matrix cores (ternary: gate/up for M >= 5, a single GEMV for M >= 6; sign: gate/up "
               "for M >= 5, a single GEMV for M >= 7). "
               "ffn_layers_kernel<M, FMT> is one tb_ffn_layers launch of up to 32 whole layers. "
