@@ -105,6 +105,7 @@ CASES = [
     (640, 2176, 3, SIGN, 8),
     (1152, 640, 2, TERN, 8),
     (1152, 640, 2, SIGN, 5),
+    (1152, 640, 2, SIGN, 6),   # sign on 8 waves from 6 rows (12 for 2 to 5, 16 for 1)
 ]
 
 
