@@ -224,7 +224,7 @@ def write_sq(sq_dir: str, out: str):
     b = read_all_counters(os.path.join(sq_dir, "pmc_sq_b"))
     keep = [k for k in a if k in b and ("gemv" in k or "ffn_layers" in k)]
     lines = ["# FFN 64-layer stream: SQ counters of the M=1, M=8 and M=32 kernels", "",
-             "Commands (on the GPU box, from /tmp with TMPDIR=/tmp; one counter set per run):", "", "```"]
+             "Commands (on the MI355X host, from /tmp with TMPDIR=/tmp; one counter set per run):", "", "```"]
     for name, cs in SQ_SETS.items():
         lines.append(f"rocprofv3 --pmc {cs} --output-format csv -d <out>/pmc_sq_{name} -o run -- "
                      "python3 /root/repo/bench.py --profile-only")
@@ -288,7 +288,7 @@ def main():
     cmd_stats = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
                  "-d <out>/prof -o bench -- python3 /root/repo/bench.py --steps 5 --warmup 2")
     lines = ["# FFN 64-layer weight stream (hidden 5120, intermediate 17408): kernel statistics",
-             "", "Command (on the GPU box; /root/repo is the repository):", "", "```", cmd_stats, "```",
+             "", "Command (on the MI355X host; /root/repo is the repository):", "", "```", cmd_stats, "```",
              "", "Kernel statistics (all dispatches of the run: both paths, M=1 and M=8, ternary and sign):",
              "", "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in stats[:16]:
@@ -375,7 +375,7 @@ def main():
         cmds.append(f"rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_copy_{c} -o run -- "
                     "python3 /root/repo/bench.py --copy-probe-mib 1024")
     md = ["# HBM traffic per launch: 64-layer FFN stream at M=1 and M=8 (hidden 5120, intermediate 17408)", "",
-          "Commands (on the GPU box, from /tmp with TMPDIR=/tmp; one counter per run; the copy runs "
+          "Commands (on the MI355X host, from /tmp with TMPDIR=/tmp; one counter per run; the copy runs "
           "calibrate the counters):", "", "```", *cmds, "```", "",
           f"Calibration: a device copy of 1 GiB (reads 1 GiB, writes 1 GiB) reads FETCH_SIZE x{ff:.4f} "
           f"and WRITE_SIZE x{wf:.4f} of its true bytes; the factors below scale the counters.", "",
