@@ -618,7 +618,7 @@ def eager_reference(torch, s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the path runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         log("bench.py: only --gpus 1 is supported (the path is single-GPU; see the design notes)")
         sys.exit(2)

@@ -35,7 +35,7 @@
  *            and outputs unread, until the stream has run it.
  *   Errors   Arguments are checked before anything is launched. A bad value
  *            returns TB_EINVAL, a misaligned pointer TB_EALIGN, an input that
- *            overlaps an output TB_EINVAL, and a shape this build cannot run
+ *            overlaps an output TB_EINVAL, and a shape the library cannot run
  *            TB_EUNSUPPORTED. In all of these cases nothing is enqueued. A HIP
  *            error at launch returns TB_EHIP. A fault while the kernel runs
  *            surfaces at the caller's next synchronisation. Nothing is
@@ -62,7 +62,7 @@ enum tb_status {
     TB_OK = 0,
     TB_EINVAL = -1,       /* bad shape, null pointer, unknown format, aliasing */
     TB_EALIGN = -2,       /* a pointer is not 16-byte aligned */
-    TB_EUNSUPPORTED = -3, /* valid arguments this build cannot run (e.g. LDS too small) */
+    TB_EUNSUPPORTED = -3, /* valid arguments the library cannot run (e.g. LDS too small) */
     TB_EHIP = -4,         /* the HIP runtime reported an error */
     TB_ESCRATCH = -5      /* input larger than the library's static scratch (tb_ffn_down_noalloc) */
 };
