@@ -298,21 +298,35 @@ def shader_clock(torch, replay, rounds: int = 4):
 
 def gateup_event_timing(torch, s: Stream64, reps: int):
     """Mean duration (s) of the gate/up launch of the separate-call path at M=1 (the
-    rotation of x inside it): HIP events around back-to-back launches over every layer's
-    weights (each launch streams its 47 MB from HBM), on the current stream, which is the
-    stream the library launches on."""
+    rotation of x inside it): back-to-back launches over every layer's weights (each
+    launch streams its 47 MB from HBM) captured in a HIP graph, and HIP events around
+    `reps` replays on the current stream, which the replay runs on. The graph keeps the
+    host's launch rate out of the figure (eager launches through the binding can trail
+    the GPU on a slow host)."""
     tb = s.tb
     torch.cuda.synchronize()
     n = len(s.layers)
+
+    def launches():
+        for wg, wu, _wd in s.layers:
+            tb.tb_ffn_gateup_silu_x(wg, wu, s.x[0], s.q[0], s.dq[0], s.h[0])
+
+    launches()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launches()
+    g.replay()
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     total = 0.0
     for _ in range(reps):
         e0.record()
-        for wg, wu, _wd in s.layers:
-            tb.tb_ffn_gateup_silu_x(wg, wu, s.x[0], s.q[0], s.dq[0], s.h[0])
+        g.replay()
         e1.record()
         torch.cuda.synchronize()
         total += e0.elapsed_time(e1) * 1e-3
+    del g
     return total / (reps * n)
 
 

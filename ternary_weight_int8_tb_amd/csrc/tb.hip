@@ -2545,7 +2545,7 @@ const char *tb_status_str(int status)
     case TB_OK: return "ok";
     case TB_EINVAL: return "invalid argument";
     case TB_EALIGN: return "pointer not 16-byte aligned";
-    case TB_EUNSUPPORTED: return "unsupported shape for this build or device";
+    case TB_EUNSUPPORTED: return "shape not supported by the library on this device";
     case TB_EHIP: return "HIP runtime error";
     case TB_ESCRATCH: return "input larger than the library's static scratch";
     default: return "unknown status";
