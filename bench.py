@@ -75,6 +75,8 @@ def parse():
     p.add_argument("--profile-m", default="1,8,32",
                    help="rows of the --profile-only passes, comma-separated (1..8: the fused "
                         "and the separate paths; 9..32: the *_batch calls)")
+    p.add_argument("--profile-fmt", choices=("ternary", "sign"), default="ternary",
+                   help="weight format of the --profile-only passes")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run a device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -648,7 +650,8 @@ def main():
         return
 
     t0 = time.perf_counter()
-    layers = synth.ffn_stream(SEED, args.layers, synth.FMT_TERNARY2, threads=16)
+    fmt = synth.FMT_SIGN1 if args.profile_only and args.profile_fmt == "sign" else synth.FMT_TERNARY2
+    layers = synth.ffn_stream(SEED, args.layers, fmt, threads=16)
     xs = [synth.normal_rows(32, synth.HIDDEN, SEED, l) for l in range(args.layers)]
     layer_bytes = layers[0].nbytes
     step_bytes = layer_bytes * args.layers

@@ -217,21 +217,26 @@ def read_all_counters(d: str):
     return {k: ({c: v / e["n"] for c, v in e["sum"].items()}, e["n"]) for k, e in agg.items()}
 
 
-def write_sq(sq_dir: str, out: str):
-    """SQ counters of the M=1, M=8 and M=32 kernels: instruction mix per wave and where wave
-    time goes (waiting on memory counters, waiting to issue, issuing VALU)."""
+def write_sq(sq_dir: str, out: str, sign: bool = False):
+    """SQ counters of the M=1, M=8 and M=32 kernels (sign weights: M=1 and M=8):
+    instruction mix per wave and where wave time goes (waiting on memory counters, waiting
+    to issue, issuing VALU)."""
     a = read_all_counters(os.path.join(sq_dir, "pmc_sq_a"))
     b = read_all_counters(os.path.join(sq_dir, "pmc_sq_b"))
     keep = [k for k in a if k in b and ("gemv" in k or "ffn_layers" in k)]
-    lines = ["# FFN 64-layer stream: SQ counters of the M=1, M=8 and M=32 kernels", "",
+    what = "Sign-weight" if sign else "FFN"
+    ms = "M=1 and M=8" if sign else "M=1, M=8 and M=32"
+    extra = " --profile-fmt sign --profile-m 1,8" if sign else ""
+    lines = [f"# {what} 64-layer stream: SQ counters of the {ms} kernels", "",
              "Commands (on the MI355X host, from /tmp with TMPDIR=/tmp; one counter set per run):", "", "```"]
     for name, cs in SQ_SETS.items():
         lines.append(f"rocprofv3 --pmc {cs} --output-format csv -d <out>/pmc_sq_{name} -o run -- "
-                     "python3 /root/repo/bench.py --profile-only")
+                     f"python3 /root/repo/bench.py --profile-only{extra}")
     lines += ["```", "",
               "Means per dispatch over every dispatch of the kernel in one pass of each path at M=1 "
-              "and M=8, and of the batch calls at M=32 (bench.py --profile-only). Instruction counts "
-              "are wave instructions per wave. "
+              + ("and M=8 (bench.py --profile-only --profile-fmt sign). " if sign else
+                 "and M=8, and of the batch calls at M=32 (bench.py --profile-only). ") +
+              "Instruction counts are wave instructions per wave. "
               "SQ_WAVE_CYCLES, SQ_WAIT_ANY (waiting on s_waitcnt: memory and LDS counters), "
               "SQ_WAIT_INST_ANY (waiting to issue the next instruction) and SQ_ACTIVE_INST_VALU "
               "share one unit (quad-cycles), so their ratios are fractions of resident wave time. "
@@ -259,9 +264,10 @@ def write_sq(sq_dir: str, out: str):
               "MODE, KS, KP> (matrix cores; KS true = the down stage split over k, KP true = k "
               "staged in two phases), "
               "ffn_layers_kernel<M, FMT> (32 layers per launch)."]
-    with open(os.path.join(out, "ffn64_stream_sq_counters.md"), "w") as fh:
+    name = "sign1_stream_sq_counters.md" if sign else "ffn64_stream_sq_counters.md"
+    with open(os.path.join(out, name), "w") as fh:
         fh.write("\n".join(lines) + "\n")
-    print(f"wrote {out}/ffn64_stream_sq_counters.md")
+    print(f"wrote {out}/{name}")
 
 
 def main():
@@ -270,10 +276,13 @@ def main():
     p.add_argument("--pmc")
     p.add_argument("--bench")
     p.add_argument("--sq", help="parent directory of the SQ counter runs pmc_sq_a and pmc_sq_b")
+    p.add_argument("--sq-sign", help="the same for the sign-weight runs (--profile-fmt sign)")
     p.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = p.parse_args()
     if a.sq:
         write_sq(a.sq, a.out)
+    if a.sq_sign:
+        write_sq(a.sq_sign, a.out, sign=True)
     if not a.stats:
         return
 
